@@ -1,0 +1,358 @@
+"""Pins for the CPU oracle: checks against what the definitions and plain
+mathematics fix, independent of the oracle's own code paths.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees.
+``test_oracle_pins.py`` runs them; ``test_oracle_mutations.py`` plants
+mistakes in the oracle and checks that some pin catches each one.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle.bsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- helpers ---
+def _coords(g, tokens):
+    """(t, h, w) of latent-order token ids."""
+    tokens = np.asarray(tokens)
+    return tokens // (g.H * g.W), (tokens // g.W) % g.H, tokens % g.W
+
+
+def _block_of_token(g):
+    """Block id of every latent-order token, from its grid coordinates."""
+    t, h, w = _coords(g, np.arange(g.seq_len))
+    return ((t // g.ct) * g.nH + (h // g.ch)) * g.nW + (w // g.cw)
+
+
+def _textbook_attention(q, k, v, scale, allowed=None):
+    """softmax(q k^T * scale [+ log allowed]) v over whole sequences, fp64."""
+    logits = (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T) * scale
+    if allowed is not None:
+        logits = np.where(allowed, logits, -np.inf)
+    logits -= logits.max(axis=1, keepdims=True)
+    w = np.exp(logits)
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ np.asarray(v, np.float64)
+
+
+def _rand(rng, g, d=16):
+    S = g.seq_len
+    return (rng.standard_normal((S, d)), rng.standard_normal((S, d)), rng.standard_normal((S, d)))
+
+
+# ------------------------------------------------------------------- pins ---
+def pin_block_order_geometry():
+    """Each block is a ct x ch x cw box at its origin, blocks run in
+    [N_T, N_H, N_W] order and slots in [t, h, w] order; perm is a bijection."""
+    for g in (O.Geometry(8, 8, 16), O.Geometry(4, 8, 8, 2, 4, 4), O.Geometry(6, 4, 9, 3, 2, 3)):
+        perm = O.block_token_order(g)
+        assert np.array_equal(np.sort(perm), np.arange(g.seq_len)), "not a permutation"
+        n = g.n
+        for i in range(g.num_blocks):
+            bt, rem = divmod(i, g.nH * g.nW)
+            bh, bw = divmod(rem, g.nW)
+            t, h, w = _coords(g, perm[i * n : (i + 1) * n])
+            lt, lh, lw = t - bt * g.ct, h - bh * g.ch, w - bw * g.cw
+            for name, loc, ext in (("t", lt, g.ct), ("h", lh, g.ch), ("w", lw, g.cw)):
+                assert loc.min() == 0 and loc.max() == ext - 1, f"block {i} {name} extent"
+            slot = (lt * g.ch + lh) * g.cw + lw
+            assert np.array_equal(slot, np.arange(n)), f"block {i} slot order"
+
+
+def _load_golden():
+    with open(os.path.join(GOLDEN, "handworked_blocks.json")) as f:
+        return json.load(f)
+
+
+def pin_handworked_golden():
+    """Hand-derived selections and outputs (tests/golden/handworked_blocks.json)."""
+    gold = _load_golden()
+    st = gold["setup"]
+    a = st["q_first_channel_per_block"]
+    b = [x * np.log(2.0) for x in st["k_first_channel_per_block_in_units_of_ln2"]]
+    for case in gold["cases"]:
+        g = O.Geometry(st["grid"]["T"], st["grid"]["H"], st["grid"]["W"], *st["chunk"],
+                       cond_frames=case["cond_frames"])
+        d = st["head_dim"]
+        blk = _block_of_token(g)
+        q = np.zeros((g.seq_len, d))
+        k = np.zeros((g.seq_len, d))
+        v = np.zeros((g.seq_len, d))
+        q[:, 0] = np.asarray(a)[blk]
+        k[:, 0] = np.asarray(b)[blk]
+        v[np.arange(g.seq_len), blk] = 1.0
+        if case["mode"] == "topk":
+            p = O.SelectParams("topk", k=case["k"])
+        else:
+            p = O.SelectParams("cdf", p=case["p"], k_min=case["k_min"], k_max=case["k_max"])
+        out, idx, cnt, _ = O.bsa_head(q, k, v, g, p, st["scale"])
+        for i, exp_ids in enumerate(case["idx"]):
+            got = idx[i, : cnt[i]].tolist()
+            assert got == exp_ids, f"{case['name']} row {i}: {got} != {exp_ids}"
+            assert np.all(idx[i, cnt[i]:] == -1)
+            want = np.array([float(Fraction(x)) for x in case["out"][i]])
+            rows = out[blk == i]
+            assert np.abs(rows - want).max() < 1e-12, f"{case['name']} output row {i}"
+
+
+def pin_dense_equals_textbook():
+    """Selecting every block reduces BSA to plain softmax attention."""
+    rng = np.random.default_rng(11)
+    g = O.Geometry(4, 8, 16)
+    q, k, v = _rand(rng, g)
+    scale = 1 / np.sqrt(q.shape[1])
+    ref = _textbook_attention(q, k, v, scale)
+    out, idx, cnt, _ = O.bsa_head(q, k, v, g, O.SelectParams("topk", k=g.num_blocks), scale)
+    assert np.all(cnt == g.num_blocks)
+    assert np.abs(out - ref).max() < 1e-12, "BSA with all blocks != dense attention"
+    assert np.abs(O.dense_head(q, k, v, g, scale) - ref).max() < 1e-12
+    big_k = O.bsa_head(q, k, v, g, O.SelectParams("topk", k=99), scale)[0]
+    assert np.abs(big_k - ref).max() < 1e-12, "k above the block count must clamp"
+
+
+def pin_mask_formula():
+    """Gathered attention equals the mask formulation over the whole sequence:
+    keys outside the selected blocks get -inf before the softmax."""
+    rng = np.random.default_rng(12)
+    for g, p in (
+        (O.Geometry(8, 8, 16), O.SelectParams("topk", k=3)),
+        (O.Geometry(8, 8, 16, cond_frames=4), O.SelectParams("cdf", p=0.6, k_min=1, k_max=5)),
+    ):
+        q, k, v = _rand(rng, g)
+        scale = 1 / np.sqrt(q.shape[1])
+        out, idx, cnt, _ = O.bsa_head(q, k, v, g, p, scale)
+        blk = _block_of_token(g)
+        sel = np.zeros((g.num_blocks, g.num_blocks), dtype=bool)
+        for i in range(g.num_blocks):
+            sel[i, idx[i, : cnt[i]]] = True
+        allowed = sel[blk[:, None], blk[None, :]]
+        ref = _textbook_attention(q, k, v, scale, allowed)
+        assert np.abs(out - ref).max() < 1e-12, "gathered attention != masked attention"
+
+
+def pin_pooled_scores_bruteforce():
+    """Pooled scores recomputed from grid coordinates (block means by
+    accumulation, then dot products) match the oracle's."""
+    rng = np.random.default_rng(13)
+    for g in (O.Geometry(8, 8, 16), O.Geometry(4, 8, 8, 2, 4, 4, cond_frames=2)):
+        q, k, _ = _rand(rng, g)
+        scale = 0.37
+        blk = _block_of_token(g)
+        qs = np.zeros((g.num_blocks, q.shape[1]))
+        ks = np.zeros_like(qs)
+        np.add.at(qs, blk, q)
+        np.add.at(ks, blk, k)
+        counts = np.bincount(blk, minlength=g.num_blocks)[:, None]
+        s_ref = (qs / counts) @ (ks / counts).T * scale
+        _, _, scores = O.select_head(q, k, g, O.SelectParams("topk", k=1), scale)
+        for i in range(g.num_blocks):
+            na = O.allowed_key_blocks(g, i)
+            assert np.abs(scores[i, :na] - s_ref[i, :na]).max() < 1e-12, "pooled score"
+            assert np.all(np.isneginf(scores[i, na:]))
+
+
+def pin_topk_property():
+    """Top-k sets: right size, every kept score >= every dropped score, and
+    equal scores at the cut go to the lower ids."""
+    rng = np.random.default_rng(14)
+    for trial in range(300):
+        n = int(rng.integers(1, 40))
+        s = np.round(rng.standard_normal(n), 1)  # rounding makes ties common
+        na = int(rng.integers(1, n + 1))
+        k = int(rng.integers(1, n + 3))
+        sel = O.select_topk(s, na, k)
+        assert sel.size == min(k, na)
+        assert np.all(np.diff(sel) > 0) and (sel.size == 0 or sel.max() < na)
+        rest = np.setdiff1d(np.arange(na), sel)
+        if rest.size and sel.size:
+            cut = s[sel].min()
+            assert cut >= s[rest].max()
+            tied_in = sel[s[sel] == cut]
+            tied_out = rest[s[rest] == cut]
+            if tied_out.size:
+                assert tied_in.max() < tied_out.min(), "ties must go to lower ids"
+
+
+def pin_cdf_property():
+    """CDF sets: a top set by probability; its mass reaches p and dropping its
+    least likely member falls below p, unless a clamp decided the count."""
+    rng = np.random.default_rng(15)
+    for trial in range(300):
+        n = int(rng.integers(1, 30))
+        s = rng.standard_normal(n) * rng.uniform(0.1, 4)
+        na = int(rng.integers(1, n + 1))
+        p = float(rng.uniform(0.05, 1.0))
+        kmin = int(rng.integers(1, 6))
+        kmax = int(rng.integers(kmin, 12))
+        sel = O.select_cdf(s, na, p, kmin, kmax)
+        e = np.exp(s[:na] - s[:na].max())
+        prob = e / e.sum()
+        assert np.all(np.diff(sel) > 0) and sel.max() < na
+        rest = np.setdiff1d(np.arange(na), sel)
+        if rest.size:
+            assert prob[sel].min() >= prob[rest].max() - 1e-15
+        m = sel.size
+        mass = prob[sel].sum()
+        hi = min(kmax, na)
+        if kmin < m < hi:
+            assert mass >= p - 1e-12, "mass must reach p"
+            assert mass - prob[sel].min() < p + 1e-12, "prefix must be minimal"
+        if m == hi and hi > kmin:
+            assert mass - prob[sel].min() < p + 1e-12
+        if m == kmin and kmin < hi:
+            assert mass >= p - 1e-12, "k_min clamp only raises the count"
+        assert kmin <= m or m == na
+        assert m <= hi
+
+
+def pin_rows_sum_to_one():
+    """With V = block indicators, each output row is the attention mass per
+    key block: non-negative, zero outside the selection, summing to 1."""
+    rng = np.random.default_rng(16)
+    g = O.Geometry(8, 8, 16, cond_frames=4)
+    q, k, _ = _rand(rng, g)
+    blk = _block_of_token(g)
+    v = np.zeros((g.seq_len, g.num_blocks))
+    v[np.arange(g.seq_len), blk] = 1.0
+    for p in (O.SelectParams("topk", k=3), O.SelectParams("cdf", p=0.8, k_min=2, k_max=6)):
+        out, idx, cnt, _ = O.bsa_head(q, k, v, g, p, 0.25)
+        assert np.abs(out.sum(axis=1) - 1).max() < 1e-12, "rows must sum to 1"
+        assert out.min() > -1e-15
+        for i in range(g.num_blocks):
+            off = np.setdiff1d(np.arange(g.num_blocks), idx[i, : cnt[i]])
+            assert np.abs(out[blk == i][:, off]).max() == 0.0
+
+
+def pin_constant_v():
+    """V constant => O equals that constant for every query."""
+    rng = np.random.default_rng(17)
+    g = O.Geometry(8, 8, 16)
+    q, k, _ = _rand(rng, g)
+    v = np.tile(np.linspace(-2, 3, q.shape[1]), (g.seq_len, 1))
+    out = O.bsa_head(q, k, v, g, O.SelectParams("topk", k=2), 0.3)[0]
+    assert np.abs(out - v).max() < 1e-12
+
+
+def pin_q_zero():
+    """Q = 0: all pooled scores tie, so top-k keeps blocks 0..k-1 and every
+    query averages V over those blocks' tokens; CDF keeps ceil(p * allowed)."""
+    rng = np.random.default_rng(18)
+    g = O.Geometry(8, 8, 16, cond_frames=4)
+    _, k, v = _rand(rng, g)
+    q = np.zeros_like(k)
+    blk = _block_of_token(g)
+    out, idx, cnt, _ = O.bsa_head(q, k, v, g, O.SelectParams("topk", k=3), 0.2)
+    for i in range(g.num_blocks):
+        na = O.allowed_key_blocks(g, i)
+        want = list(range(min(3, na)))
+        assert idx[i, : cnt[i]].tolist() == want
+        mean_v = v[np.isin(blk, want)].mean(axis=0)
+        assert np.abs(out[blk == i] - mean_v).max() < 1e-12
+    _, idx, cnt, _ = O.bsa_head(q, k, v, g, O.SelectParams("cdf", p=0.3, k_min=1, k_max=8), 0.2)
+    for i in range(g.num_blocks):
+        na = O.allowed_key_blocks(g, i)
+        want = min(int(np.ceil(0.3 * na)), 8)
+        assert cnt[i] == want and idx[i, : cnt[i]].tolist() == list(range(want))
+
+
+def pin_intra_block_shuffle():
+    """Shuffling tokens inside every block (same shuffle for Q, K, V) keeps
+    pooled scores and selections and moves the outputs with the tokens."""
+    rng = np.random.default_rng(19)
+    g = O.Geometry(8, 8, 16)
+    q, k, v = _rand(rng, g)
+    perm = O.block_token_order(g)
+    shuffled = perm.copy()
+    for i in range(g.num_blocks):
+        seg = shuffled[i * g.n : (i + 1) * g.n]
+        shuffled[i * g.n : (i + 1) * g.n] = seg[rng.permutation(g.n)]
+    remap = np.empty(g.seq_len, dtype=np.int64)
+    remap[perm] = shuffled  # token perm[x] now holds the data of token shuffled[x]
+    p = O.SelectParams("topk", k=3)
+    out, idx, cnt, sc = O.bsa_head(q, k, v, g, p, 0.25)
+    out2, idx2, cnt2, sc2 = O.bsa_head(q[remap], k[remap], v[remap], g, p, 0.25)
+    assert np.abs(sc - sc2)[np.isfinite(sc)].max() < 1e-12
+    assert np.array_equal(idx, idx2) and np.array_equal(cnt, cnt2)
+    assert np.abs(out2 - out[remap]).max() < 1e-12
+
+
+def pin_block_causal_independence():
+    """Condition rows never see noisy tokens: replacing every noisy token's
+    Q, K, V leaves their selections and outputs bitwise unchanged."""
+    rng = np.random.default_rng(20)
+    g = O.Geometry(12, 8, 16, cond_frames=4)
+    q, k, v = _rand(rng, g)
+    t = _coords(g, np.arange(g.seq_len))[0]
+    noisy = t >= g.cond_frames
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for a in (q2, k2, v2):
+        a[noisy] = rng.standard_normal((int(noisy.sum()), a.shape[1]))
+    for p in (O.SelectParams("topk", k=2), O.SelectParams("cdf", p=0.7, k_min=1, k_max=4)):
+        out, idx, cnt, _ = O.bsa_head(q, k, v, g, p, 0.25)
+        out2, idx2, cnt2, _ = O.bsa_head(q2, k2, v2, g, p, 0.25)
+        c = g.cond_blocks
+        assert np.array_equal(idx[:c], idx2[:c]) and np.array_equal(cnt[:c], cnt2[:c])
+        assert np.array_equal(out[~noisy], out2[~noisy])
+        assert idx[:c].max() < c
+
+
+def pin_block_causal_dense_definition():
+    """Dense block-causal attention equals X_cond = Attn(Q_c, K_c, V_c) and
+    X_noisy = Attn(Q_n, [K_c, K_n], [V_c, V_n]) over the token sets."""
+    rng = np.random.default_rng(21)
+    g = O.Geometry(8, 8, 16, cond_frames=4)
+    q, k, v = _rand(rng, g)
+    cond = _coords(g, np.arange(g.seq_len))[0] < g.cond_frames
+    scale = 0.21
+    ref = np.zeros_like(q)
+    ref[cond] = _textbook_attention(q[cond], k[cond], v[cond], scale)
+    ref[~cond] = _textbook_attention(q[~cond], k, v, scale)
+    assert np.abs(O.dense_head(q, k, v, g, scale) - ref).max() < 1e-12
+
+
+def pin_monotonic():
+    """Selections grow with k and with p."""
+    rng = np.random.default_rng(22)
+    g = O.Geometry(8, 16, 16)
+    q, k, _ = _rand(rng, g)
+    prev = None
+    for kk in range(1, g.num_blocks + 1):
+        idx, cnt, _ = O.select_head(q, k, g, O.SelectParams("topk", k=kk), 0.25)
+        sets = [set(idx[i, : cnt[i]].tolist()) for i in range(g.num_blocks)]
+        if prev is not None:
+            assert all(a <= b for a, b in zip(prev, sets))
+        prev = sets
+    prev = None
+    for pp in (0.1, 0.3, 0.5, 0.7, 0.9, 1.0):
+        idx, cnt, _ = O.select_head(
+            q, k, g, O.SelectParams("cdf", p=pp, k_min=1, k_max=g.num_blocks), 0.25)
+        sets = [set(idx[i, : cnt[i]].tolist()) for i in range(g.num_blocks)]
+        if prev is not None:
+            assert all(a <= b for a, b in zip(prev, sets))
+        prev = sets
+
+
+ALL_PINS = [
+    pin_block_order_geometry,
+    pin_handworked_golden,
+    pin_dense_equals_textbook,
+    pin_mask_formula,
+    pin_pooled_scores_bruteforce,
+    pin_topk_property,
+    pin_cdf_property,
+    pin_rows_sum_to_one,
+    pin_constant_v,
+    pin_q_zero,
+    pin_intra_block_shuffle,
+    pin_block_causal_independence,
+    pin_block_causal_dense_definition,
+    pin_monotonic,
+]

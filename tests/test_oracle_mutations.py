@@ -1,0 +1,116 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at
+least one pin catches each of them. Shows the pins are strong enough to
+notice a dropped term, a wrong index, a transposed operand or a wrong rule."""
+
+import numpy as np
+import pytest
+
+import oracle.bsa_oracle as O
+import oracle_pins as P
+
+_orig_attend = O.attend_query_block
+_orig_order = O.block_token_order
+_orig_pool = O.pool_blocks
+_orig_cdf = O.select_cdf
+
+
+def _attend_no_scale(q, k, v, g, i, key_blocks, scale, perm=None):
+    return _orig_attend(q, k, v, g, i, key_blocks, 1.0, perm)
+
+
+def _attend_keys_as_values(q, k, v, g, i, key_blocks, scale, perm=None):
+    return _orig_attend(q, k, k, g, i, key_blocks, scale, perm)
+
+
+def _order_hw_swapped(g):
+    perm = np.empty(g.seq_len, dtype=np.int64)
+    pos = 0
+    for bt in range(g.nT):
+        for bh in range(g.nH):
+            for bw in range(g.nW):
+                for it in range(g.ct):
+                    for iw in range(g.cw):
+                        for ih in range(g.ch):
+                            perm[pos] = ((bt * g.ct + it) * g.H + bh * g.ch + ih) * g.W + bw * g.cw + iw
+                            pos += 1
+    return perm
+
+
+def _order_blocks_w_major(g):
+    perm = _orig_order(g)
+    n = g.n
+    blocks = perm.reshape(g.nT, g.nH, g.nW, n).transpose(0, 2, 1, 3)
+    return blocks.reshape(-1).copy()
+
+
+def _pool_sum(x, perm, n):
+    return _orig_pool(x, perm, n) * n
+
+
+def _pool_first_token(x, perm, n):
+    xb = np.asarray(x, dtype=np.float64)[perm]
+    return xb.reshape(-1, n, xb.shape[-1])[:, 0, :].copy()
+
+
+def _rank_ties_high(values):
+    ids = np.arange(values.shape[0])
+    return np.lexsort((-ids, -values))
+
+
+def _cdf_drop_crossing(scores_row, n_allowed, p, k_min, k_max):
+    probs = O.softmax_allowed(scores_row, n_allowed)
+    order = O._rank_order(probs)
+    cum = np.cumsum(probs[order])
+    reached = np.nonzero(cum >= p)[0]
+    count = int(reached[0]) if reached.size else n_allowed
+    count = min(max(count, k_min), min(k_max, n_allowed))
+    return np.sort(order[:count])
+
+
+def _cdf_no_clamp(scores_row, n_allowed, p, k_min, k_max):
+    return _orig_cdf(scores_row, n_allowed, p, 1, n_allowed)
+
+
+def _topk_lowest(scores_row, n_allowed, k):
+    order = np.lexsort((np.arange(n_allowed), np.asarray(scores_row[:n_allowed])))
+    return np.sort(order[: min(k, n_allowed)])
+
+
+def _scores_unscaled(q_pool, k_pool, scale):
+    return q_pool @ k_pool.T
+
+
+def _scores_transposed(q_pool, k_pool, scale):
+    return (k_pool @ q_pool.T) * scale
+
+
+MUTANTS = {
+    "attention scale dropped": ("attend_query_block", _attend_no_scale),
+    "keys used as values": ("attend_query_block", _attend_keys_as_values),
+    "intra-block order h/w swapped": ("block_token_order", _order_hw_swapped),
+    "block order w before h": ("block_token_order", _order_blocks_w_major),
+    "pool sums instead of means": ("pool_blocks", _pool_sum),
+    "pool takes first token only": ("pool_blocks", _pool_first_token),
+    "ties go to higher ids": ("_rank_order", _rank_ties_high),
+    "CDF drops the crossing block": ("select_cdf", _cdf_drop_crossing),
+    "CDF ignores k_min/k_max": ("select_cdf", _cdf_no_clamp),
+    "top-k keeps the lowest scores": ("select_topk", _topk_lowest),
+    "pooled score scale dropped": ("pooled_scores", _scores_unscaled),
+    "pooled scores transposed": ("pooled_scores", _scores_transposed),
+    "block-causal ignored": ("allowed_key_blocks", lambda g, i: g.num_blocks),
+    "noisy rows restricted too": ("allowed_key_blocks",
+                                  lambda g, i: g.cond_blocks if g.cond_frames else g.num_blocks),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin noticed the planted mistake: {name}"
