@@ -1,0 +1,152 @@
+/*
+ * bsa.h -- C ABI of libbsa.so: 3D Block Sparse Attention (BSA) on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is the one described in "LongCat-Video Technical Report"
+ * (paper-graph-ui deep dive), section "Block Sparse Attention":
+ *   1. the latent grid T x H x W is cut into blocks of ct x ch x cw tokens
+ *      ("3D block partitioning"; the default chunk shape [4, 4, 8] comes from
+ *      the zhaifeiyue notes, section 3, "3D Block Sparse Attention");
+ *   2. Q and K are mean-pooled per block ("Pooled block similarity
+ *      computation");
+ *   3. S_pool = Q_pool K_pool^T / sqrt(d) is scored per (batch, head) and each
+ *      query block keeps its top-k key blocks, or, in CDF mode, the smallest
+ *      set of most probable key blocks whose softmax mass reaches p, clamped
+ *      to [k_min, k_max] ("Block selection via pooled attention scores";
+ *      Top-r and CDF-p modes under "Implementation details and design
+ *      trade-offs");
+ *   4. attention runs only over the kept key blocks ("Sparse attention
+ *      computation": non-selected keys are excluded from the softmax).
+ * Block-causal attention follows section "Block Attention with KV-Cache for
+ * Efficient Multi-Task Inference", "Attention structure": the first
+ * cond_frames latent frames are condition tokens that attend only to
+ * condition tokens; the other (noisy) tokens attend to all tokens.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors. q, k, v, o are bfloat16 [batch, heads, S, head_dim], contiguous,
+ *   S = T*H*W tokens in latent order s = (t*H + h)*W + w. Pointers are device
+ *   pointers, 16-byte aligned. head_dim must be 128.
+ * Blocks. nT = T/ct, nH = H/ch, nW = W/cw; block id
+ *   i = (bt*nH + bh)*nW + bw; a block holds ct*ch*cw = 128 tokens. The grid
+ *   must divide by the chunk shape.
+ * Ownership. The caller owns every buffer. The library never allocates,
+ *   frees, or synchronises; all work is enqueued on `stream` (a hipStream_t;
+ *   NULL is the default stream). Workspace contents do not carry over from
+ *   one call to the next. Outputs must not alias inputs.
+ * Errors. Arguments are checked on the host before anything is launched; a
+ *   bad call returns a negative status and launches nothing.
+ *   bsa_last_error() gives a message for the last failure on this thread.
+ *   A launch failure reported by the HIP runtime returns BSA_ERR_LAUNCH.
+ * Empty problems. batch == 0 or heads == 0 is valid: nothing is launched and
+ *   pointers may be NULL.
+ * Concurrency. Calls are asynchronous and stream-ordered. Two calls may not
+ *   share a workspace unless they are ordered on one stream.
+ * Determinism. Identical inputs give bit-identical idx, cnt and o.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsa_status {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = -1, /* a pointer, size or parameter is out of range */
+  BSA_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
+  BSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  BSA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
+} bsa_status;
+
+/* Selection modes (Top-r and CDF-p modes of the deep dive's
+ * "Implementation details and design trade-offs"). */
+enum { BSA_TOPK = 0, BSA_CDF = 1 };
+
+/* Problem shape: latent grid, heads, chunk shape, block-causal split. */
+typedef struct bsa_problem {
+  int32_t batch;       /* >= 0 */
+  int32_t heads;       /* >= 0 */
+  int32_t head_dim;    /* must be 128 */
+  int32_t T, H, W;     /* latent grid, each > 0 */
+  int32_t ct, ch, cw;  /* chunk shape; ct*ch*cw must be 128 and divide the grid */
+  int32_t cond_frames; /* 0: no block-causal mask; else a multiple of ct, < T */
+  float scale;         /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+} bsa_problem;
+
+/* Block-selection rule. */
+typedef struct bsa_select_params {
+  int32_t mode;  /* BSA_TOPK or BSA_CDF */
+  int32_t k;     /* top-k: key blocks per query block, >= 1; clamped per row
+                    to the number of key blocks that row may see */
+  float cdf_p;   /* CDF: 0 < p <= 1 */
+  int32_t k_min; /* CDF: lower clamp on the count, >= 1 */
+  int32_t k_max; /* CDF: upper clamp on the count, >= k_min */
+} bsa_select_params;
+
+/* Row length of the idx array written by bsa_select: k (top-k) or k_max
+ * (CDF). Returns -1 on invalid parameters. */
+int32_t bsa_index_stride(const bsa_select_params* params);
+
+/* Bytes of device workspace bsa_select needs (pooled Q/K and the pooled
+ * score matrix: 4*(2*128 + Nb) bytes per block per (batch, head), plus
+ * alignment). Returns 0 on invalid arguments. */
+size_t bsa_select_workspace_bytes(const bsa_problem* problem,
+                                  const bsa_select_params* params);
+
+/* Bytes of device workspace bsa_attention and dense_attention need (V
+ * repacked per block with head_dim as the outer index: 2*S*128 bytes per
+ * (batch, head), plus alignment). Returns 0 on invalid arguments. */
+size_t bsa_attention_workspace_bytes(const bsa_problem* problem);
+
+/* Block selection: pooling, pooled scores, softmax and top-k / CDF selection
+ * with the block-causal restriction (steps 1-3 above).
+ *   q, k     bf16 [batch, heads, S, 128], read only.
+ *   idx      int32 [batch, heads, Nb, stride] out: kept key-block ids of each
+ *            query block in ascending order, then -1 up to stride.
+ *   cnt      int32 [batch, heads, Nb] out: number of kept key blocks.
+ *   Ties between equal pooled scores keep the lower key-block id. A
+ *   condition query block only considers condition key blocks.
+ * Limits: Nb <= 4096 key blocks per (batch, head) (BSA_ERR_UNSUPPORTED). */
+bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* params,
+                      const void* q, const void* k, int32_t* idx, int32_t* cnt,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sparse attention over the kept key blocks (step 4 above): for every query
+ * block, softmax(Q K_sel^T * scale) V_sel over the tokens of its kept key
+ * blocks, written in latent order.
+ *   idx, cnt   as written by bsa_select (any ascending or unordered list of
+ *              key-block ids is accepted); ids outside [0, Nb) are skipped
+ *              and cnt is clamped to [0, idx_stride]. A query block with no
+ *              key blocks gets zeros.
+ *   o          bf16 [batch, heads, S, 128] out.
+ * The softmax is computed in fp32 from bf16 products accumulated in fp32;
+ * the probabilities are rounded to bf16 before multiplying V. */
+bsa_status bsa_attention(const bsa_problem* problem, const void* q, const void* k,
+                         const void* v, const int32_t* idx, const int32_t* cnt,
+                         int32_t idx_stride, void* o, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Dense softmax attention over every key the query may see (all keys, or
+ * condition keys only for condition queries when cond_frames > 0): the
+ * baseline that BSA is measured against, using the same tile engine.
+ * Arguments as for bsa_attention. */
+bsa_status dense_attention(const bsa_problem* problem, const void* q, const void* k,
+                           const void* v, void* o, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* bsa_status_string(int32_t status);
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none). The pointer stays valid until the next call on that thread. */
+const char* bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

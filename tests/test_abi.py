@@ -1,0 +1,158 @@
+"""Host-side checks of the C ABI (no GPU needed): every symbol that
+include/bsa.h declares is exported, and invalid calls return the documented
+status before anything is launched."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_dit_block_bsa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("bsa_select", "bsa_attention", "dense_attention"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = B.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    lib = B.lib()
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.bsa_status_string(code)
+
+
+def _problem(**kw):
+    args = dict(T=56, H=48, W=80, heads=32)
+    args.update({k: kw.pop(k) for k in list(kw) if k in args})
+    return B.Problem.make(**args, **kw)
+
+
+def test_workspace_sizes():
+    p = _problem()
+    nb = 1680
+    sel = B.select_workspace_bytes(p, B.SelectParams.topk(105))
+    assert sel >= 32 * nb * (2 * 128 * 4 + nb * 4)
+    assert sel < 32 * nb * (2 * 128 * 4 + nb * 4) + 3 * 256
+    att = B.attention_workspace_bytes(p)
+    assert att == 32 * 215040 * 128 * 2
+    assert B.select_workspace_bytes(_problem(head_dim=64), B.SelectParams.topk(1)) == 0
+    assert B.attention_workspace_bytes(_problem(T=57)) == 0
+
+
+def test_index_stride():
+    assert B.index_stride(B.SelectParams.topk(45)) == 45
+    assert B.index_stride(B.SelectParams.cdf(0.9, 4, 64)) == 64
+    assert B.index_stride(B.SelectParams.topk(0)) == -1
+
+
+def _select(problem, params, q=FAKE, k=FAKE, idx=FAKE, cnt=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    lib = B.lib()
+    return lib.bsa_select(ctypes.byref(problem), ctypes.byref(params), q, k, idx, cnt, ws,
+                          ws_bytes, None)
+
+
+def _attn(problem, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE, stride=4, o=FAKE + 4096,
+          ws=FAKE, ws_bytes=1 << 40):
+    lib = B.lib()
+    return lib.bsa_attention(ctypes.byref(problem), q, k, v, idx, cnt, stride, o, ws, ws_bytes,
+                             None)
+
+
+@pytest.mark.parametrize(
+    "problem,code",
+    [
+        (dict(head_dim=64), UNSUPPORTED),
+        (dict(head_dim=0), INVALID),
+        (dict(chunk=(4, 4, 4)), UNSUPPORTED),
+        (dict(T=57), UNSUPPORTED),
+        (dict(cond_frames=3), INVALID),
+        (dict(cond_frames=56), INVALID),
+        (dict(cond_frames=-4), INVALID),
+        (dict(heads=-1), INVALID),
+        (dict(T=0), INVALID),
+        (dict(chunk=(0, 4, 8)), INVALID),
+    ],
+)
+def test_invalid_problem(problem, code):
+    p = _problem(**problem)
+    assert _select(p, B.SelectParams.topk(4)) == code
+    assert _attn(p) == code
+    assert B.lib().bsa_last_error()
+
+
+@pytest.mark.parametrize(
+    "params,code",
+    [
+        (B.SelectParams.topk(0), INVALID),
+        (B.SelectParams.cdf(0.0, 1, 4), INVALID),
+        (B.SelectParams.cdf(1.5, 1, 4), INVALID),
+        (B.SelectParams.cdf(0.9, 5, 4), INVALID),
+        (B.SelectParams.cdf(0.9, 0, 4), INVALID),
+        (B.SelectParams(7, 1, 0.5, 1, 1), INVALID),
+    ],
+)
+def test_invalid_params(params, code):
+    assert _select(_problem(), params) == code
+
+
+def test_null_and_misaligned_pointers():
+    p = _problem()
+    sp = B.SelectParams.topk(4)
+    assert _select(p, sp, q=None) == INVALID
+    assert _select(p, sp, idx=None) == INVALID
+    assert _select(p, sp, k=FAKE + 2) == INVALID
+    assert _attn(p, v=None) == INVALID
+    assert _attn(p, o=FAKE + 8) == INVALID
+    assert _attn(p, o=FAKE) == INVALID  # aliases q
+    assert _attn(p, stride=0) == INVALID
+
+
+def test_workspace_too_small():
+    p = _problem()
+    assert _select(p, B.SelectParams.topk(4), ws_bytes=1024) == WORKSPACE
+    assert _select(p, B.SelectParams.topk(4), ws=None) == WORKSPACE
+    assert _attn(p, ws_bytes=1024) == WORKSPACE
+    lib = B.lib()
+    assert lib.dense_attention(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE + 4096, None, 0, None) == WORKSPACE
+
+
+def test_too_many_blocks_for_selection():
+    p = _problem(T=4 * 100, H=48, W=80)  # 12,000 blocks
+    assert _select(p, B.SelectParams.topk(4)) == UNSUPPORTED
+
+
+def test_empty_problem_is_a_no_op():
+    lib = B.lib()
+    p = _problem(heads=0)
+    sp = B.SelectParams.topk(4)
+    assert lib.bsa_select(ctypes.byref(p), ctypes.byref(sp), None, None, None, None, None, 0, None) == OK
+    assert lib.bsa_attention(ctypes.byref(p), None, None, None, None, None, 4, None, None, 0, None) == OK
+    assert lib.dense_attention(ctypes.byref(p), None, None, None, None, None, 0, None) == OK
+
+
+def test_binding_raises_with_message():
+    p = _problem(head_dim=64)
+    with pytest.raises(B.BSAError, match="head_dim"):
+        B.bsa_select(p, B.SelectParams.topk(4), FAKE, FAKE, FAKE, FAKE, (FAKE, 1 << 40), stream=0)

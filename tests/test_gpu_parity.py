@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small problems are compared element by element over every query block;
+the full-size workloads compare every index row and a seeded sample of
+query blocks' outputs. Tolerances: index sets exact up to near-ties of
+1e-5 in pooled score; outputs max-abs <= 2e-2 and mean-abs <= 1e-3.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.bsa_oracle as O
+import parity as PT
+from video_dit_block_bsa_amd import WORKLOADS
+from video_dit_block_bsa_amd.binding import Problem, SelectParams
+from video_dit_block_bsa_amd.inputs import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(128)
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _run_and_compare(problem, params, q, k, v, all_outputs=True, sample=None, seed=0):
+    g = PT.geometry(problem)
+    sp = PT.oracle_params(params)
+    stride = O.index_stride(sp)
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    idx_d, cnt_d = PT.run_select(problem, params, qd, kd)
+    o_d = PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, stride)
+    idx = idx_d.cpu().numpy()
+    cnt = cnt_d.cpu().numpy()
+    out = PT.from_device(o_d).reshape(q.shape)
+    rows = PT.oracle_select_all(q, k, g, sp, SCALE)
+    exact, ties, fails = PT.check_selection(idx, cnt, rows, g, sp, stride)
+    _log(f"selection: {exact} exact rows, {ties} near-tie rows, {len(fails)} failures")
+    assert not fails, fails[:5]
+    nb = g.num_blocks
+    pairs = q.shape[0] * q.shape[1]
+    if all_outputs:
+        items = [(p, i) for p in range(pairs) for i in range(nb)]
+    else:
+        rng = np.random.default_rng(seed)
+        heads = sorted(rng.choice(pairs, size=min(sample[0], pairs), replace=False).tolist())
+        items = []
+        for p in heads:
+            blocks = set(rng.choice(nb, size=min(sample[1], nb), replace=False).tolist())
+            blocks |= {0, nb - 1}
+            if g.cond_blocks:
+                blocks |= {g.cond_blocks - 1, g.cond_blocks}
+            items += [(p, i) for i in sorted(blocks)]
+    mx, mean, nvals = PT.compare_outputs(
+        out, q, k, v, g, lambda p, i: idx[p * nb + i, : cnt[p * nb + i]], SCALE, items)
+    _log(f"outputs: max-abs {mx:.3e}, mean-abs {mean:.3e} over {nvals} values")
+    assert mx <= PT.MAX_ABS and mean <= PT.MEAN_ABS
+    return idx, cnt, out, o_d
+
+
+def test_tiny_topk2():
+    w = WORKLOADS["tiny"]
+    q, k, v = make_qkv(w.T, w.H, w.W, w.heads, kind=w.kind, seed=w.seed)
+    _run_and_compare(Problem.from_workload(w), SelectParams.topk(2), q, k, v)
+
+
+def test_tiny_all_blocks_equals_dense():
+    """k = all blocks: BSA equals the oracle's dense attention and the GPU's
+    own dense kernel."""
+    w = WORKLOADS["tiny"]
+    q, k, v = make_qkv(w.T, w.H, w.W, w.heads, kind=w.kind, seed=w.seed)
+    problem = Problem.from_workload(w)
+    _, _, out, o_sparse = _run_and_compare(problem, SelectParams.topk(4), q, k, v)
+    g = PT.geometry(problem)
+    o_dense = PT.run_dense(problem, PT.to_device(q), PT.to_device(k), PT.to_device(v))
+    dense = PT.from_device(o_dense).reshape(q.shape)
+    for h in range(w.heads):
+        ref = O.dense_head(O.bf16_bits_to_f64(q[0, h]), O.bf16_bits_to_f64(k[0, h]),
+                           O.bf16_bits_to_f64(v[0, h]), g, SCALE)
+        err = np.abs(O.bf16_bits_to_f64(dense[0, h]) - ref)
+        assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS
+    # same tile engine, same key order: the two GPU results agree bitwise
+    assert np.array_equal(dense, out)
+
+
+@pytest.mark.parametrize(
+    "grid,heads,k",
+    [((8, 12, 40), 3, 5),     # 30 blocks: fewer than one 64-wide selection chunk
+     ((12, 16, 48), 2, 7),    # 72 blocks: a ragged second chunk
+     ((4, 4, 8), 2, 3)],      # a single block: k clamps to 1
+)
+def test_small_field_topk(grid, heads, k):
+    T, H, W = grid
+    q, k_, v = make_qkv(T, H, W, heads, kind="field", seed=T * 100 + W)
+    _run_and_compare(Problem.make(T, H, W, heads), SelectParams.topk(k), q, k_, v)
+
+
+def test_small_cdf_block_causal():
+    T, H, W = 12, 16, 32  # 48 blocks, 16 condition blocks
+    q, k, v = make_qkv(T, H, W, 2, kind="field", seed=77)
+    problem = Problem.make(T, H, W, 2, cond_frames=4)
+    idx, cnt, _, _ = _run_and_compare(problem, SelectParams.cdf(0.9, 2, 12), q, k, v)
+    assert cnt.min() >= 2 and cnt.max() <= 12
+
+
+def test_small_topk_block_causal_clamp():
+    """k above the condition block count clamps condition rows."""
+    T, H, W = 8, 8, 16  # 8 blocks, 4 condition blocks
+    q, k, v = make_qkv(T, H, W, 2, kind="iid", seed=78)
+    problem = Problem.make(T, H, W, 2, cond_frames=4)
+    idx, cnt, _, _ = _run_and_compare(problem, SelectParams.topk(6), q, k, v)
+    cnt = cnt.reshape(2, 8)
+    assert np.all(cnt[:, :4] == 4) and np.all(cnt[:, 4:] == 6)
+
+
+def test_q_zero_closed_form():
+    """Q = 0: all pooled scores tie, so blocks 0..k-1 are kept and every query
+    averages V over their tokens."""
+    T, H, W, heads, kk = 8, 16, 16, 2, 3
+    _, k, v = make_qkv(T, H, W, heads, kind="iid", seed=5)
+    q = np.zeros_like(k)
+    problem = Problem.make(T, H, W, heads)
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    idx_d, cnt_d = PT.run_select(problem, SelectParams.topk(kk), qd, kd)
+    idx = idx_d.cpu().numpy()
+    assert np.all(idx == np.arange(kk)) and np.all(cnt_d.cpu().numpy() == kk)
+    out = O.bf16_bits_to_f64(PT.from_device(PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, kk)))
+    g = PT.geometry(problem)
+    perm = O.block_token_order(g)
+    for h in range(heads):
+        vv = O.bf16_bits_to_f64(v[0, h])
+        mean_v = vv[perm[: kk * g.n]].mean(axis=0)
+        err = np.abs(out.reshape(q.shape)[0, h] - mean_v)
+        assert err.max() < 8e-3
+
+
+def test_constant_v():
+    """V constant: every output equals it (weights sum to one)."""
+    T, H, W, heads = 8, 16, 16, 2
+    q, k, _ = make_qkv(T, H, W, heads, kind="iid", seed=6)
+    v = np.full_like(q, 0x3F00)  # bf16 0.5
+    problem = Problem.make(T, H, W, heads)
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    idx_d, cnt_d = PT.run_select(problem, SelectParams.topk(5), qd, kd)
+    out = O.bf16_bits_to_f64(PT.from_device(PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, 5)))
+    assert np.abs(out - 0.5).max() < 4e-3
+
+
+def test_deterministic():
+    T, H, W, heads = 8, 16, 24, 2
+    q, k, v = make_qkv(T, H, W, heads, kind="field", seed=8)
+    problem = Problem.make(T, H, W, heads, cond_frames=4)
+    params = SelectParams.cdf(0.8, 1, 6)
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    res = []
+    for _ in range(2):
+        idx_d, cnt_d = PT.run_select(problem, params, qd, kd)
+        o = PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, 6)
+        res.append((idx_d.cpu().numpy(), cnt_d.cpu().numpy(), PT.from_device(o)))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a, b)
+
+
+def test_block_causal_independence():
+    """Condition rows' indices and outputs do not change, bit for bit, when
+    every noisy token's Q, K and V is replaced."""
+    T, H, W, heads = 12, 16, 16, 2
+    q, k, v = make_qkv(T, H, W, heads, kind="field", seed=9)
+    q2, k2, v2 = make_qkv(T, H, W, heads, kind="field", seed=10)
+    cond_tokens = 4 * H * W
+    for a, b in ((q2, q), (k2, k), (v2, v)):
+        a[:, :, :cond_tokens] = b[:, :, :cond_tokens]
+    problem = Problem.make(T, H, W, heads, cond_frames=4)
+    params = SelectParams.topk(4)
+    outs = []
+    for qq, kk, vv in ((q, k, v), (q2, k2, v2)):
+        qd, kd, vd = PT.to_device(qq), PT.to_device(kk), PT.to_device(vv)
+        idx_d, cnt_d = PT.run_select(problem, params, qd, kd)
+        o = PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, 4)
+        outs.append((idx_d.cpu().numpy().reshape(heads, -1, 4), PT.from_device(o)))
+    nb_cond = 4  # (4/4) * (16/4) * (16/8)
+    assert np.array_equal(outs[0][0][:, :nb_cond], outs[1][0][:, :nb_cond])
+    assert np.array_equal(outs[0][1][:, :, :cond_tokens], outs[1][1][:, :, :cond_tokens])
+
+
+def test_skips_invalid_ids_and_clamps_cnt():
+    """bsa_attention skips ids outside [0, Nb) and clamps cnt to the stride;
+    a row with no valid block gives zeros."""
+    import torch
+
+    T, H, W, heads = 8, 8, 16, 1
+    q, k, v = make_qkv(T, H, W, heads, kind="iid", seed=12)
+    problem = Problem.make(T, H, W, heads)
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    idx = torch.tensor([[0, 5, -3, 2], [99, -1, -1, -1], [1, 3, 0, 0], [7, 6, 5, 4],
+                        [4, 4, 4, 4], [0, 1, 2, 3], [2, 2, 2, 2], [3, 1, 0, 2]],
+                       dtype=torch.int32, device="cuda")
+    cnt = torch.tensor([4, 1, 2, 9, 0, -5, 1, 4], dtype=torch.int32, device="cuda")
+    out = O.bf16_bits_to_f64(PT.from_device(PT.run_attention(problem, qd, kd, vd, idx, cnt, 4)))
+    g = PT.geometry(problem)
+    perm = O.block_token_order(g)
+    qf, kf, vf = (O.bf16_bits_to_f64(a[0, 0]) for a in (q, k, v))
+    want_blocks = {0: [0, 5, 2], 2: [1, 3], 3: [7, 6, 5, 4], 6: [2], 7: [3, 1, 0, 2]}
+    for i in range(g.num_blocks):
+        got = out[0, 0][perm[i * g.n : (i + 1) * g.n]]
+        if i in want_blocks:
+            ref = O.attend_query_block(qf, kf, vf, g, i, want_blocks[i], SCALE, perm)
+            assert np.abs(got - ref).max() <= PT.MAX_ABS
+        else:
+            assert np.all(got == 0.0)
+
+
+@pytest.mark.parametrize("name", ["480p", "720p", "long", "vc"])
+def test_full_size_workload(name):
+    """Full-size workloads in the configuration the benchmark times: every
+    index row against the oracle, outputs on a seeded sample."""
+    w = WORKLOADS[name]
+    _log(f"generating {name}: {w.T}x{w.H}x{w.W}, {w.heads} heads")
+    q, k, v = make_qkv(w.T, w.H, w.W, w.heads, kind=w.kind, seed=w.seed)
+    _, cnt, _, _ = _run_and_compare(Problem.from_workload(w), SelectParams.from_workload(w),
+                                    q, k, v, all_outputs=False, sample=(4, 10), seed=w.seed)
+    if w.mode == "cdf":
+        _log(f"CDF counts: min {cnt.min()}, mean {cnt.mean():.2f}, max {cnt.max()}")
+        assert cnt.min() >= w.k_min and cnt.max() <= w.k_max
+
+
+def test_dense_720p_sampled():
+    """Dense baseline at 720p x 93f on sampled query blocks."""
+    w = WORKLOADS["720p"]
+    q, k, v = make_qkv(w.T, w.H, w.W, w.heads, kind=w.kind, seed=w.seed, head_subset=[0, 17])
+    problem = Problem.make(w.T, w.H, w.W, 2)
+    o = PT.from_device(PT.run_dense(problem, PT.to_device(q), PT.to_device(k), PT.to_device(v)))
+    g = PT.geometry(problem)
+    items = [(p, i) for p in range(2) for i in (0, 1, 359, 719)]
+    mx, mean, _ = PT.compare_outputs(o.reshape(q.shape), q, k, v, g,
+                                     lambda p, i: range(g.num_blocks), SCALE, items)
+    _log(f"dense 720p: max-abs {mx:.3e}, mean-abs {mean:.3e}")
+    assert mx <= PT.MAX_ABS and mean <= PT.MEAN_ABS

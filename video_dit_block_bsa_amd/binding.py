@@ -1,0 +1,189 @@
+"""ctypes binding over libbsa.so (C ABI in include/bsa.h).
+
+Argument marshalling only: every function here turns Python objects into
+the pointers and sizes of the C entry point of the same name and raises
+``BSAError`` on a non-OK status. Device buffers may be torch tensors (their
+``data_ptr()`` is passed) or raw integer device addresses. ``stream`` is a
+``torch.cuda.Stream``, a raw hipStream_t integer, or None for torch's current
+stream. The library must have been built (``python -m
+video_dit_block_bsa_amd.build``); nothing here falls back to other code.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
+
+BSA_TOPK = 0
+BSA_CDF = 1
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``bsa_problem``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("T", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("W", ctypes.c_int32),
+        ("ct", ctypes.c_int32),
+        ("ch", ctypes.c_int32),
+        ("cw", ctypes.c_int32),
+        ("cond_frames", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+    @classmethod
+    def make(cls, T, H, W, heads, batch=1, head_dim=128, chunk=(4, 4, 8), cond_frames=0,
+             scale=0.0):
+        return cls(batch, heads, head_dim, T, H, W, chunk[0], chunk[1], chunk[2], cond_frames,
+                   scale)
+
+    @classmethod
+    def from_workload(cls, w):
+        return cls.make(w.T, w.H, w.W, w.heads, w.batch, w.head_dim, w.chunk, w.cond_frames)
+
+    @property
+    def seq_len(self):
+        return self.T * self.H * self.W
+
+    @property
+    def num_blocks(self):
+        return (self.T // self.ct) * (self.H // self.ch) * (self.W // self.cw)
+
+
+class SelectParams(ctypes.Structure):
+    """Mirror of ``bsa_select_params``."""
+
+    _fields_ = [
+        ("mode", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("cdf_p", ctypes.c_float),
+        ("k_min", ctypes.c_int32),
+        ("k_max", ctypes.c_int32),
+    ]
+
+    @classmethod
+    def topk(cls, k):
+        return cls(BSA_TOPK, k, 0.0, 0, 0)
+
+    @classmethod
+    def cdf(cls, p, k_min, k_max):
+        return cls(BSA_CDF, 0, p, k_min, k_max)
+
+    @classmethod
+    def from_workload(cls, w):
+        return cls.topk(w.k) if w.mode == "topk" else cls.cdf(w.p, w.k_min, w.k_max)
+
+
+class BSAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libbsa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m video_dit_block_bsa_amd.build`"
+            )
+        L = ctypes.CDLL(_LIB_PATH)
+        P, SP = ctypes.POINTER(Problem), ctypes.POINTER(SelectParams)
+        vp, i32p = ctypes.c_void_p, ctypes.c_void_p
+        L.bsa_index_stride.argtypes = [SP]
+        L.bsa_index_stride.restype = ctypes.c_int32
+        L.bsa_select_workspace_bytes.argtypes = [P, SP]
+        L.bsa_select_workspace_bytes.restype = ctypes.c_size_t
+        L.bsa_attention_workspace_bytes.argtypes = [P]
+        L.bsa_attention_workspace_bytes.restype = ctypes.c_size_t
+        L.bsa_select.argtypes = [P, SP, vp, vp, i32p, i32p, vp, ctypes.c_size_t, vp]
+        L.bsa_select.restype = ctypes.c_int32
+        L.bsa_attention.argtypes = [P, vp, vp, vp, i32p, i32p, ctypes.c_int32, vp, vp,
+                                    ctypes.c_size_t, vp]
+        L.bsa_attention.restype = ctypes.c_int32
+        L.dense_attention.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.dense_attention.restype = ctypes.c_int32
+        L.bsa_status_string.argtypes = [ctypes.c_int32]
+        L.bsa_status_string.restype = ctypes.c_char_p
+        L.bsa_last_error.argtypes = []
+        L.bsa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _nbytes(x):
+    if x is None:
+        return 0
+    if isinstance(x, tuple):
+        return x[1]
+    return x.numel() * x.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status):
+    if status != 0:
+        L = lib()
+        msg = L.bsa_last_error().decode() or L.bsa_status_string(status).decode()
+        raise BSAError(status, msg)
+
+
+def index_stride(params: SelectParams) -> int:
+    return lib().bsa_index_stride(ctypes.byref(params))
+
+
+def select_workspace_bytes(problem: Problem, params: SelectParams) -> int:
+    return lib().bsa_select_workspace_bytes(ctypes.byref(problem), ctypes.byref(params))
+
+
+def attention_workspace_bytes(problem: Problem) -> int:
+    return lib().bsa_attention_workspace_bytes(ctypes.byref(problem))
+
+
+def bsa_select(problem, params, q, k, idx, cnt, workspace, stream=None):
+    """bsa_select: pooled scores and key-block selection -> idx, cnt.
+    ``workspace`` is a tensor or a (pointer, nbytes) tuple."""
+    ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
+    _check(lib().bsa_select(ctypes.byref(problem), ctypes.byref(params), _ptr(q), _ptr(k),
+                            _ptr(idx), _ptr(cnt), ws_ptr, _nbytes(workspace), _stream(stream)))
+
+
+def bsa_attention(problem, q, k, v, idx, cnt, idx_stride, o, workspace, stream=None):
+    """bsa_attention: attention restricted to the listed key blocks -> o."""
+    ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
+    _check(lib().bsa_attention(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                               _ptr(cnt), int(idx_stride), _ptr(o), ws_ptr, _nbytes(workspace),
+                               _stream(stream)))
+
+
+def dense_attention(problem, q, k, v, o, workspace, stream=None):
+    """dense_attention: softmax attention over every allowed key -> o."""
+    ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
+    _check(lib().dense_attention(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                 ws_ptr, _nbytes(workspace), _stream(stream)))

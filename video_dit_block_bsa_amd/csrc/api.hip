@@ -1,0 +1,238 @@
+// C ABI of libbsa.so (declared in include/bsa.h): argument checks, workspace
+// layout and kernel dispatch. Every check runs on the host before the first
+// launch, so a rejected call launches nothing and touches no device state.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bsa.h"
+#include "common.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+bsa_status fail(bsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bsa_status fail(bsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+constexpr int kMaxBlocks = 4096;  // select keeps a row's scores in registers
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Checked {
+  bsa::Geom g;
+  bool empty;
+};
+
+// Validates the problem and fills the kernel geometry.
+bsa_status check_problem(const bsa_problem* p, Checked* out) {
+  if (!p) return fail(BSA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 0 || p->heads < 0)
+    return fail(BSA_ERR_INVALID_ARG, "batch and heads must be >= 0");
+  if (p->T <= 0 || p->H <= 0 || p->W <= 0)
+    return fail(BSA_ERR_INVALID_ARG, "latent grid T, H, W must be positive");
+  if (p->ct <= 0 || p->ch <= 0 || p->cw <= 0)
+    return fail(BSA_ERR_INVALID_ARG, "chunk extents must be positive");
+  if (p->head_dim <= 0) return fail(BSA_ERR_INVALID_ARG, "head_dim must be positive");
+  if (p->head_dim != bsa::kHeadDim)
+    return fail(BSA_ERR_UNSUPPORTED, "head_dim %d: only 128 is implemented", p->head_dim);
+  if ((long)p->ct * p->ch * p->cw != bsa::kBlockTokens)
+    return fail(BSA_ERR_UNSUPPORTED, "chunk %dx%dx%d: blocks of exactly 128 tokens are implemented",
+                p->ct, p->ch, p->cw);
+  if (p->T % p->ct || p->H % p->ch || p->W % p->cw)
+    return fail(BSA_ERR_UNSUPPORTED, "grid %dx%dx%d is not divisible by chunk %dx%dx%d", p->T,
+                p->H, p->W, p->ct, p->ch, p->cw);
+  if (p->cond_frames < 0 || p->cond_frames % p->ct || (p->cond_frames && p->cond_frames >= p->T))
+    return fail(BSA_ERR_INVALID_ARG, "cond_frames %d must be a multiple of ct=%d and < T=%d",
+                p->cond_frames, p->ct, p->T);
+  if (!(p->scale == p->scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
+  const long S = (long)p->T * p->H * p->W;
+  if (S > (1L << 30)) return fail(BSA_ERR_UNSUPPORTED, "sequence of %ld tokens is too long", S);
+  const long bh = (long)p->batch * p->heads;
+  if (bh > (1L << 24)) return fail(BSA_ERR_UNSUPPORTED, "batch*heads = %ld is too large", bh);
+  bsa::Geom& g = out->g;
+  g.bh = (int)bh;
+  g.S = (int)S;
+  g.T = p->T;
+  g.H = p->H;
+  g.W = p->W;
+  g.ct = p->ct;
+  g.ch = p->ch;
+  g.cw = p->cw;
+  g.nH = p->H / p->ch;
+  g.nW = p->W / p->cw;
+  g.nb = (int)(S / bsa::kBlockTokens);
+  g.cond_blocks = (p->cond_frames / p->ct) * g.nH * g.nW;
+  g.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  out->empty = (bh == 0);
+  return BSA_OK;
+}
+
+bsa_status check_params(const bsa_select_params* sp) {
+  if (!sp) return fail(BSA_ERR_INVALID_ARG, "select params are NULL");
+  if (sp->mode == BSA_TOPK) {
+    if (sp->k < 1) return fail(BSA_ERR_INVALID_ARG, "top-k needs k >= 1 (got %d)", sp->k);
+  } else if (sp->mode == BSA_CDF) {
+    if (!(sp->cdf_p > 0.f && sp->cdf_p <= 1.f))
+      return fail(BSA_ERR_INVALID_ARG, "CDF threshold p must be in (0, 1]");
+    if (sp->k_min < 1 || sp->k_max < sp->k_min)
+      return fail(BSA_ERR_INVALID_ARG, "CDF needs 1 <= k_min <= k_max (got %d, %d)", sp->k_min,
+                  sp->k_max);
+  } else {
+    return fail(BSA_ERR_INVALID_ARG, "unknown selection mode %d", sp->mode);
+  }
+  return BSA_OK;
+}
+
+struct SelectLayout {
+  size_t qp, kp, s, total;
+};
+
+SelectLayout select_layout(const bsa::Geom& g) {
+  SelectLayout L;
+  const size_t pooled = align_up((size_t)g.bh * g.nb * bsa::kHeadDim * sizeof(float));
+  L.qp = 0;
+  L.kp = pooled;
+  L.s = 2 * pooled;
+  L.total = L.s + align_up((size_t)g.bh * g.nb * g.nb * sizeof(float));
+  return L;
+}
+
+size_t attention_ws(const bsa::Geom& g) {
+  return align_up((size_t)g.bh * g.S * bsa::kHeadDim * sizeof(bsa::bf16_bits));
+}
+
+bsa_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(BSA_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return BSA_OK;
+}
+
+bsa_status attention_common(const bsa_problem* problem, const void* q, const void* k,
+                            const void* v, const int32_t* idx, const int32_t* cnt,
+                            int32_t idx_stride, void* o, void* workspace,
+                            size_t workspace_bytes, void* stream, bool dense) {
+  Checked c;
+  bsa_status st = check_problem(problem, &c);
+  if (st != BSA_OK) return st;
+  if (c.empty) return BSA_OK;
+  if (!q || !k || !v || !o) return fail(BSA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BSA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (!dense) {
+    if (!idx || !cnt) return fail(BSA_ERR_INVALID_ARG, "idx and cnt must be non-NULL");
+    if (idx_stride < 1) return fail(BSA_ERR_INVALID_ARG, "idx_stride must be >= 1");
+  }
+  if (o == q || o == k || o == v) return fail(BSA_ERR_INVALID_ARG, "o must not alias q, k or v");
+  const size_t need = attention_ws(c.g);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "attention needs %zu workspace bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  auto* vt = reinterpret_cast<bsa::bf16_bits*>(workspace);
+  st = launched(bsa::launch_pack_v(c.g, static_cast<const bsa::bf16_bits*>(v), vt, s), "pack_v");
+  if (st != BSA_OK) return st;
+  return launched(bsa::launch_attention(c.g, static_cast<const bsa::bf16_bits*>(q),
+                                        static_cast<const bsa::bf16_bits*>(k), vt, idx, cnt,
+                                        dense ? 1 : idx_stride, dense,
+                                        static_cast<bsa::bf16_bits*>(o), s),
+                  "attention");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bsa_index_stride(const bsa_select_params* params) {
+  if (check_params(params) != BSA_OK) return -1;
+  return params->mode == BSA_TOPK ? params->k : params->k_max;
+}
+
+size_t bsa_select_workspace_bytes(const bsa_problem* problem, const bsa_select_params* params) {
+  Checked c;
+  if (check_problem(problem, &c) != BSA_OK || check_params(params) != BSA_OK) return 0;
+  return select_layout(c.g).total;
+}
+
+size_t bsa_attention_workspace_bytes(const bsa_problem* problem) {
+  Checked c;
+  if (check_problem(problem, &c) != BSA_OK) return 0;
+  return attention_ws(c.g);
+}
+
+bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* params,
+                      const void* q, const void* k, int32_t* idx, int32_t* cnt,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  Checked c;
+  bsa_status st = check_problem(problem, &c);
+  if (st != BSA_OK) return st;
+  st = check_params(params);
+  if (st != BSA_OK) return st;
+  if (c.empty) return BSA_OK;
+  if (c.g.nb > kMaxBlocks)
+    return fail(BSA_ERR_UNSUPPORTED, "%d blocks per head: selection supports at most %d", c.g.nb,
+                kMaxBlocks);
+  if (!q || !k || !idx || !cnt)
+    return fail(BSA_ERR_INVALID_ARG, "q, k, idx and cnt must be non-NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(BSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  const SelectLayout L = select_layout(c.g);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(BSA_ERR_WORKSPACE, "select needs %zu workspace bytes (got %zu)", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const int stride = params->mode == BSA_TOPK ? params->k : params->k_max;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qp = reinterpret_cast<float*>(ws + L.qp);
+  float* kp = reinterpret_cast<float*>(ws + L.kp);
+  float* sc = reinterpret_cast<float*>(ws + L.s);
+  st = launched(bsa::launch_pool(c.g, static_cast<const bsa::bf16_bits*>(q),
+                                 static_cast<const bsa::bf16_bits*>(k), qp, kp, s),
+                "pool");
+  if (st != BSA_OK) return st;
+  st = launched(bsa::launch_scores(c.g, qp, kp, sc, s), "scores");
+  if (st != BSA_OK) return st;
+  return launched(bsa::launch_select(c.g, sc, params->mode, params->k, params->cdf_p,
+                                     params->k_min, params->k_max, stride, idx, cnt, s),
+                  "select");
+}
+
+bsa_status bsa_attention(const bsa_problem* problem, const void* q, const void* k, const void* v,
+                         const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* o,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_common(problem, q, k, v, idx, cnt, idx_stride, o, workspace, workspace_bytes,
+                          stream, false);
+}
+
+bsa_status dense_attention(const bsa_problem* problem, const void* q, const void* k,
+                           const void* v, void* o, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return attention_common(problem, q, k, v, nullptr, nullptr, 1, o, workspace, workspace_bytes,
+                          stream, true);
+}
+
+const char* bsa_status_string(int32_t status) {
+  switch (status) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_INVALID_ARG: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported problem";
+    case BSA_ERR_WORKSPACE: return "workspace too small";
+    case BSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* bsa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal definitions shared by the HIP kernels of libbsa.so (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+constexpr int kHeadDim = 128;   // d
+constexpr int kBlockTokens = 128;  // ct*ch*cw
+constexpr int kThreads = 256;   // four wave64 per workgroup
+
+typedef uint16_t bf16_bits;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Geometry of one problem as the kernels see it.
+struct Geom {
+  int bh;           // batch * heads
+  int S;            // tokens per (batch, head)
+  int T, H, W;      // latent grid
+  int ct, ch, cw;   // chunk shape
+  int nH, nW;       // blocks along h and w
+  int nb;           // blocks per (batch, head)
+  int cond_blocks;  // leading condition key blocks (0 = no block-causal mask)
+  float scale;      // softmax scale
+};
+
+// Latent-order token of slot j (0..127) of block i: blocks run in
+// [nT, nH, nW] order and the slots of a block in [t, h, w] order.
+__device__ __forceinline__ int block_token(const Geom& g, int i, int j) {
+  const int bw = i % g.nW;
+  const int rest = i / g.nW;
+  const int bh = rest % g.nH;
+  const int bt = rest / g.nH;
+  const int iw = j % g.cw;
+  const int r2 = j / g.cw;
+  const int ih = r2 % g.ch;
+  const int it = r2 / g.ch;
+  return ((bt * g.ct + it) * g.H + bh * g.ch + ih) * g.W + bw * g.cw + iw;
+}
+
+// Number of leading key blocks query block i may see.
+__device__ __forceinline__ int allowed_blocks(const Geom& g, int i) {
+  return (g.cond_blocks > 0 && i < g.cond_blocks) ? g.cond_blocks : g.nb;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_pool(const Geom& g, const bf16_bits* q, const bf16_bits* k, float* qp,
+                       float* kp, hipStream_t stream);
+hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float* s,
+                         hipStream_t stream);
+hipError_t launch_select(const Geom& g, const float* s, int mode, int k, float p, int k_min,
+                         int k_max, int stride, int32_t* idx, int32_t* cnt,
+                         hipStream_t stream);
+hipError_t launch_pack_v(const Geom& g, const bf16_bits* v, bf16_bits* vt, hipStream_t stream);
+hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
+                            const bf16_bits* vt, const int32_t* idx, const int32_t* cnt,
+                            int stride, bool dense, bf16_bits* o, hipStream_t stream);
+
+}  // namespace bsa
