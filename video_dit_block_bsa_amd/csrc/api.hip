@@ -60,6 +60,10 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
   if (S > (1L << 30)) return fail(BSA_ERR_UNSUPPORTED, "sequence of %ld tokens is too long", S);
   const long bh = (long)p->batch * p->heads;
   if (bh > (1L << 24)) return fail(BSA_ERR_UNSUPPORTED, "batch*heads = %ld is too large", bh);
+  const long nb = S / bsa::kBlockTokens;
+  const long nhw = (long)(p->H / p->ch) * (p->W / p->cw);
+  if ((unsigned long)nb * (unsigned long)nhw >= (1ul << 32))
+    return fail(BSA_ERR_UNSUPPORTED, "block grid %ld x %ld is too large", nb, nhw);
   bsa::Geom& g = out->g;
   g.bh = (int)bh;
   g.S = (int)S;

@@ -37,8 +37,6 @@
 
 namespace bsa {
 
-constexpr int kPitch = kHeadDim + 8;  // LDS row pitch in bf16 elements
-
 __device__ __forceinline__ bf16x8 lds_frag(const bf16_bits* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -76,76 +74,150 @@ __device__ __forceinline__ int swap23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// Kernel arguments. Block ids are split into (bt, bh, bw) with multiply-high
+// division by magic numbers (exact for the ranges the host checks), so the
+// per-key-block address math stays on the scalar unit.
+struct AttnArgs {
+  Geom g;
+  const bf16_bits* q;
+  const bf16_bits* k;
+  const bf16_bits* vt;
+  const int32_t* idx;
+  const int32_t* cnt;
+  bf16_bits* o;
+  int stride;
+  int nq8;           // query blocks per head rounded up to a multiple of 8
+  uint32_t mag_nw;   // floor(2^32 / nW) + 1
+  uint32_t mag_nhw;  // floor(2^32 / (nH*nW)) + 1
+  float c_log2;      // scale * log2(e)
+};
+
+// Latent-order token of the first slot of block i.
+__device__ __forceinline__ int block_origin(const AttnArgs& a, int i) {
+  const Geom& g = a.g;
+  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhw);
+  const int rem = i - bt * g.nH * g.nW;
+  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nw);
+  const int bw = rem - bh * g.nW;
+  return ((bt * g.ct) * g.H + bh * g.ch) * g.W + bw * g.cw;
+}
+
+// Offset (in tokens) of slot j inside its block.
+__device__ __forceinline__ int slot_offset(const Geom& g, int j) {
+  const int iw = j % g.cw;
+  const int r2 = j / g.cw;
+  return ((r2 / g.ch) * g.H + r2 % g.ch) * g.W + iw;
+}
+
+// Softmax rescaling is lazy: the running max m (log2 units) is only moved
+// when a tile's max exceeds it by more than this, so most tiles skip the
+// O *= alpha pass. Probabilities stay <= 2^8, well inside fp32 and bf16.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Tiles live in LDS as 128 rows of 256 bytes (16 chunks of 16 bytes) with
+// no padding. Chunk c of row r is stored at chunk c ^ swz(r), where swz(r) is
+// swap23 of the row's low four bits. The MFMA operand reads of a wave touch
+// rows swap23(n) + const with the same logical chunk, which this spreads over
+// all 16 chunk positions: conflict-free. Each direct-to-LDS load writes 64
+// lanes x 16 bytes = 4 whole rows, so lane L of a load writes physical chunk
+// L % 16 of row base + L / 16 and fetches the logical chunk that lands there.
+__device__ __forceinline__ int swz(int row) { return swap23(row & 15); }
+
 template <bool kDense>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(
-    Geom g, const bf16_bits* __restrict__ q, const bf16_bits* __restrict__ k,
-    const bf16_bits* __restrict__ vt, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ cnt, int stride, bf16_bits* __restrict__ o, int nq8,
-    float c_log2) {
-  __shared__ __attribute__((aligned(16))) bf16_bits ks[kBlockTokens * kPitch];
-  __shared__ __attribute__((aligned(16))) bf16_bits vs[kHeadDim * kPitch];
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) bf16_bits ks[kBlockTokens * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits vs[kHeadDim * kBlockTokens];
+  const Geom& g = a.g;
 
   // XCD-aware remap: hardware id x runs on XCD x % 8; give XCD c the query
   // blocks [c*chunk, (c+1)*chunk) of the current head.
   const int x = blockIdx.x;
-  const int pair = x / nq8;
-  const int r = x - pair * nq8;
-  const int chunk = nq8 >> 3;
+  const int pair = x / a.nq8;
+  const int r = x - pair * a.nq8;
+  const int chunk = a.nq8 >> 3;
   const int qb = (r & 7) * chunk + (r >> 3);
   if (qb >= g.nb) return;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int w = t >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n = lane & 31;
   const int gs = lane >> 5;
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
-  const bf16_bits* qh = q + hoff;
-  const bf16_bits* kh = k + hoff;
-  const bf16_bits* vth = vt + hoff;
-  bf16_bits* oh = o + hoff;
+  const char* kh = reinterpret_cast<const char*>(a.k + hoff);
+  const char* vth = reinterpret_cast<const char*>(a.vt + hoff);
 
-  const int qtok = block_token(g, qb, 32 * w + n);
+  const int qtok = block_origin(a, qb) + slot_offset(g, 32 * w + n);
   bf16x8 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     qf[s] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(qh + (size_t)qtok * kHeadDim + 16 * s + 8 * gs));
+        bf16x8, *reinterpret_cast<const u32x4*>(a.q + hoff + (size_t)qtok * kHeadDim + 16 * s + 8 * gs));
+
+  // This wave stages rows 32w .. 32w+31 of each tile: 8 loads of 4 rows.
+  uint32_t koff[8], voff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 32 * w + 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);
+    koff[i] = (uint32_t)slot_offset(g, row) * (kHeadDim * 2) + c * 16;
+    voff[i] = (uint32_t)row * (kBlockTokens * 2) + c * 16;
+  }
+  char* ks_w = reinterpret_cast<char*>(ks) + 32 * w * 256;
+  char* vs_w = reinterpret_cast<char*>(vs) + 32 * w * 256;
 
   int count;
   const int32_t* list = nullptr;
   if (kDense) {
     count = allowed_blocks(g, qb);
   } else {
-    list = idx + ((size_t)pair * g.nb + qb) * stride;
-    count = min(max(cnt[(size_t)pair * g.nb + qb], 0), stride);
+    list = a.idx + ((size_t)pair * g.nb + qb) * a.stride;
+    count = min(max(a.cnt[(size_t)pair * g.nb + qb], 0), a.stride);
   }
+  // Next usable list position at or after `from` (ids outside [0, nb) are skipped).
+  auto next_valid = [&](int from) {
+    if (kDense) return from;
+    while (from < count) {
+      const int kb = list[from];
+      if (kb >= 0 && kb < g.nb) break;
+      ++from;
+    }
+    return from;
+  };
+  auto kb_at = [&](int pos) { return kDense ? pos : list[pos]; };
+  auto load_k = [&](int kb) {
+    const char* base = kh + (size_t)block_origin(a, kb) * (kHeadDim * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(base + koff[i], (lds_void*)(ks_w + i * 1024), 16, 0, 0);
+  };
+  auto load_v = [&](int kb) {
+    const char* base = vth + (size_t)kb * (kBlockTokens * kHeadDim * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(base + voff[i], (lds_void*)(vs_w + i * 1024), 16, 0, 0);
+  };
 
   f32x16 oacc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) oacc[u] = f32x16{};
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-  const int krow = swap23(n);
+  float m2 = -INFINITY;  // running max of score * c_log2
+  float l_part = 0.f;    // this lane's share of the softmax denominator
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int rowA = swap23(n);  // operand row of this lane inside a 32-row sub-tile
+  const int cx = n & 15;       // chunk swizzle of that row
 
-  for (int it = 0; it < count; ++it) {
-    const int kb = kDense ? it : list[it];
-    if (!kDense && (kb < 0 || kb >= g.nb)) continue;  // same value in every lane
+  int pos = next_valid(0);
+  if (pos < count) load_k(kb_at(pos));
+  while (pos < count) {
+    const int kb = kb_at(pos);
+    const int nxt = next_valid(pos + 1);
 
-    __syncthreads();  // the previous tiles are no longer being read
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int c = t + kThreads * rr;
-      const int row = c >> 4;
-      const int col = c & 15;
-      const int ktok = block_token(g, kb, row);
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kh + (size_t)ktok * kHeadDim + col * 8);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(
-          vth + ((size_t)kb * kHeadDim + row) * kBlockTokens + col * 8);
-      *reinterpret_cast<u32x4*>(&ks[row * kPitch + col * 8]) = kv;
-      *reinterpret_cast<u32x4*>(&vs[row * kPitch + col * 8]) = vv;
-    }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's K rows are in LDS
+    __builtin_amdgcn_s_barrier();        // all K rows in; every wave is done with vs
+    load_v(kb);
 
     // S^T = K Q^T for this wave's 32 queries and all 128 keys.
     f32x16 sacc[4];
@@ -154,62 +226,68 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
       sacc[tt] = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 a = lds_frag(&ks[(32 * tt + krow) * kPitch + 16 * s + 8 * gs]);
-        sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[tt], 0, 0, 0);
+        const bf16x8 af = lds_frag(&ks[(32 * tt + rowA) * kHeadDim + (((2 * s + gs) ^ cx) << 3)]);
+        sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[tt], 0, 0, 0);
       }
     }
 
-    // Online softmax for this lane's query.
+    // Online softmax for this lane's query (both lane halves agree on m2).
     float mx = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[tt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-    m_run = m_new;
-    const float mc = m_new * c_log2;
-    float rs = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c_log2;
+    const bool grow = mx > m2 + kRescaleSlack;
+    if (__ballot(grow) != 0ull) {
+      const float m_new = grow ? mx : m2;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - m_new);
+      m2 = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
+    }
     bf16x8 pf[8];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        f32x2 pr[4];
+        u32x4 packed;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + j], c_log2, -mc));
-          rs += pv;
-          pr[j >> 1][j & 1] = pv;
+        for (int j2 = 0; j2 < 4; ++j2) {
+          const f32x2 pr = {
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2], a.c_log2, -m2)),
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2 + 1], a.c_log2, -m2))};
+          const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
+          packed[j2] = __builtin_bit_cast(uint32_t, pb);
         }
-        bf16x2 b0 = __builtin_convertvector(pr[0], bf16x2);
-        bf16x2 b1 = __builtin_convertvector(pr[1], bf16x2);
-        bf16x2 b2 = __builtin_convertvector(pr[2], bf16x2);
-        bf16x2 b3 = __builtin_convertvector(pr[3], bf16x2);
-        u32x4 packed = {__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
-                        __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3)};
         pf[2 * tt + h] = __builtin_bit_cast(bf16x8, packed);
       }
     }
-    l_part = l_part * alpha + rs;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
 
-    // O^T += V^T P^T.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V^T rows are in LDS
+    __builtin_amdgcn_s_barrier();        // all V^T rows in; every wave is done with ks
+    if (nxt < count) load_k(kb_at(nxt));
+
+    // O^T += V^T P^T; operand row swap23(n) of each sub-tile is channel
+    // 32u + swap23(n), undone in the epilogue.
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 a = lds_frag(&vs[(32 * u + n) * kPitch + 16 * s + 8 * gs]);
-        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], oacc[u], 0, 0, 0);
+        const bf16x8 af = lds_frag(&vs[(32 * u + rowA) * kBlockTokens + (((2 * s + gs) ^ cx) << 3)]);
+        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[s], oacc[u], 0, 0, 0);
       }
     }
+    pos = nxt;
   }
 
   const float l = l_part + __shfl_xor(l_part, 32);
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-  bf16_bits* orow = oh + (size_t)qtok * kHeadDim;
+  bf16_bits* orow = a.o + hoff + (size_t)qtok * kHeadDim;
+  // Accumulator value i of sub-tile u is channel 32u + swap23(8(i/4) + 4gs + i%4)
+  // = 32u + 16(a4/2) + 8gs + 4(a4%2) + i%4 with a4 = i/4.
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -218,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
       const f32x2 hi = {oacc[u][4 * a4 + 2] * inv, oacc[u][4 * a4 + 3] * inv};
       const u32x2 packed = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
                             __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
-      *reinterpret_cast<u32x2*>(orow + 32 * u + 8 * a4 + 4 * gs) = packed;
+      *reinterpret_cast<u32x2*>(orow + 32 * u + 16 * (a4 >> 1) + 8 * gs + 4 * (a4 & 1)) = packed;
     }
   }
 }
@@ -232,15 +310,24 @@ hipError_t launch_pack_v(const Geom& g, const bf16_bits* v, bf16_bits* vt, hipSt
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                             const bf16_bits* vt, const int32_t* idx, const int32_t* cnt,
                             int stride, bool dense, bf16_bits* o, hipStream_t stream) {
-  const int nq8 = (g.nb + 7) / 8 * 8;
-  const float c_log2 = g.scale * 1.4426950408889634f;
-  dim3 grid((unsigned)((size_t)g.bh * nq8));
+  AttnArgs a;
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.vt = vt;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.o = o;
+  a.stride = stride;
+  a.nq8 = (g.nb + 7) / 8 * 8;
+  a.mag_nw = (uint32_t)(0x100000000ull / (uint64_t)g.nW + 1);
+  a.mag_nhw = (uint32_t)(0x100000000ull / (uint64_t)(g.nH * g.nW) + 1);
+  a.c_log2 = g.scale * 1.4426950408889634f;
+  dim3 grid((unsigned)((size_t)g.bh * a.nq8));
   if (dense)
-    hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kThreads), 0, stream, g, q, k, vt, idx, cnt,
-                       stride, o, nq8, c_log2);
+    hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kThreads), 0, stream, g, q, k, vt, idx,
-                       cnt, stride, o, nq8, c_log2);
+    hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
