@@ -220,12 +220,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     load_v(kb);
 
     // S^T = K Q^T for this wave's 32 queries and all 128 keys.
+    // Channel steps outermost: four independent accumulators between
+    // dependent MFMAs.
     f32x16 sacc[4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      sacc[tt] = f32x16{};
+    for (int tt = 0; tt < 4; ++tt) sacc[tt] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
         const bf16x8 af = lds_frag(&ks[(32 * tt + rowA) * kHeadDim + (((2 * s + gs) ^ cx) << 3)]);
         sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[tt], 0, 0, 0);
       }
@@ -273,9 +276,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     // O^T += V^T P^T; operand row swap23(n) of each sub-tile is channel
     // 32u + swap23(n), undone in the epilogue.
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int s = 0; s < 8; ++s) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int u = 0; u < 4; ++u) {
         const bf16x8 af = lds_frag(&vs[(32 * u + rowA) * kBlockTokens + (((2 * s + gs) ^ cx) << 3)]);
         oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[s], oacc[u], 0, 0, 0);
       }
