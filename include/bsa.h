@@ -97,9 +97,10 @@ int32_t bsa_index_stride(const bsa_select_params* params);
 size_t bsa_select_workspace_bytes(const bsa_problem* problem,
                                   const bsa_select_params* params);
 
-/* Bytes of device workspace bsa_attention and dense_attention need (V
- * repacked per block with head_dim as the outer index: 2*S*128 bytes per
- * (batch, head), plus alignment). Returns 0 on invalid arguments. */
+/* Bytes of device workspace bsa_attention and dense_attention need. The
+ * current kernels need none (0); the workspace arguments are kept so that a
+ * kernel that needs scratch can be added without changing the ABI. Returns 0
+ * on invalid arguments too. */
 size_t bsa_attention_workspace_bytes(const bsa_problem* problem);
 
 /* Block selection: pooling, pooled scores, softmax and top-k / CDF selection

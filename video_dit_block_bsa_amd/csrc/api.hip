@@ -112,9 +112,7 @@ SelectLayout select_layout(const bsa::Geom& g) {
   return L;
 }
 
-size_t attention_ws(const bsa::Geom& g) {
-  return align_up((size_t)g.bh * g.S * bsa::kHeadDim * sizeof(bsa::bf16_bits));
-}
+size_t attention_ws(const bsa::Geom&) { return 0; }
 
 bsa_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess)
@@ -139,16 +137,14 @@ bsa_status attention_common(const bsa_problem* problem, const void* q, const voi
   }
   if (o == q || o == k || o == v) return fail(BSA_ERR_INVALID_ARG, "o must not alias q, k or v");
   const size_t need = attention_ws(c.g);
-  if (!workspace || workspace_bytes < need)
+  if (workspace_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "attention needs %zu workspace bytes (got %zu)", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+                workspace_bytes);
+  (void)workspace;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  auto* vt = reinterpret_cast<bsa::bf16_bits*>(workspace);
-  st = launched(bsa::launch_pack_v(c.g, static_cast<const bsa::bf16_bits*>(v), vt, s), "pack_v");
-  if (st != BSA_OK) return st;
   return launched(bsa::launch_attention(c.g, static_cast<const bsa::bf16_bits*>(q),
-                                        static_cast<const bsa::bf16_bits*>(k), vt, idx, cnt,
+                                        static_cast<const bsa::bf16_bits*>(k),
+                                        static_cast<const bsa::bf16_bits*>(v), idx, cnt,
                                         dense ? 1 : idx_stride, dense,
                                         static_cast<bsa::bf16_bits*>(o), s),
                   "attention");

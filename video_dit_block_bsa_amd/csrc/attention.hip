@@ -3,11 +3,10 @@
 // keys of the selected blocks only) and its dense baseline, for gfx950.
 //
 // Work decomposition
-//   One workgroup (4 x wave64) per (batch*head, query block of 128 tokens);
-//   wave w owns queries 32w .. 32w+31 of the block. The workgroup walks the
-//   query block's key-block list; for each key block the 128 x 128 K tile and
-//   the 128 x 128 V^T tile are staged in LDS (rows padded to 272 bytes so the
-//   16-byte fragment reads of 32 consecutive rows hit distinct banks).
+//   One workgroup (4 x wave64) per (batch*head, query block of 128 tokens),
+//   two workgroups per CU; wave w owns queries 32w .. 32w+31 of the block.
+//   The workgroup walks the query block's key-block list; for each key block
+//   the 128 x 128 K and V tiles are staged in LDS as [token][channel] rows.
 //
 // Math per key block and wave (bf16 MFMA 32x32x16, fp32 accumulate)
 //   S^T = K Q^T     4 key sub-tiles x 8 channel steps = 32 MFMA. Q^T stays in
@@ -17,16 +16,21 @@
 //                   128 scores; the row max needs one exchange with lane^32.
 //                   exp2 with scale*log2(e) folded in.
 //   O^T += V^T P^T  4 channel sub-tiles x 8 key steps = 32 MFMA; P^T is taken
-//                   straight from the S^T accumulators (converted to bf16),
-//                   V^T rows come from LDS.
+//                   straight from the S^T accumulators (converted to bf16).
+//                   The V^T operand is read from the [key][channel] V tile
+//                   with gfx950's transposing LDS read (ds_read_b64_tr_b16),
+//                   two 4-key reads per fragment, so V needs no repacked copy.
 //   For the P^T registers to line up with natural key order, the K rows are
 //   read with bits 2 and 3 of the row index swapped: the accumulator of row m
 //   then holds key swap23(m), and the 8 values a lane contributes to one
 //   16-key MFMA step are consecutive keys.
 //
-// V^T comes from pack_v_kernel, which rewrites V per block as [channel][key]
-// (an 8 x 8 register transpose per thread). The attention epilogue divides
-// by the softmax sum and writes O in latent order.
+// Tiles reach LDS with direct-to-LDS loads (global_load_lds_dwordx4), no
+// VGPR staging: V of the current key block is fetched while S and the
+// softmax run, K of the next key block while P V runs. LDS rows are unpadded;
+// XOR swizzles on 16-byte chunks keep the operand reads free of bank
+// conflicts. The epilogue divides by the softmax sum and writes O in latent
+// order.
 //
 // Workgroup order is XCD-aware: MI355X dispatches consecutive workgroups
 // round-robin over its 8 XCDs, so the id is remapped to give each XCD a
@@ -41,35 +45,6 @@ __device__ __forceinline__ bf16x8 lds_frag(const bf16_bits* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-// V [S][d] in latent order -> V^T per block: vt[block][d][slot].
-__global__ __launch_bounds__(kThreads) void pack_v_kernel(Geom g, const bf16_bits* __restrict__ v,
-                                                          bf16_bits* __restrict__ vt) {
-  const int blk = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int t = threadIdx.x;
-  const int dg = t & 15;  // channels 8*dg .. 8*dg+7
-  const int kg = t >> 4;  // slots 8*kg .. 8*kg+7
-  const bf16_bits* src = v + (size_t)bh * g.S * kHeadDim;
-  u32x4 in[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int tok = block_token(g, blk, kg * 8 + e);
-    in[e] = *reinterpret_cast<const u32x4*>(src + (size_t)tok * kHeadDim + dg * 8);
-  }
-  bf16_bits* dst = vt + ((size_t)bh * g.nb + blk) * kBlockTokens * kHeadDim;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    u32x4 out;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const uint32_t lo = in[2 * a][r >> 1];
-      const uint32_t hi = in[2 * a + 1][r >> 1];
-      out[a] = (r & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    *reinterpret_cast<u32x4*>(dst + (size_t)(dg * 8 + r) * kBlockTokens + kg * 8) = out;
-  }
-}
-
 __device__ __forceinline__ int swap23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
@@ -81,7 +56,7 @@ struct AttnArgs {
   Geom g;
   const bf16_bits* q;
   const bf16_bits* k;
-  const bf16_bits* vt;
+  const bf16_bits* v;
   const int32_t* idx;
   const int32_t* cnt;
   bf16_bits* o;
@@ -125,6 +100,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 // L % 16 of row base + L / 16 and fetches the logical chunk that lands there.
 __device__ __forceinline__ int swz(int row) { return swap23(row & 15); }
 
+// V tiles are read four rows at a time (transposing reads); spreading rows
+// r..r+3 over the four 64-byte slots of a 256-byte row keeps them apart.
+__device__ __forceinline__ int swzv(int row) { return 4 * (row & 3); }
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
 template <bool kDense>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_bits ks[kBlockTokens * kHeadDim];
@@ -147,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const int gs = lane >> 5;
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
   const char* kh = reinterpret_cast<const char*>(a.k + hoff);
-  const char* vth = reinterpret_cast<const char*>(a.vt + hoff);
+  const char* vh = reinterpret_cast<const char*>(a.v + hoff);
 
   const int qtok = block_origin(a, qb) + slot_offset(g, 32 * w + n);
   bf16x8 qf[8];
@@ -163,7 +144,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     const int row = 32 * w + 4 * i + (lane >> 4);
     const int c = (lane & 15) ^ swz(row);
     koff[i] = (uint32_t)slot_offset(g, row) * (kHeadDim * 2) + c * 16;
-    voff[i] = (uint32_t)row * (kBlockTokens * 2) + c * 16;
+    const int cv = (lane & 15) ^ swzv(row);
+    voff[i] = (uint32_t)slot_offset(g, row) * (kHeadDim * 2) + cv * 16;
   }
   char* ks_w = reinterpret_cast<char*>(ks) + 32 * w * 256;
   char* vs_w = reinterpret_cast<char*>(vs) + 32 * w * 256;
@@ -194,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_global_load_lds(base + koff[i], (lds_void*)(ks_w + i * 1024), 16, 0, 0);
   };
   auto load_v = [&](int kb) {
-    const char* base = vth + (size_t)kb * (kBlockTokens * kHeadDim * 2);
+    const char* base = vh + (size_t)block_origin(a, kb) * (kHeadDim * 2);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_global_load_lds(base + voff[i], (lds_void*)(vs_w + i * 1024), 16, 0, 0);
@@ -208,6 +190,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int rowA = swap23(n);  // operand row of this lane inside a 32-row sub-tile
   const int cx = n & 15;       // chunk swizzle of that row
+  // Transposing V reads: in each group of 16 lanes, lane j points at key
+  // 16s + 8gs + (j%16)/4 (+4 for the second read) and channels
+  // 32u + 16*((lane/16)%2) + 4*(j%4) .. +3; lane i then receives channel
+  // 32u + (lane%32) of those four keys. Chunk c of V row r sits at c ^ swzv(r).
+  int vtr_base[4];
+  {
+    const int jj = lane & 15;
+    const int q = jj >> 2;
+    const int c0 = 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      vtr_base[u] = (8 * gs + q) * 256 + ((4 * u + c0) ^ (4 * q)) * 16 + 8 * (jj & 1);
+  }
 
   int pos = next_valid(0);
   if (pos < count) load_k(kb_at(pos));
@@ -269,17 +264,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       }
     }
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V^T rows are in LDS
-    __builtin_amdgcn_s_barrier();        // all V^T rows in; every wave is done with ks
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V rows are in LDS
+    __builtin_amdgcn_s_barrier();        // all V rows in; every wave is done with ks
     if (nxt < count) load_k(kb_at(nxt));
 
-    // O^T += V^T P^T; operand row swap23(n) of each sub-tile is channel
-    // 32u + swap23(n), undone in the epilogue.
+    // O^T += V^T P^T. The V tile is [key][channel] in LDS; each V^T operand
+    // fragment (channel 32u + lane%32, keys 16s + 8gs .. +7) is two
+    // transposing reads of four keys each.
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8 af = lds_frag(&vs[(32 * u + rowA) * kBlockTokens + (((2 * s + gs) ^ cx) << 3)]);
+        const char* p0 = reinterpret_cast<const char*>(vs) + vtr_base[u] + s * 16 * 256;
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0 + 4 * 256));
+        const bf16x8 af = __builtin_bit_cast(
+            bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
         oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[s], oacc[u], 0, 0, 0);
       }
     }
@@ -289,8 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const float l = l_part + __shfl_xor(l_part, 32);
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
   bf16_bits* orow = a.o + hoff + (size_t)qtok * kHeadDim;
-  // Accumulator value i of sub-tile u is channel 32u + swap23(8(i/4) + 4gs + i%4)
-  // = 32u + 16(a4/2) + 8gs + 4(a4%2) + i%4 with a4 = i/4.
+  // Accumulator value i of sub-tile u is channel 32u + 8(i/4) + 4gs + i%4.
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -299,25 +299,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       const f32x2 hi = {oacc[u][4 * a4 + 2] * inv, oacc[u][4 * a4 + 3] * inv};
       const u32x2 packed = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
                             __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2))};
-      *reinterpret_cast<u32x2*>(orow + 32 * u + 16 * (a4 >> 1) + 8 * gs + 4 * (a4 & 1)) = packed;
+      *reinterpret_cast<u32x2*>(orow + 32 * u + 8 * a4 + 4 * gs) = packed;
     }
   }
 }
 
-hipError_t launch_pack_v(const Geom& g, const bf16_bits* v, bf16_bits* vt, hipStream_t stream) {
-  dim3 grid(g.nb, g.bh);
-  hipLaunchKernelGGL(pack_v_kernel, grid, dim3(kThreads), 0, stream, g, v, vt);
-  return hipGetLastError();
-}
-
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
-                            const bf16_bits* vt, const int32_t* idx, const int32_t* cnt,
+                            const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
                             int stride, bool dense, bf16_bits* o, hipStream_t stream) {
   AttnArgs a;
   a.g = g;
   a.q = q;
   a.k = k;
-  a.vt = vt;
+  a.v = v;
   a.idx = idx;
   a.cnt = cnt;
   a.o = o;

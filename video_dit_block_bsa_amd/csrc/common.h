@@ -61,9 +61,8 @@ hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float*
 hipError_t launch_select(const Geom& g, const float* s, int mode, int k, float p, int k_min,
                          int k_max, int stride, int32_t* idx, int32_t* cnt,
                          hipStream_t stream);
-hipError_t launch_pack_v(const Geom& g, const bf16_bits* v, bf16_bits* vt, hipStream_t stream);
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
-                            const bf16_bits* vt, const int32_t* idx, const int32_t* cnt,
+                            const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
                             int stride, bool dense, bf16_bits* o, hipStream_t stream);
 
 }  // namespace bsa
