@@ -57,10 +57,11 @@ def traffic_for(workload_name: str):
     return w.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, blocks: int):
+def cpu_baseline(w, q, k, v, blocks: int, seconds: float):
     """Time the CPU oracle on one head: full selection for the head, then
-    attention for the first `blocks` query blocks. Selection time is prorated
-    to those blocks. Returns the baseline record."""
+    attention for query blocks 0, 1, ... until `blocks` are done or the
+    attention part has run for `seconds`. Selection time is prorated to the
+    blocks done. Returns the baseline record."""
     import numpy as np
 
     import oracle.bsa_oracle as O
@@ -83,9 +84,12 @@ def cpu_baseline(w, q, k, v, blocks: int):
     blocks = min(blocks, g.num_blocks)
     perm = O.block_token_order(g)
     t0 = time.perf_counter()
-    for i in range(blocks):
-        O.attend_query_block(qf, kf, vf, g, i, idx[i, : cnt[i]], scale, perm)
+    done = 0
+    while done < blocks and (done == 0 or time.perf_counter() - t0 < seconds):
+        O.attend_query_block(qf, kf, vf, g, done, idx[done, : cnt[done]], scale, perm)
+        done += 1
     t_att = time.perf_counter() - t0
+    blocks = done
     t = t_att + t_sel * blocks / g.num_blocks
     flops = 4.0 * g.n * g.n * w.head_dim * float(cnt[:blocks].sum())
     return {
@@ -108,8 +112,10 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--dense-steps", type=int, default=1,
                     help="timed dense_attention runs for the speedup figure (0 = skip)")
-    ap.add_argument("--cpu-blocks", type=int, default=320,
-                    help="query blocks in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--cpu-blocks", type=int, default=1 << 20,
+                    help="at most this many query blocks in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="stop the CPU oracle sample after this much attention time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first, so that "
                          "hardware byte counters can be calibrated against a known size")
@@ -207,7 +213,7 @@ def main():
     traffic = traffic_for(w.name)
     roofline = {
         "bound": "mfma",
-        "kernel": "bsa_attention (V repack + block-sparse flash attention)",
+        "kernel": "bsa_attention (block-sparse flash attention, attn_kernel<false>)",
         "achieved": round(att_tflops, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
@@ -221,7 +227,7 @@ def main():
         del qd, kd, vd
         torch.cuda.empty_cache()
         log("[bench] timing the CPU oracle sample ...")
-        cpu = cpu_baseline(w, q, k, v, args.cpu_blocks)
+        cpu = cpu_baseline(w, q, k, v, args.cpu_blocks, args.cpu_seconds)
         log(f"[bench] CPU oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads "
             f"({cpu['seconds']} s)")
 
