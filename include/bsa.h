@@ -71,7 +71,7 @@ typedef struct bsa_problem {
   int32_t batch;       /* >= 0 */
   int32_t heads;       /* >= 0 */
   int32_t head_dim;    /* must be 128 */
-  int32_t T, H, W;     /* latent grid, each > 0 */
+  int32_t T, H, W;     /* latent grid, each > 0; T*H*W < 2^24 */
   int32_t ct, ch, cw;  /* chunk shape; ct*ch*cw must be 128 and divide the grid */
   int32_t cond_frames; /* 0: no block-causal mask; else a multiple of ct, < T */
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(head_dim) */

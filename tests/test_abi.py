@@ -153,3 +153,14 @@ def test_binding_raises_with_message():
     p = _problem(head_dim=64)
     with pytest.raises(B.BSAError, match="head_dim"):
         B.bsa_select(p, B.SelectParams.topk(4), FAKE, FAKE, FAKE, FAKE, (FAKE, 1 << 40), stream=0)
+
+
+def test_sequence_limit():
+    # T*H*W must stay below 2^24 tokens (K/V of one head are addressed with
+    # 32-bit byte offsets); the check happens on the host, before any launch.
+    lib = B.lib()
+    ok = B.Problem.make(256, 256, 248, 1)          # 16,252,928 tokens
+    bad = B.Problem.make(256, 256, 256, 1)         # 2^24 tokens
+    assert lib.bsa_attention_workspace_bytes(ctypes.byref(ok)) == 0
+    r = lib.bsa_attention(ctypes.byref(bad), None, None, None, None, None, 1, None, None, 0, None)
+    assert r == -2 and b"too long" in lib.bsa_last_error()

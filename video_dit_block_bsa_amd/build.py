@@ -28,6 +28,10 @@ HIPCC_FLAGS = [
     "-Wall",
     # Packed fp32 VALU forms are kept out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results go to arch VGPRs: the attention kernel feeds its score
+    # accumulators straight to VALU softmax code, and AGPR results would cost
+    # a copy per value.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

@@ -57,7 +57,10 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
                 p->cond_frames, p->ct, p->T);
   if (!(p->scale == p->scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
   const long S = (long)p->T * p->H * p->W;
-  if (S > (1L << 30)) return fail(BSA_ERR_UNSUPPORTED, "sequence of %ld tokens is too long", S);
+  // The attention kernel addresses one (batch, head) of K or V (S x 256 bytes)
+  // through a buffer resource with a 32-bit size.
+  if (S >= (1L << 24))
+    return fail(BSA_ERR_UNSUPPORTED, "sequence of %ld tokens is too long (at most 2^24 - 1)", S);
   const long bh = (long)p->batch * p->heads;
   if (bh > (1L << 24)) return fail(BSA_ERR_UNSUPPORTED, "batch*heads = %ld is too large", bh);
   const long nb = S / bsa::kBlockTokens;

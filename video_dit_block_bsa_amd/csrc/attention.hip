@@ -5,8 +5,8 @@
 // Work decomposition
 //   One workgroup (4 x wave64) per (batch*head, query block of 128 tokens),
 //   two workgroups per CU; wave w owns queries 32w .. 32w+31 of the block.
-//   The workgroup walks the query block's key-block list; for each key block
-//   the 128 x 128 K and V tiles are staged in LDS as [token][channel] rows.
+//   The workgroup walks the query block's key-block list; K and V tiles are
+//   staged in LDS as [token][channel] rows, in half tiles of 64 keys.
 //
 // Math per key block and wave (bf16 MFMA 32x32x16, fp32 accumulate)
 //   S^T = K Q^T     4 key sub-tiles x 8 channel steps = 32 MFMA. Q^T stays in
@@ -25,25 +25,22 @@
 //   then holds key swap23(m), and the 8 values a lane contributes to one
 //   16-key MFMA step are consecutive keys.
 //
-// Tiles reach LDS with direct-to-LDS loads (global_load_lds_dwordx4), no
-// VGPR staging: V of the current key block is fetched while S and the
-// softmax run, K of the next key block while P V runs. LDS rows are unpadded;
-// XOR swizzles on 16-byte chunks keep the operand reads free of bank
-// conflicts. The epilogue divides by the softmax sum and writes O in latent
-// order.
+// Tiles reach LDS with direct-to-LDS buffer loads (buffer_load_dwordx4 ...
+// lds), no VGPR staging, through a ring of five half-tile slots described at
+// the kernel. LDS rows are unpadded; XOR swizzles on 16-byte chunks keep the
+// operand reads free of bank conflicts. The epilogue divides by the softmax
+// sum and writes O in latent order.
 //
 // Workgroup order is XCD-aware: MI355X dispatches consecutive workgroups
 // round-robin over its 8 XCDs, so the id is remapped to give each XCD a
-// contiguous run of query blocks of the same head (spatial neighbours select
-// overlapping key blocks, which then hit that XCD's L2), while all XCDs work
-// on the same head at a time (its K/V stay resident in the shared cache).
+// contiguous run of query blocks of the same head, while all XCDs work on the
+// same head at a time (its K/V, 110 MB at 215K tokens, stay resident in the
+// 256 MB Infinity Cache).
+#include <type_traits>
+
 #include "common.h"
 
 namespace bsa {
-
-__device__ __forceinline__ bf16x8 lds_frag(const bf16_bits* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
 
 __device__ __forceinline__ int swap23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -54,12 +51,6 @@ __device__ __forceinline__ int swap23(int m) {
 // per-key-block address math stays on the scalar unit.
 struct AttnArgs {
   Geom g;
-  const bf16_bits* q;
-  const bf16_bits* k;
-  const bf16_bits* v;
-  const int32_t* idx;
-  const int32_t* cnt;
-  bf16_bits* o;
   int stride;
   int nq8;           // query blocks per head rounded up to a multiple of 8
   uint32_t mag_nw;   // floor(2^32 / nW) + 1
@@ -91,13 +82,14 @@ constexpr float kRescaleSlack = 8.0f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Tiles live in LDS as 128 rows of 256 bytes (16 chunks of 16 bytes) with
-// no padding. Chunk c of row r is stored at chunk c ^ swz(r), where swz(r) is
-// swap23 of the row's low four bits. The MFMA operand reads of a wave touch
-// rows swap23(n) + const with the same logical chunk, which this spreads over
-// all 16 chunk positions: conflict-free. Each direct-to-LDS load writes 64
-// lanes x 16 bytes = 4 whole rows, so lane L of a load writes physical chunk
-// L % 16 of row base + L / 16 and fetches the logical chunk that lands there.
+// Half tiles live in LDS as 64 rows of 256 bytes (16 chunks of 16 bytes)
+// with no padding. Chunk c of row r is stored at chunk c ^ swz(r), where
+// swz(r) is swap23 of the row's low four bits. The MFMA operand reads of a
+// wave touch rows swap23(n) + const with the same logical chunk, which this
+// spreads over all 16 chunk positions: conflict-free. Each direct-to-LDS load
+// writes 64 lanes x 16 bytes = 4 whole rows, so lane L of a load writes
+// physical chunk L % 16 of row base + L / 16 and fetches the logical chunk
+// that lands there.
 __device__ __forceinline__ int swz(int row) { return swap23(row & 15); }
 
 // V tiles are read four rows at a time (transposing reads); spreading rows
@@ -106,10 +98,49 @@ __device__ __forceinline__ int swzv(int row) { return 4 * (row & 3); }
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
+constexpr int kHalfRows = kBlockTokens / 2;            // key rows per half tile
+constexpr int kSlots = 5;                               // half-tile ring per workgroup
+// Word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Joins the workgroup without a memory fence: a fence would also wait for
+// the tile loads still in flight into other slots. Callers wait for their
+// own loads with s_waitcnt first; the empty asm statements keep the compiler
+// from moving LDS accesses across the barrier.
+__device__ __forceinline__ void workgroup_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Tiles stream through a ring of five 16 KB half-tile slots in the order
+// K_0 lo, K_0 hi, V_0 lo, V_0 hi, K_1 lo, ... (lo = key rows 0..63). Phase p
+// (S^T and softmax of key block p/2 for even p, P V for odd p) reads half
+// tiles 2p and 2p+1 and, once every wave is past the barrier that opens it,
+// refills the two slots phase p-1 read with half tiles 2p+3 and 2p+4. Each
+// load is thus issued two phases before it is read, with three half tiles
+// (48 KB) in flight per workgroup. Slot of half tile n is n mod 5; every
+// slot is its own LDS object, and the phase loop is unrolled over the ten
+// phases after which the assignment repeats, so that each read names its
+// slot at compile time and never waits on loads into the other slots.
 template <bool kDense>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) bf16_bits ks[kBlockTokens * kHeadDim];
-  __shared__ __attribute__((aligned(1024))) bf16_bits vs[kHeadDim * kBlockTokens];
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(
+    AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
+    const bf16_bits* __restrict__ vp, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ cntp, bf16_bits* __restrict__ op) {
+  __shared__ __attribute__((aligned(1024))) bf16_bits slot0[kHalfRows * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits slot1[kHalfRows * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits slot2[kHalfRows * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits slot3[kHalfRows * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits slot4[kHalfRows * kHeadDim];
+  auto slot_ptr = [&](auto sc) -> bf16_bits* {
+    constexpr int sl = decltype(sc)::value;
+    if constexpr (sl == 0) return slot0;
+    else if constexpr (sl == 1) return slot1;
+    else if constexpr (sl == 2) return slot2;
+    else if constexpr (sl == 3) return slot3;
+    else return slot4;
+  };
   const Geom& g = a.g;
 
   // XCD-aware remap: hardware id x runs on XCD x % 8; give XCD c the query
@@ -127,36 +158,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const int n = lane & 31;
   const int gs = lane >> 5;
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
-  const char* kh = reinterpret_cast<const char*>(a.k + hoff);
-  const char* vh = reinterpret_cast<const char*>(a.v + hoff);
+  // K and V of this (batch, head) as buffer resources: a tile load takes one
+  // 32-bit lane offset, and anything past the head reads as zero.
+  const uint32_t head_bytes = (uint32_t)g.S * (kHeadDim * 2);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kp + hoff), (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vp + hoff), (short)0, head_bytes, kBufferWord3);
 
   const int qtok = block_origin(a, qb) + slot_offset(g, 32 * w + n);
   bf16x8 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
     qf[s] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(a.q + hoff + (size_t)qtok * kHeadDim + 16 * s + 8 * gs));
+        bf16x8, *reinterpret_cast<const u32x4*>(qp + hoff + (size_t)qtok * kHeadDim + 16 * s + 8 * gs));
+  // Q must be in registers before the first tile load is issued: a later
+  // wait for Q would also wait for every tile load in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  // This wave stages rows 32w .. 32w+31 of each tile: 8 loads of 4 rows.
-  uint32_t koff[8], voff[8];
+  // This wave stages rows 16w .. 16w+15 of each half tile: 4 loads of 4
+  // rows. The chunk sides are powers of two, so a slot's token offset is
+  // linear in the bits of its index and the upper half tile is the lower one
+  // shifted by the (uniform) offset of slot 64. K and V rows differ only in
+  // their chunk swizzle; the swizzles depend on the row's low four bits,
+  // which both halves share.
+  uint32_t koff[4], voff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 32 * w + 4 * i + (lane >> 4);
-    const int c = (lane & 15) ^ swz(row);
-    koff[i] = (uint32_t)slot_offset(g, row) * (kHeadDim * 2) + c * 16;
-    const int cv = (lane & 15) ^ swzv(row);
-    voff[i] = (uint32_t)slot_offset(g, row) * (kHeadDim * 2) + cv * 16;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * w + 4 * i + (lane >> 4);
+    const uint32_t rowoff = (uint32_t)slot_offset(g, row) * (kHeadDim * 2);
+    koff[i] = rowoff + (((lane & 15) ^ swz(row)) << 4);
+    voff[i] = rowoff + (((lane & 15) ^ swzv(row)) << 4);
   }
-  char* ks_w = reinterpret_cast<char*>(ks) + 32 * w * 256;
-  char* vs_w = reinterpret_cast<char*>(vs) + 32 * w * 256;
+  const uint32_t half_off = (uint32_t)slot_offset(g, kHalfRows) * (kHeadDim * 2);
 
   int count;
   const int32_t* list = nullptr;
   if (kDense) {
     count = allowed_blocks(g, qb);
   } else {
-    list = a.idx + ((size_t)pair * g.nb + qb) * a.stride;
-    count = min(max(a.cnt[(size_t)pair * g.nb + qb], 0), a.stride);
+    list = idx + ((size_t)pair * g.nb + qb) * a.stride;
+    count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
   }
   // Next usable list position at or after `from` (ids outside [0, nb) are skipped).
   auto next_valid = [&](int from) {
@@ -169,17 +211,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     return from;
   };
   auto kb_at = [&](int pos) { return kDense ? pos : list[pos]; };
-  auto load_k = [&](int kb) {
-    const char* base = kh + (size_t)block_origin(a, kb) * (kHeadDim * 2);
+  // Half tile e (0: K lo, 1: K hi, 2: V lo, 3: V hi) of key block kb into a slot.
+  auto load_half = [&](int kb, int e, bf16_bits* dst_slot) {
+    const uint32_t base = (uint32_t)block_origin(a, kb) * (kHeadDim * 2) + (e & 1) * half_off;
+    char* dst = reinterpret_cast<char*>(dst_slot) + 16 * w * 256;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(base + koff[i], (lds_void*)(ks_w + i * 1024), 16, 0, 0);
-  };
-  auto load_v = [&](int kb) {
-    const char* base = vh + (size_t)block_origin(a, kb) * (kHeadDim * 2);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(base + voff[i], (lds_void*)(vs_w + i * 1024), 16, 0, 0);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(e < 2 ? krs : vrs, (lds_void*)(dst + i * 1024), 16,
+                                               e < 2 ? koff[i] : voff[i], base, 0, 0);
   };
 
   f32x16 oacc[4];
@@ -188,108 +227,155 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   float m2 = -INFINITY;  // running max of score * c_log2
   float l_part = 0.f;    // this lane's share of the softmax denominator
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  const int rowA = swap23(n);  // operand row of this lane inside a 32-row sub-tile
-  const int cx = n & 15;       // chunk swizzle of that row
+  // K operand reads: lane n reads row swap23(n) of a 32-row sub-tile at
+  // logical chunk 2s + gs, stored at chunk (2s + gs) ^ (n & 15). In bytes that
+  // is ka0 ^ 32s (the XOR only touches bits 5..7, which ka0 keeps for it).
+  const int cx = n & 15;
+  const int ka0 = swap23(n) * 256 + ((cx >> 1) << 5) + ((gs ^ (cx & 1)) << 4);
   // Transposing V reads: in each group of 16 lanes, lane j points at key
   // 16s + 8gs + (j%16)/4 (+4 for the second read) and channels
   // 32u + 16*((lane/16)%2) + 4*(j%4) .. +3; lane i then receives channel
-  // 32u + (lane%32) of those four keys. Chunk c of V row r sits at c ^ swzv(r).
-  int vtr_base[4];
+  // 32u + (lane%32) of those four keys. Chunk c of V row r sits at c ^ swzv(r),
+  // which in bytes is va0 ^ 64u for channel sub-tile u.
+  int va0;
   {
     const int jj = lane & 15;
     const int q = jj >> 2;
     const int c0 = 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      vtr_base[u] = (8 * gs + q) * 256 + ((4 * u + c0) ^ (4 * q)) * 16 + 8 * (jj & 1);
+    va0 = (8 * gs + q) * 256 + 64 * q + 16 * c0 + 8 * (jj & 1);
   }
 
-  int pos = next_valid(0);
-  if (pos < count) load_k(kb_at(pos));
-  while (pos < count) {
-    const int kb = kb_at(pos);
-    const int nxt = next_valid(pos + 1);
-
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's K rows are in LDS
-    __builtin_amdgcn_s_barrier();        // all K rows in; every wave is done with vs
-    load_v(kb);
-
-    // S^T = K Q^T for this wave's 32 queries and all 128 keys.
-    // Channel steps outermost: four independent accumulators between
-    // dependent MFMAs.
-    f32x16 sacc[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) sacc[tt] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const bf16x8 af = lds_frag(&ks[(32 * tt + rowA) * kHeadDim + (((2 * s + gs) ^ cx) << 3)]);
-        sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[tt], 0, 0, 0);
-      }
-    }
-
-    // Online softmax for this lane's query (both lane halves agree on m2).
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[tt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c_log2;
-    const bool grow = mx > m2 + kRescaleSlack;
-    if (__ballot(grow) != 0ull) {
-      const float m_new = grow ? mx : m2;
-      const float alpha = __builtin_amdgcn_exp2f(m2 - m_new);
-      m2 = m_new;
-      l_part *= alpha;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
-    }
+  // Block positions: cur (the block of the current phase) and nxt (the one
+  // after it, or count).
+  int cur = next_valid(0);
+  if (cur < count) {
+    int nxt = next_valid(cur + 1);
+    // Half tiles 0, 1, 2 (K_0 lo, K_0 hi, V_0 lo) into slots 0, 1, 2.
+    load_half(kb_at(cur), 0, slot0);
+    load_half(kb_at(cur), 1, slot1);
+    load_half(kb_at(cur), 2, slot2);
     bf16x8 pf[8];
+
+    // Phase with index pm = p mod 10 (its slots are fixed at compile time).
+    // Returns false when the last block's P V phase is done.
+    auto phase = [&](auto pmc) -> bool {
+      constexpr int pm = decltype(pmc)::value;
+      constexpr bool is_s = (pm % 2) == 0;
+      constexpr int sa = (2 * pm) % kSlots, sb = (2 * pm + 1) % kSlots;
+      constexpr int sc = (2 * pm + 3) % kSlots, sd = (2 * pm + 4) % kSlots;
+      // Every phase issues exactly two half tiles (past the last block they
+      // repeat the current one and are never read), so at the start of phase
+      // p the loads in flight are always half tiles 2p, 2p+1, 2p+2: a fixed
+      // vmcnt lets the last of them stay in flight.
+      __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+      workgroup_barrier();
+      // Refill the slots of the previous phase with half tiles 2p+3, 2p+4:
+      // V_j hi and K_{j+1} lo in an S phase, K_{j+1} hi and V_{j+1} lo in a
+      // P V phase.
+      const int kb_next = kb_at(nxt < count ? nxt : cur);
+      if constexpr (is_s) {
+        load_half(kb_at(cur), 3, slot_ptr(std::integral_constant<int, sc>{}));
+        load_half(kb_next, 0, slot_ptr(std::integral_constant<int, sd>{}));
+      } else {
+        load_half(kb_next, 1, slot_ptr(std::integral_constant<int, sc>{}));
+        load_half(kb_next, 2, slot_ptr(std::integral_constant<int, sd>{}));
+      }
+      const char* lo = reinterpret_cast<const char*>(slot_ptr(std::integral_constant<int, sa>{}));
+      const char* hi = reinterpret_cast<const char*>(slot_ptr(std::integral_constant<int, sb>{}));
+      if constexpr (is_s) {
+        // S^T = K Q^T for this wave's 32 queries and all 128 keys, channel
+        // steps outermost (four independent accumulators between dependent
+        // MFMAs).
+        f32x16 sacc[4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+        for (int tt = 0; tt < 4; ++tt) sacc[tt] = f32x16{};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 packed;
+        for (int s = 0; s < 8; ++s) {
 #pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2) {
-          const f32x2 pr = {
-              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2], a.c_log2, -m2)),
-              __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2 + 1], a.c_log2, -m2))};
-          const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
-          l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
-          packed[j2] = __builtin_bit_cast(uint32_t, pb);
+          for (int tt = 0; tt < 4; ++tt) {
+            const char* kt = tt < 2 ? lo : hi;
+            const bf16x8 af =
+                *reinterpret_cast<const bf16x8*>(kt + 32 * (tt & 1) * 256 + (ka0 ^ (32 * s)));
+            sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[tt], 0, 0, 0);
+          }
         }
-        pf[2 * tt + h] = __builtin_bit_cast(bf16x8, packed);
-      }
-    }
-
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's V rows are in LDS
-    __builtin_amdgcn_s_barrier();        // all V rows in; every wave is done with ks
-    if (nxt < count) load_k(kb_at(nxt));
-
-    // O^T += V^T P^T. The V tile is [key][channel] in LDS; each V^T operand
-    // fragment (channel 32u + lane%32, keys 16s + 8gs .. +7) is two
-    // transposing reads of four keys each.
+        // Online softmax for this lane's query (both lane halves agree on m2).
+        float mx = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const char* p0 = reinterpret_cast<const char*>(vs) + vtr_base[u] + s * 16 * 256;
-        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0));
-        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0 + 4 * 256));
-        const bf16x8 af = __builtin_bit_cast(
-            bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[s], oacc[u], 0, 0, 0);
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[tt][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c_log2;
+        const bool grow = mx > m2 + kRescaleSlack;
+        if (__ballot(grow) != 0ull) {
+          const float m_new = grow ? mx : m2;
+          const float alpha = __builtin_amdgcn_exp2f(m2 - m_new);
+          m2 = m_new;
+          l_part *= alpha;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x4 packed;
+#pragma unroll
+            for (int j2 = 0; j2 < 4; ++j2) {
+              const f32x2 pr = {
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2], a.c_log2, -m2)),
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2 + 1], a.c_log2, -m2))};
+              const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+              l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
+              packed[j2] = __builtin_bit_cast(uint32_t, pb);
+            }
+            pf[2 * tt + h] = __builtin_bit_cast(bf16x8, packed);
+          }
+        }
+        return true;
+      } else {
+        // O^T += V^T P^T; the V^T operand of channel sub-tile u for key step
+        // s is two transposing reads of four keys each. The two halves are
+        // separate loops so that every read names one slot (through a select
+        // of two slots the compiler would wait for all tile loads in flight).
+        auto pv_half = [&](const char* vhalf, int s0) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const char* p0 = vhalf + (va0 ^ (64 * u)) + s * 16 * 256;
+              const short4_t vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0));
+              const short4_t vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0 + 4 * 256));
+              const bf16x8 af = __builtin_bit_cast(
+                  bf16x8, u32x4{__builtin_bit_cast(u32x2, vlo)[0], __builtin_bit_cast(u32x2, vlo)[1],
+                                __builtin_bit_cast(u32x2, vhi)[0], __builtin_bit_cast(u32x2, vhi)[1]});
+              oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[s0 + s], oacc[u], 0, 0, 0);
+            }
+          }
+        };
+        pv_half(lo, 0);
+        pv_half(hi, 4);
+        if (nxt >= count) return false;
+        cur = nxt;
+        nxt = next_valid(cur + 1);
+        return true;
       }
+    };
+    using std::integral_constant;
+    while (phase(integral_constant<int, 0>{}) && phase(integral_constant<int, 1>{}) &&
+           phase(integral_constant<int, 2>{}) && phase(integral_constant<int, 3>{}) &&
+           phase(integral_constant<int, 4>{}) && phase(integral_constant<int, 5>{}) &&
+           phase(integral_constant<int, 6>{}) && phase(integral_constant<int, 7>{}) &&
+           phase(integral_constant<int, 8>{}) && phase(integral_constant<int, 9>{})) {
     }
-    pos = nxt;
+    // The trailing loads are never read, but must land before the workgroup
+    // gives its LDS to the next one.
+    __builtin_amdgcn_s_waitcnt(0x0070);
   }
 
   const float l = l_part + __shfl_xor(l_part, 32);
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-  bf16_bits* orow = a.o + hoff + (size_t)qtok * kHeadDim;
+  bf16_bits* orow = op + hoff + (size_t)qtok * kHeadDim;
   // Accumulator value i of sub-tile u is channel 32u + 8(i/4) + 4gs + i%4.
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -309,12 +395,6 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
                             int stride, bool dense, bf16_bits* o, hipStream_t stream) {
   AttnArgs a;
   a.g = g;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.idx = idx;
-  a.cnt = cnt;
-  a.o = o;
   a.stride = stride;
   a.nq8 = (g.nb + 7) / 8 * 8;
   a.mag_nw = (uint32_t)(0x100000000ull / (uint64_t)g.nW + 1);
@@ -322,9 +402,9 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
   a.c_log2 = g.scale * 1.4426950408889634f;
   dim3 grid((unsigned)((size_t)g.bh * a.nq8));
   if (dense)
-    hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kThreads), 0, stream, a, q, k, v, idx, cnt, o);
   else
-    hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kThreads), 0, stream, a, q, k, v, idx, cnt, o);
   return hipGetLastError();
 }
 
