@@ -100,6 +100,31 @@ def test_small_field_topk(grid, heads, k):
     _run_and_compare(Problem.make(T, H, W, heads), SelectParams.topk(k), q, k_, v)
 
 
+@pytest.mark.parametrize(
+    "chunk,grid",
+    [((2, 8, 8), (6, 16, 24)),     # 36 blocks
+     ((8, 4, 4), (16, 12, 8)),     # 12 blocks, deep in time
+     ((1, 8, 16), (5, 16, 32)),    # 20 blocks, one frame per block
+     ((4, 8, 4), (8, 16, 12)),     # 12 blocks
+     ((1, 1, 128), (3, 4, 256))],  # 24 blocks, one row of 128 tokens each
+)
+def test_other_chunk_shapes(chunk, grid):
+    """Block shapes other than [4,4,8]: every power-of-two chunk of 128
+    tokens goes through the same tile-address arithmetic."""
+    T, H, W = grid
+    q, k, v = make_qkv(T, H, W, 2, kind="field", seed=sum(grid) + chunk[0])
+    problem = Problem.make(T, H, W, 2, chunk=chunk)
+    _run_and_compare(problem, SelectParams.topk(5), q, k, v)
+
+
+def test_batch_two_three_heads():
+    """batch > 1: rows and heads are laid out (batch, head, block)."""
+    T, H, W = 8, 16, 32  # 16 blocks
+    q, k, v = make_qkv(T, H, W, 3, batch=2, kind="field", seed=91)
+    problem = Problem.make(T, H, W, 3, batch=2, cond_frames=4)
+    _run_and_compare(problem, SelectParams.topk(6), q, k, v)
+
+
 def test_small_cdf_block_causal():
     T, H, W = 12, 16, 32  # 48 blocks, 16 condition blocks
     q, k, v = make_qkv(T, H, W, 2, kind="field", seed=77)

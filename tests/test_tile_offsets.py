@@ -1,0 +1,61 @@
+"""Host-side check of the address identities the attention kernel's tile
+loads rely on (CPU only; no device code runs here).
+
+The kernel stages a 128-token block as two half tiles of 64 rows; a wave of
+lane L stages rows 16w + 4i + L/16 of each half at physical 16-byte chunk
+L % 16. Instead of one offset register per load it keeps one lane offset and
+derives the others:
+* a row's token offset is linear in the bits of its slot index when the
+  chunk sides are powers of two, so slot(16w + 4i + r) = slot(16w + r) +
+  slot(4i), and the upper half is the lower one plus slot(64);
+* the K swizzle (logical chunk = physical ^ swap23(row & 15)) then reduces to
+  an XOR of the lane offset with 64 * sb(i), sb swapping the two bits of i;
+  the V swizzle (physical ^ 4 (row & 3)) does not depend on i.
+This test recomputes every offset directly from those definitions for all
+36 chunk shapes of 128 tokens and checks the derived form.
+"""
+
+import itertools
+
+
+def swap23(m):
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1)
+
+
+def slot(j, ct, ch, cw, H, W):
+    iw, r2 = j % cw, j // cw
+    return ((r2 // ch) * H + r2 % ch) * W + iw
+
+
+def chunk_shapes():
+    sides = [1 << e for e in range(8)]
+    return [(ct, ch, 128 // (ct * ch)) for ct, ch in itertools.product(sides, sides)
+            if 128 % (ct * ch) == 0]
+
+
+def test_all_chunk_shapes_are_counted():
+    assert len(chunk_shapes()) == 36
+
+
+def test_tile_offsets_from_one_lane_offset():
+    sb64 = [0, 128, 64, 192]
+    for ct, ch, cw in chunk_shapes():
+        H, W = ch * 3, cw * 5  # any grid the chunk divides
+        half = slot(64, ct, ch, cw, H, W) * 256
+        rows_s = [slot(4 * i, ct, ch, cw, H, W) * 256 for i in range(4)]
+        for w in range(4):
+            for lane in range(64):
+                r = lane >> 4
+                base = slot(16 * w + r, ct, ch, cw, H, W) * 256
+                k0 = base + (((lane & 15) ^ r) << 4)
+                v0 = base + (((lane & 15) ^ (4 * r)) << 4)
+                vx = 80 * r
+                assert v0 == k0 ^ vx
+                for h in range(2):
+                    for i in range(4):
+                        row = 64 * h + 16 * w + 4 * i + r
+                        rowoff = slot(row, ct, ch, cw, H, W) * 256
+                        k_direct = rowoff + (((lane & 15) ^ swap23(row & 15)) << 4)
+                        v_direct = rowoff + (((lane & 15) ^ (4 * (row & 3))) << 4)
+                        assert (k0 ^ sb64[i]) + rows_s[i] + h * half == k_direct
+                        assert v0 + rows_s[i] + h * half == v_direct

@@ -177,19 +177,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // This wave stages rows 16w .. 16w+15 of each half tile: 4 loads of 4
-  // rows. The chunk sides are powers of two, so a slot's token offset is
-  // linear in the bits of its index and the upper half tile is the lower one
-  // shifted by the (uniform) offset of slot 64. K and V rows differ only in
-  // their chunk swizzle; the swizzles depend on the row's low four bits,
-  // which both halves share.
-  uint32_t koff[4], voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * w + 4 * i + (lane >> 4);
-    const uint32_t rowoff = (uint32_t)slot_offset(g, row) * (kHeadDim * 2);
-    koff[i] = rowoff + (((lane & 15) ^ swz(row)) << 4);
-    voff[i] = rowoff + (((lane & 15) ^ swzv(row)) << 4);
-  }
+  // rows, load i covering rows 16w + 4i .. +3 (lane L: row 16w + 4i + L/16,
+  // physical chunk L%16). The chunk sides are powers of two, so a slot's
+  // token offset is linear in the bits of its index: the offset of row
+  // 16w + 4i + r is that of 16w + r plus the (uniform) offset of slot 4i, and
+  // the upper half tile is the lower one shifted by the offset of slot 64.
+  // The swizzles depend on the row's low four bits 4i + r: for K the logical
+  // chunk is (L%16) ^ r ^ 4*sb(i), with sb swapping the two bits of i; for V
+  // it is (L%16) ^ 4r. So one lane offset k0 serves every load: load i of K
+  // uses k0 ^ 64*sb(i), every load of V uses k0 ^ 80r, and the rest is scalar.
+  const int r_lane = lane >> 4;
+  const uint32_t k0 = (uint32_t)slot_offset(g, 16 * w + r_lane) * (kHeadDim * 2) +
+                      (uint32_t)(((lane & 15) ^ r_lane) << 4);
+  const uint32_t vx = 80u * (uint32_t)r_lane;  // ((L%16) ^ 4r) ^ ((L%16) ^ r), in bytes
   const uint32_t half_off = (uint32_t)slot_offset(g, kHalfRows) * (kHeadDim * 2);
 
   int count;
@@ -216,9 +216,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     const uint32_t base = (uint32_t)block_origin(a, kb) * (kHeadDim * 2) + (e & 1) * half_off;
     char* dst = reinterpret_cast<char*>(dst_slot) + 16 * w * 256;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      constexpr uint32_t sb64[4] = {0, 128, 64, 192};  // 64 * (i with its two bits swapped)
+      const uint32_t row_s = (uint32_t)slot_offset(g, 4 * i) * (kHeadDim * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(e < 2 ? krs : vrs, (lds_void*)(dst + i * 1024), 16,
-                                               e < 2 ? koff[i] : voff[i], base, 0, 0);
+                                               e < 2 ? (k0 ^ sb64[i]) : (k0 ^ vx), base + row_s, 0, 0);
+    }
   };
 
   f32x16 oacc[4];
