@@ -4,11 +4,12 @@
 // ct x ch x cw box of the latent grid.
 //
 // One workgroup per (batch*head, block). Thread t reads channel chunk
-// t % 16 (8 bf16 = 16 bytes) of tokens 8*(t/16) .. 8*(t/16)+7 of the block;
-// a wave's 64 lanes read 4 tokens x 256 contiguous bytes per load, so every
-// load is a full-row, coalesced access. Partial sums go through LDS and are
-// added in a fixed order, so the result is deterministic. HBM-bound: 2 x 32 KB
-// read and 2 x 512 B written per workgroup.
+// t % 16 (8 bf16 = 16 bytes) of tokens 8*(t/16) .. 8*(t/16)+7 of the block,
+// from Q and from K; a wave's 64 lanes read 4 tokens x 256 contiguous bytes
+// per load, so every load is a full-row, coalesced access. Partial sums go
+// through LDS and are added in a fixed order, so the result is deterministic
+// (and the same as summing the 8 tokens, then the 16 groups, in order).
+// HBM-bound: 2 x 32 KB read and 2 x 512 B written per workgroup.
 #include "common.h"
 
 namespace bsa {
@@ -17,7 +18,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Geom g, const bf16_bits*
                                                         const bf16_bits* __restrict__ k,
                                                         float* __restrict__ qp,
                                                         float* __restrict__ kp) {
-  __shared__ float part[16][kHeadDim + 4];
+  __shared__ float part[2][16][kHeadDim + 4];
   const int blk = blockIdx.x;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
@@ -25,33 +26,41 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Geom g, const bf16_bits*
   const int grp = t >> 4;
   const size_t head_off = (size_t)bh * g.S * kHeadDim;
 
+  // All 16 loads of this thread (8 tokens of Q, the same 8 of K) are issued
+  // before any is summed, so each thread keeps 256 bytes in flight.
+  u32x4 raw[2][8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const size_t off = head_off + (size_t)block_token(g, blk, grp * 8 + r) * kHeadDim + chunk * 8;
+    raw[0][r] = *reinterpret_cast<const u32x4*>(q + off);
+    raw[1][r] = *reinterpret_cast<const u32x4*>(k + off);
+  }
+#pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const bf16_bits* src = (which == 0 ? q : k) + head_off;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int tok = block_token(g, blk, grp * 8 + r);
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (size_t)tok * kHeadDim + chunk * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += bf16_to_f32(raw[e] & 0xffffu);
-        acc[2 * e + 1] += bf16_to_f32(raw[e] >> 16);
+        acc[2 * e] += bf16_to_f32(raw[which][r][e] & 0xffffu);
+        acc[2 * e + 1] += bf16_to_f32(raw[which][r][e] >> 16);
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part[grp][chunk * 8 + e] = acc[e];
-    __syncthreads();
-    if (t < kHeadDim) {
-      float s = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s += part[r][t];
-      float* dst = (which == 0 ? qp : kp);
-      dst[((size_t)bh * g.nb + blk) * kHeadDim + t] = s * (1.0f / kBlockTokens);
-    }
-    __syncthreads();
+    for (int e = 0; e < 8; ++e) part[which][grp][chunk * 8 + e] = acc[e];
   }
+  __syncthreads();
+  // Threads 0..127 finish Q, 128..255 finish K: channel t % 128, the 16
+  // partial sums added in a fixed order.
+  const int which = t >> 7;
+  const int c = t & (kHeadDim - 1);
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += part[which][r][c];
+  float* dst = (which == 0 ? qp : kp);
+  dst[((size_t)bh * g.nb + blk) * kHeadDim + c] = s * (1.0f / kBlockTokens);
 }
 
 hipError_t launch_pool(const Geom& g, const bf16_bits* q, const bf16_bits* k, float* qp,

@@ -4,10 +4,8 @@
 // Attention"; combined top-k/CDF clamps from the zhaifeiyue notes, section 3).
 //
 // scores_kernel: S = (Q_pool K_pool^T) * scale per (batch, head), fp32. A
-//   64 x 64 output tile per workgroup, both operand tiles staged in LDS with
-//   the channel index outermost so that each thread reads 4 consecutive rows
-//   with one 16-byte LDS load; 16 FMAs per pair of loads; fixed summation
-//   order over the 128 channels.
+//   64 x 64 output tile per workgroup, both operand tiles staged in LDS, fp32
+//   MFMA 32x32x2 with a fixed summation order over the 128 channels.
 // select_kernel: one wave64 per query-block row. The row's scores live in
 //   registers (lane l holds key blocks l, l+64, ...). Scores are mapped to
 //   order-preserving 32-bit keys; the k-th largest key is found by a 32-step
@@ -21,12 +19,19 @@
 namespace bsa {
 
 constexpr int kScoreTile = 64;
+constexpr int kScoreRow = kHeadDim + 4;  // padded LDS row (floats)
 
+// One 64 x 64 tile of S per workgroup; wave w computes the 32 x 32 sub-tile
+// (w / 2, w % 2) with fp32 MFMA 32x32x2 (exact fp32 products, fp32 sums).
+// Step kk of the 64 MFMAs contracts channels kk (lanes 0..31) and 64 + kk
+// (lanes 32..63): any pairing of channels works as long as both operands use
+// the same one, and this one lets a lane read four steps of its row with one
+// 16-byte LDS load. Row stride 132 floats keeps those loads conflict-free.
 __global__ __launch_bounds__(kThreads) void scores_kernel(Geom g, const float* __restrict__ qp,
                                                           const float* __restrict__ kp,
                                                           float* __restrict__ s) {
-  __shared__ float qs[kHeadDim][kScoreTile + 4];
-  __shared__ float ks[kHeadDim][kScoreTile + 4];
+  __shared__ __attribute__((aligned(16))) float qs[kScoreTile][kScoreRow];
+  __shared__ __attribute__((aligned(16))) float ks[kScoreTile][kScoreRow];
   const int bh = blockIdx.z;
   const int i0 = blockIdx.y * kScoreTile;
   const int j0 = blockIdx.x * kScoreTile;
@@ -34,55 +39,45 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(Geom g, const float* _
   const float* qb = qp + (size_t)bh * g.nb * kHeadDim;
   const float* kb = kp + (size_t)bh * g.nb * kHeadDim;
 
-  // Rows run fastest across lanes so that the transposed LDS stores are
-  // conflict-free; every loaded 16-byte piece is used.
+  // Stage both 64 x 128 operand tiles row-major; rows past nb are zero.
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int c = t + kThreads * r;
-    const int row = c & 63;
-    const int d4 = c >> 6;
+    const int row = c >> 5;
+    const int d4 = c & 31;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i0 + row < g.nb) a = *reinterpret_cast<const float4*>(qb + (size_t)(i0 + row) * kHeadDim + d4 * 4);
     if (j0 + row < g.nb) b = *reinterpret_cast<const float4*>(kb + (size_t)(j0 + row) * kHeadDim + d4 * 4);
-    qs[d4 * 4 + 0][row] = a.x;
-    qs[d4 * 4 + 1][row] = a.y;
-    qs[d4 * 4 + 2][row] = a.z;
-    qs[d4 * 4 + 3][row] = a.w;
-    ks[d4 * 4 + 0][row] = b.x;
-    ks[d4 * 4 + 1][row] = b.y;
-    ks[d4 * 4 + 2][row] = b.z;
-    ks[d4 * 4 + 3][row] = b.w;
+    *reinterpret_cast<float4*>(&qs[row][d4 * 4]) = a;
+    *reinterpret_cast<float4*>(&ks[row][d4 * 4]) = b;
   }
   __syncthreads();
 
-  const int tx = t & 15;
-  const int ty = t >> 4;
-  float acc[4][4];
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int wr = w >> 1, wc = w & 1;
+  const int m = lane & 31;
+  const int h = lane >> 5;
+  const float* arow = &qs[32 * wr + m][64 * h];
+  const float* brow = &ks[32 * wc + m][64 * h];
+  f32x16 acc = {};
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
-#pragma unroll 8
-  for (int d = 0; d < kHeadDim; ++d) {
-    const float4 a = *reinterpret_cast<const float4*>(&qs[d][ty * 4]);
-    const float4 b = *reinterpret_cast<const float4*>(&ks[d][tx * 4]);
-    const float av[4] = {a.x, a.y, a.z, a.w};
-    const float bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_fmaf(av[x], bv[y], acc[x][y]);
+  for (int c = 0; c < 16; ++c) {
+    const float4 a = *reinterpret_cast<const float4*>(arow + 4 * c);
+    const float4 b = *reinterpret_cast<const float4*>(brow + 4 * c);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
   }
+  // Accumulator value v holds row 8(v/4) + 4h + v%4, column m of the sub-tile.
+  const int j = j0 + 32 * wc + m;
+  if (j < g.nb) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int i = i0 + ty * 4 + x;
-    if (i >= g.nb) continue;
-    float* dst = s + ((size_t)bh * g.nb + i) * g.nb;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int j = j0 + tx * 4 + y;
-      if (j < g.nb) dst[j] = acc[x][y] * g.scale;
+    for (int v = 0; v < 16; ++v) {
+      const int i = i0 + 32 * wr + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (i < g.nb) s[((size_t)bh * g.nb + i) * g.nb + j] = acc[v] * g.scale;
     }
   }
 }
