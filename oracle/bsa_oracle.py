@@ -45,6 +45,15 @@ with its reason in the design notes of the repository):
   over the allowed blocks only.
 * k larger than the number of allowed blocks is clamped to that number.
 
+Backward pass (the gradients of the attention step for fixed selections):
+[DeepDive] "Implementation details and design trade-offs" states that the
+operator has both a forward and a backward pass, and [Blog-CN] section 7
+("实现 cross-reference") lists separate dQ and dK/dV backward kernels and a
+forward-to-backward transpose of the block index lists. The pages print no
+backward formulas; ``backward_head`` differentiates the forward above
+(softmax over the gathered keys) by the chain rule, and treats the block
+selection as a constant (it is a discrete choice with no gradient).
+
 Every function works on one (batch, head) slice: arrays are [S, d] in the
 latent grid's own memory order (token s = (t*H + h)*W + w).
 """
@@ -71,6 +80,8 @@ __all__ = [
     "bsa_head",
     "dense_head",
     "index_stride",
+    "forward_lse_head",
+    "backward_head",
 ]
 
 
@@ -348,3 +359,74 @@ def dense_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Geometry, scale: 
             q, k, v, g, i, range(na), scale, perm
         )
     return out
+
+
+def _gathered(q, k, v, g, i, key_blocks, perm):
+    n = g.n
+    qt = perm[i * n : (i + 1) * n]
+    kt = np.concatenate([perm[j * n : (j + 1) * n] for j in key_blocks])
+    return qt, kt
+
+
+def forward_lse_head(q, k, v, g: Geometry, idx, cnt, scale: float):
+    """Forward over given selections, also returning each query's softmax
+    log-normaliser lse = log(sum_j exp(s_j)) (natural log, over its gathered
+    keys; -inf for a query block with no key block). Returns (out [S, d],
+    lse [S]) in latent order, float64."""
+    perm = block_token_order(g)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    out = np.zeros((g.seq_len, v.shape[-1]))
+    lse = np.full(g.seq_len, -np.inf)
+    for i in range(g.num_blocks):
+        blocks = [int(j) for j in idx[i, : cnt[i]]]
+        if not blocks:
+            continue
+        qt, kt = _gathered(q, k, v, g, i, blocks, perm)
+        logits = (q[qt] @ k[kt].T) * scale
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        l = e.sum(axis=1, keepdims=True)
+        out[qt] = (e / l) @ v[kt]
+        lse[qt] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def backward_head(q, k, v, do, g: Geometry, idx, cnt, scale: float):
+    """Gradients of L = sum(dO * O) with respect to q, k and v, where O is the
+    forward over the given selections (held fixed). For query block i with
+    gathered keys K_J, values V_J and probabilities P = softmax(Q_i K_J^T s):
+
+        dV_J += P^T dO_i
+        dP    = dO_i V_J^T
+        dS    = P * (dP - rowsum(dO_i * O_i))     (softmax Jacobian)
+        dQ_i += s * dS K_J
+        dK_J += s * dS^T Q_i
+
+    Returns (dq, dk, dv), each [S, d] in latent order, float64."""
+    perm = block_token_order(g)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for i in range(g.num_blocks):
+        blocks = [int(j) for j in idx[i, : cnt[i]]]
+        if not blocks:
+            continue
+        qt, kt = _gathered(q, k, v, g, i, blocks, perm)
+        logits = (q[qt] @ k[kt].T) * scale
+        logits -= logits.max(axis=1, keepdims=True)
+        p = np.exp(logits)
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ v[kt]
+        delta = (do[qt] * o).sum(axis=1, keepdims=True)
+        dp = do[qt] @ v[kt].T
+        ds = p * (dp - delta)
+        dq[qt] += scale * (ds @ k[kt])
+        np.add.at(dk, kt, scale * (ds.T @ q[qt]))
+        np.add.at(dv, kt, p.T @ do[qt])
+    return dq, dk, dv

@@ -340,6 +340,114 @@ def pin_monotonic():
         prev = sets
 
 
+# ------------------------------------------------------------ backward pins ---
+def _bwd_case(seed=11, d=8):
+    """A 4-block geometry, random float64 tensors and fixed selections that
+    include a one-block row and overlapping key sets."""
+    g = O.Geometry(4, 8, 16)
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((g.seq_len, d)) for _ in range(4))
+    idx = np.array([[0, 2, -1], [1, 3, 0], [3, -1, -1], [0, 1, 2]])
+    cnt = np.array([2, 3, 1, 3])
+    return g, q, k, v, do, idx, cnt
+
+
+def _loss(q, k, v, do, g, idx, cnt, scale):
+    """L = sum(dO * O) with O from the forward definition (attention over the
+    gathered keys of each query block)."""
+    perm = O.block_token_order(g)
+    total = 0.0
+    n = g.n
+    for i in range(g.num_blocks):
+        blocks = [int(j) for j in idx[i, : cnt[i]]]
+        if blocks:
+            o = O.attend_query_block(q, k, v, g, i, blocks, scale, perm)
+            total += float((do[perm[i * n : (i + 1) * n]] * o).sum())
+    return total
+
+
+def pin_backward_finite_differences():
+    """Analytic gradients equal central differences of L = sum(dO * O) taken
+    through the forward definition, on 24 random coordinates of each input."""
+    g, q, k, v, do, idx, cnt = _bwd_case()
+    scale = 0.35
+    dq, dk, dv = O.backward_head(q, k, v, do, g, idx, cnt, scale)
+    rng = np.random.default_rng(5)
+    h = 1e-5
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(24):
+            r = int(rng.integers(x.shape[0]))
+            c = int(rng.integers(x.shape[1]))
+            xp = x.copy()
+            xm = x.copy()
+            xp[r, c] += h
+            xm[r, c] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, g, idx, cnt, scale)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, g, idx, cnt, scale)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[r, c]) <= 1e-6 * max(1.0, abs(fd)), (name, r, c, fd, grad[r, c])
+
+
+def pin_backward_dense_autograd():
+    """With every block selected, the gradients are those of textbook softmax
+    attention over the whole sequence, here from torch autograd in float64."""
+    import torch
+
+    g = O.Geometry(4, 8, 16)
+    rng = np.random.default_rng(8)
+    q, k, v, do = (rng.standard_normal((g.seq_len, 8)) for _ in range(4))
+    nb = g.num_blocks
+    idx = np.tile(np.arange(nb), (nb, 1))
+    cnt = np.full(nb, nb)
+    scale = 0.3
+    dq, dk, dv = O.backward_head(q, k, v, do, g, idx, cnt, scale)
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    out = torch.softmax((tq @ tk.T) * scale, dim=1) @ tv
+    (out * torch.tensor(do)).sum().backward()
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.abs(mine - ref.numpy()).max() < 1e-10
+
+
+def pin_backward_constant_v():
+    """V constant: O does not depend on q or k, so dQ = dK = 0."""
+    g, q, k, _, do, idx, cnt = _bwd_case(seed=12)
+    v = np.full_like(q, -1.25)
+    dq, dk, _ = O.backward_head(q, k, v, do, g, idx, cnt, 0.4)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+
+
+def pin_backward_dv_total():
+    """Rows of P sum to one, so the sum of dV over all keys equals the sum of
+    dO over the queries that attend to anything."""
+    g, q, k, v, do, idx, cnt = _bwd_case(seed=13)
+    _, _, dv = O.backward_head(q, k, v, do, g, idx, cnt, 0.4)
+    perm = O.block_token_order(g)
+    n = g.n
+    rows = np.concatenate([perm[i * n : (i + 1) * n] for i in range(g.num_blocks) if cnt[i] > 0])
+    assert np.abs(dv.sum(axis=0) - do[rows].sum(axis=0)).max() < 1e-10
+
+
+def pin_forward_lse():
+    """forward_lse_head reproduces the pinned forward, and exp(s - lse) over a
+    query's gathered keys sums to one."""
+    g, q, k, v, _, idx, cnt = _bwd_case(seed=14)
+    scale = 0.4
+    out, lse = O.forward_lse_head(q, k, v, g, idx, cnt, scale)
+    perm = O.block_token_order(g)
+    n = g.n
+    for i in range(g.num_blocks):
+        blocks = [int(j) for j in idx[i, : cnt[i]]]
+        qt = perm[i * n : (i + 1) * n]
+        ref = O.attend_query_block(q, k, v, g, i, blocks, scale, perm)
+        assert np.abs(out[qt] - ref).max() < 1e-12
+        kt = np.concatenate([perm[j * n : (j + 1) * n] for j in blocks])
+        s = (q[qt] @ k[kt].T) * scale
+        assert np.abs(np.exp(s - lse[qt][:, None]).sum(axis=1) - 1).max() < 1e-12
+
+
 ALL_PINS = [
     pin_block_order_geometry,
     pin_handworked_golden,
@@ -355,4 +463,9 @@ ALL_PINS = [
     pin_block_causal_independence,
     pin_block_causal_dense_definition,
     pin_monotonic,
+    pin_backward_finite_differences,
+    pin_backward_dense_autograd,
+    pin_backward_constant_v,
+    pin_backward_dv_total,
+    pin_forward_lse,
 ]

@@ -12,6 +12,7 @@ _orig_attend = O.attend_query_block
 _orig_order = O.block_token_order
 _orig_pool = O.pool_blocks
 _orig_cdf = O.select_cdf
+_orig_lse = O.forward_lse_head
 
 
 def _attend_no_scale(q, k, v, g, i, key_blocks, scale, perm=None):
@@ -84,6 +85,53 @@ def _scores_transposed(q_pool, k_pool, scale):
     return (k_pool @ q_pool.T) * scale
 
 
+def _backward_variant(mistake):
+    """backward_head with one planted mistake."""
+
+    def fn(q, k, v, do, g, idx, cnt, scale):
+        perm = O.block_token_order(g)
+        q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        n = g.n
+        for i in range(g.num_blocks):
+            blocks = [int(j) for j in idx[i, : cnt[i]]]
+            if not blocks:
+                continue
+            qt = perm[i * n : (i + 1) * n]
+            kt = np.concatenate([perm[j * n : (j + 1) * n] for j in blocks])
+            logits = (q[qt] @ k[kt].T) * scale
+            logits -= logits.max(axis=1, keepdims=True)
+            p = np.exp(logits)
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ v[kt]
+            delta = (do[qt] * o).sum(axis=1, keepdims=True)
+            dp = do[qt] @ v[kt].T
+            ds = p * dp if mistake == "no delta" else p * (dp - delta)
+            kk = v[kt] if mistake == "dq from v" else k[kt]
+            dq[qt] += scale * (ds @ kk)
+            sk = 1.0 if mistake == "dk unscaled" else scale
+            np.add.at(dk, kt, sk * (ds.T @ q[qt]))
+            pv = p if mistake == "dv from p" else p.T
+            np.add.at(dv, kt, pv @ do[qt])
+        return dq, dk, dv
+
+    return fn
+
+
+def _lse_without_max(q, k, v, g, idx, cnt, scale):
+    out, lse = _orig_lse(q, k, v, g, idx, cnt, scale)
+    perm = O.block_token_order(g)
+    n = g.n
+    for i in range(g.num_blocks):
+        blocks = [int(j) for j in idx[i, : cnt[i]]]
+        if blocks:
+            qt = perm[i * n : (i + 1) * n]
+            kt = np.concatenate([perm[j * n : (j + 1) * n] for j in blocks])
+            s = (np.asarray(q)[qt] @ np.asarray(k)[kt].T) * scale
+            lse[qt] -= s.max(axis=1)
+    return out, lse
+
+
 MUTANTS = {
     "attention scale dropped": ("attend_query_block", _attend_no_scale),
     "keys used as values": ("attend_query_block", _attend_keys_as_values),
@@ -100,6 +148,11 @@ MUTANTS = {
     "block-causal ignored": ("allowed_key_blocks", lambda g, i: g.num_blocks),
     "noisy rows restricted too": ("allowed_key_blocks",
                                   lambda g, i: g.cond_blocks if g.cond_frames else g.num_blocks),
+    "backward drops the softmax Jacobian's row term": ("backward_head", _backward_variant("no delta")),
+    "backward dQ uses V": ("backward_head", _backward_variant("dq from v")),
+    "backward dK unscaled": ("backward_head", _backward_variant("dk unscaled")),
+    "backward dV from P instead of P^T": ("backward_head", _backward_variant("dv from p")),
+    "lse without the max": ("forward_lse_head", _lse_without_max),
 }
 
 
