@@ -104,6 +104,62 @@ def cpu_baseline(w, q, k, v, blocks: int, seconds: float):
     }
 
 
+def backward_bench(w, problem, qd, kd, vd, idx, cnt, stride, ws_att, stream, eff, steps):
+    """Training step of the attention on the same selection: bsa_attention_lse
+    (forward that also writes the log-normaliser) then bsa_attention_bwd with
+    a synthetic dO. Effective FLOP of the backward follow the usual count of
+    five products (dV, dP, dQ, dK and the recomputed S: 2.5x the forward's);
+    the kernels execute seven (S and dP are recomputed for dQ and for dK/dV)."""
+    import numpy as np
+    import torch
+
+    from video_dit_block_bsa_amd import binding as B
+    from video_dit_block_bsa_amd.inputs import make_grad
+
+    dod = torch.from_numpy(make_grad(w.T, w.H, w.W, w.heads, w.head_dim, w.batch,
+                                     seed=w.seed)).view(torch.bfloat16).cuda()
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.batch, w.heads, w.seq_len), dtype=torch.float32, device="cuda")
+    grads = [torch.empty_like(qd) for _ in range(3)]
+    wsb = torch.empty(B.attention_bwd_workspace_bytes(problem), dtype=torch.uint8, device="cuda")
+
+    def one(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.bsa_attention_lse(problem, qd, kd, vd, idx, cnt, stride, o, lse, ws_att, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.bsa_attention_bwd(problem, qd, kd, vd, o, dod, lse, idx, cnt, stride, *grads, wsb,
+                            stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    one()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s in range(steps):
+        one(events[s])
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    bwd_eff = 2.5 * eff
+    log(f"[bench] training pass: forward with lse {fwd_ms:.3f} ms, backward {bwd_ms:.3f} ms "
+        f"({bwd_eff / (bwd_ms * 1e-3) / 1e12:.1f} effective TFLOP/s)")
+    del dod, o, lse, grads, wsb
+    torch.cuda.empty_cache()
+    return {
+        "entry_points": "bsa_attention_lse + bsa_attention_bwd (selection fixed)",
+        "steps": steps,
+        "forward_lse_ms": round(fwd_ms, 4),
+        "backward_ms": round(bwd_ms, 4),
+        "effective_tflop": round(bwd_eff / 1e12, 4),
+        "effective_tflops": round(bwd_eff / (bwd_ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * bwd_eff / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "executed_mfma_tflop": round(3.5 * eff / 1e12, 4),
+        "dtype": "bf16",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +172,8 @@ def main():
                     help="at most this many query blocks in the CPU oracle sample (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="stop the CPU oracle sample after this much attention time")
+    ap.add_argument("--backward-steps", type=int, default=5,
+                    help="timed training forward (with lse) + backward passes (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first, so that "
                          "hardware byte counters can be calibrated against a known size")
@@ -209,6 +267,11 @@ def main():
         log(f"[bench] dense_attention: {dense_ms:.2f} ms")
         del od
 
+    bwd = None
+    if args.backward_steps > 0:
+        bwd = backward_bench(w, problem, qd, kd, vd, idx, cnt, stride, ws_att, stream, eff,
+                             args.backward_steps)
+
     att_tflops = eff / (att_avg * 1e-3) / 1e12
     traffic = traffic_for(w.name)
     roofline = {
@@ -264,6 +327,7 @@ def main():
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_per_step, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "backward": bwd,
     }
     print(json.dumps(result), flush=True)
 

@@ -139,6 +139,56 @@ bsa_status dense_attention(const bsa_problem* problem, const void* q, const void
                            const void* v, void* o, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Training forward: bsa_attention that also writes each query's softmax
+ * log-normaliser, which bsa_attention_bwd needs to recompute probabilities
+ * (the operator has a forward and a backward pass: deep dive, section "Block
+ * Sparse Attention", "Implementation details and design trade-offs").
+ *   lse   float32 [batch, heads, S] out, latent order, 4-byte aligned:
+ *         natural log of sum_j exp(scale q.k_j) over the query's kept keys,
+ *         with the sum taken over the same bf16-rounded probabilities the
+ *         forward multiplies V with; -inf for a query block with no key block.
+ * Everything else (arguments, checks, o) as for bsa_attention; o is
+ * bit-identical to bsa_attention's. */
+bsa_status bsa_attention_lse(const bsa_problem* problem, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const int32_t* cnt,
+                             int32_t idx_stride, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace bsa_attention_bwd needs: 1 KB of per-query
+ * statistics per block and a bit mask of Nb x Nb bits per (batch, head),
+ * each part rounded up to 256 bytes. Returns 0 on invalid arguments. */
+size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
+
+/* Backward of bsa_attention with the key-block selection held fixed (the
+ * selection is discrete and carries no gradient; the training use of the
+ * selection is in the deep dive's "Block selection via pooled attention
+ * scores", the backward pass in "Implementation details and design
+ * trade-offs"). Computes the gradients of L = sum(dout * o) with respect to
+ * q, k and v, where for query block i with kept keys K_J, values V_J:
+ *   P = softmax(scale Q_i K_J^T),  D = rowsum(dout_i * o_i),
+ *   dS = P * (dout_i V_J^T - D),
+ *   dq_i = scale dS K_J,  dk_J += scale dS^T Q_i,  dv_J += P^T dout_i.
+ *   q, k, v       the forward's inputs.
+ *   o, lse        as written by bsa_attention_lse for the same q, k, v, idx, cnt.
+ *   dout          bf16 [batch, heads, S, 128]: dL/do.
+ *   idx, cnt      the forward's key-block lists. The valid ids of a row must
+ *                 be distinct (bsa_select's are); ids outside [0, Nb) are
+ *                 skipped and cnt is clamped to [0, idx_stride], as in the
+ *                 forward.
+ *   dq, dk, dv    bf16 [batch, heads, S, 128] out, every element written
+ *                 (zero for query blocks with no key block and for keys no
+ *                 query block kept). They must not overlap the inputs or
+ *                 each other.
+ * P is recomputed in fp32 from lse; the products run in bf16 with fp32
+ * accumulation (P and dS are rounded to bf16 as MFMA operands). No
+ * floating-point atomics: results are bit-identical from run to run.
+ * Limits: Nb <= 4096 key blocks per (batch, head) (BSA_ERR_UNSUPPORTED). */
+bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const void* k,
+                             const void* v, const void* o, const void* dout, const float* lse,
+                             const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* dq,
+                             void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Static description of a status code. */
 const char* bsa_status_string(int32_t status);
 

@@ -368,18 +368,19 @@ def _gathered(q, k, v, g, i, key_blocks, perm):
     return qt, kt
 
 
-def forward_lse_head(q, k, v, g: Geometry, idx, cnt, scale: float):
+def forward_lse_head(q, k, v, g: Geometry, idx, cnt, scale: float, query_blocks=None):
     """Forward over given selections, also returning each query's softmax
     log-normaliser lse = log(sum_j exp(s_j)) (natural log, over its gathered
     keys; -inf for a query block with no key block). Returns (out [S, d],
-    lse [S]) in latent order, float64."""
+    lse [S]) in latent order, float64. With `query_blocks` given, only those
+    query blocks are computed (the others stay 0 / -inf)."""
     perm = block_token_order(g)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     out = np.zeros((g.seq_len, v.shape[-1]))
     lse = np.full(g.seq_len, -np.inf)
-    for i in range(g.num_blocks):
+    for i in range(g.num_blocks) if query_blocks is None else sorted(set(query_blocks)):
         blocks = [int(j) for j in idx[i, : cnt[i]]]
         if not blocks:
             continue
@@ -393,7 +394,7 @@ def forward_lse_head(q, k, v, g: Geometry, idx, cnt, scale: float):
     return out, lse
 
 
-def backward_head(q, k, v, do, g: Geometry, idx, cnt, scale: float):
+def backward_head(q, k, v, do, g: Geometry, idx, cnt, scale: float, query_blocks=None):
     """Gradients of L = sum(dO * O) with respect to q, k and v, where O is the
     forward over the given selections (held fixed). For query block i with
     gathered keys K_J, values V_J and probabilities P = softmax(Q_i K_J^T s):
@@ -404,7 +405,12 @@ def backward_head(q, k, v, do, g: Geometry, idx, cnt, scale: float):
         dQ_i += s * dS K_J
         dK_J += s * dS^T Q_i
 
-    Returns (dq, dk, dv), each [S, d] in latent order, float64."""
+    Returns (dq, dk, dv), each [S, d] in latent order, float64.
+
+    With `query_blocks` given, only those query blocks are visited: dq is
+    then exact on their tokens, and dk, dv are exact on the tokens of any key
+    block that only those query blocks keep (the sums above run over the
+    query blocks that kept each key block)."""
     perm = block_token_order(g)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -413,7 +419,7 @@ def backward_head(q, k, v, do, g: Geometry, idx, cnt, scale: float):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for i in range(g.num_blocks):
+    for i in range(g.num_blocks) if query_blocks is None else sorted(set(query_blocks)):
         blocks = [int(j) for j in idx[i, : cnt[i]]]
         if not blocks:
             continue

@@ -448,6 +448,30 @@ def pin_forward_lse():
         assert np.abs(np.exp(s - lse[qt][:, None]).sum(axis=1) - 1).max() < 1e-12
 
 
+def pin_backward_query_block_subset():
+    """Visiting a subset of query blocks: dq exact on those blocks, dk and dv
+    exact on a key block kept only by the subset (key block 3 is kept by rows
+    1 and 2 only), and the forward's lse exact on the visited blocks."""
+    g, q, k, v, do, idx, cnt = _bwd_case(seed=5)
+    s = 0.37
+    full = O.backward_head(q, k, v, do, g, idx, cnt, s)
+    sub = O.backward_head(q, k, v, do, g, idx, cnt, s, query_blocks=[2, 1, 1])
+    perm = O.block_token_order(g)
+    blk = lambda b: perm[b * g.n:(b + 1) * g.n]
+    for b in (1, 2):
+        assert np.allclose(sub[0][blk(b)], full[0][blk(b)], rtol=0, atol=1e-12)
+    for b in (0, 3):
+        assert np.all(sub[0][blk(b)] == 0)
+    for t in (1, 2):
+        assert np.allclose(sub[t][blk(3)], full[t][blk(3)], rtol=0, atol=1e-12)
+    o_full, l_full = O.forward_lse_head(q, k, v, g, idx, cnt, s)
+    o_sub, l_sub = O.forward_lse_head(q, k, v, g, idx, cnt, s, query_blocks=[3, 0])
+    for b in (0, 3):
+        assert np.allclose(l_sub[blk(b)], l_full[blk(b)], rtol=0, atol=1e-12)
+        assert np.allclose(o_sub[blk(b)], o_full[blk(b)], rtol=0, atol=1e-12)
+    assert np.all(l_sub[blk(1)] == -np.inf) and np.all(o_sub[blk(2)] == 0)
+
+
 ALL_PINS = [
     pin_block_order_geometry,
     pin_handworked_golden,
@@ -468,4 +492,5 @@ ALL_PINS = [
     pin_backward_constant_v,
     pin_backward_dv_total,
     pin_forward_lse,
+    pin_backward_query_block_subset,
 ]

@@ -164,3 +164,69 @@ def test_sequence_limit():
     assert lib.bsa_attention_workspace_bytes(ctypes.byref(ok)) == 0
     r = lib.bsa_attention(ctypes.byref(bad), None, None, None, None, None, 1, None, None, 0, None)
     assert r == -2 and b"too long" in lib.bsa_last_error()
+
+
+GiB4 = 1 << 32  # spacing of the fake tensors below: the 215K x 32-head tensors are 1.76 GB
+
+
+def _bwd(p, **kw):
+    """bsa_attention_bwd with fake, well-separated pointers; every call in
+    the tests below is rejected by the host checks before any launch."""
+    lib = B.lib()
+    names = ["q", "k", "v", "o", "dout", "lse", "idx", "cnt", "dq", "dk", "dv", "ws"]
+    a = {n: GiB4 * (i + 1) for i, n in enumerate(names)}
+    a.update(stride=4, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.bsa_attention_bwd(ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["dout"],
+                                 a["lse"], a["idx"], a["cnt"], a["stride"], a["dq"], a["dk"],
+                                 a["dv"], a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_workspace_size():
+    p = _problem()
+    nb, nbw = 1680, 53
+    stats = 32 * nb * 256 * 4
+    mask = 32 * nb * nbw * 4
+    got = B.attention_bwd_workspace_bytes(p)
+    assert stats + mask <= got < stats + mask + 2 * 256
+    assert B.attention_bwd_workspace_bytes(_problem(head_dim=64)) == 0
+
+
+def test_backward_rejects_bad_arguments():
+    p = _problem()
+    for name in ("q", "o", "dout", "lse", "idx", "cnt", "dq", "dk", "dv"):
+        assert _bwd(p, **{name: None}) == INVALID, name
+    assert _bwd(p, stride=0) == INVALID
+    assert _bwd(p, dq=GiB4 * 9 + 8) == INVALID        # misaligned
+    assert _bwd(p, dout=GiB4 * 5 + 4) == INVALID
+    assert _bwd(p, lse=GiB4 * 6 + 2) == INVALID
+    assert _bwd(p, dk=GiB4 * 9 + 4096) == INVALID     # overlaps dq
+    assert _bwd(p, dv=GiB4 * 1) == INVALID            # is q
+    assert _bwd(p, dq=GiB4 * 6 + 256) == INVALID      # overlaps lse
+    assert _bwd(p, ws_bytes=1024) == WORKSPACE
+    assert _bwd(p, ws=None) == WORKSPACE
+    assert _bwd(p, ws=GiB4 * 12 + 8) == INVALID
+    assert _bwd(_problem(T=4 * 100)) == UNSUPPORTED   # 12,000 blocks
+    assert _bwd(_problem(head_dim=64)) == UNSUPPORTED
+
+
+def test_backward_and_lse_forward_empty_problem():
+    lib = B.lib()
+    p = _problem(heads=0)
+    assert lib.bsa_attention_bwd(ctypes.byref(p), *([None] * 8), 4, None, None, None, None, 0,
+                                 None) == OK
+    assert lib.bsa_attention_lse(ctypes.byref(p), None, None, None, None, None, 4, None, None,
+                                 None, 0, None) == OK
+
+
+def test_lse_forward_rejects_bad_lse():
+    lib = B.lib()
+    p = _problem()
+
+    def call(lse, o=GiB4 * 4):
+        return lib.bsa_attention_lse(ctypes.byref(p), GiB4, GiB4 * 2, GiB4 * 3, GiB4 * 5,
+                                     GiB4 * 6, 4, o, lse, None, 0, None)
+
+    assert call(None) == INVALID
+    assert call(GiB4 * 7 + 2) == INVALID
+    assert call(GiB4 * 4) == INVALID  # is o

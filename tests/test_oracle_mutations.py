@@ -88,12 +88,12 @@ def _scores_transposed(q_pool, k_pool, scale):
 def _backward_variant(mistake):
     """backward_head with one planted mistake."""
 
-    def fn(q, k, v, do, g, idx, cnt, scale):
+    def fn(q, k, v, do, g, idx, cnt, scale, query_blocks=None):
         perm = O.block_token_order(g)
         q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
         dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
         n = g.n
-        for i in range(g.num_blocks):
+        for i in range(g.num_blocks) if query_blocks is None else sorted(set(query_blocks)):
             blocks = [int(j) for j in idx[i, : cnt[i]]]
             if not blocks:
                 continue
@@ -118,11 +118,11 @@ def _backward_variant(mistake):
     return fn
 
 
-def _lse_without_max(q, k, v, g, idx, cnt, scale):
-    out, lse = _orig_lse(q, k, v, g, idx, cnt, scale)
+def _lse_without_max(q, k, v, g, idx, cnt, scale, query_blocks=None):
+    out, lse = _orig_lse(q, k, v, g, idx, cnt, scale, query_blocks=query_blocks)
     perm = O.block_token_order(g)
     n = g.n
-    for i in range(g.num_blocks):
+    for i in range(g.num_blocks) if query_blocks is None else sorted(set(query_blocks)):
         blocks = [int(j) for j in idx[i, : cnt[i]]]
         if blocks:
             qt = perm[i * n : (i + 1) * n]

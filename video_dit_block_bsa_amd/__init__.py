@@ -24,6 +24,9 @@ def __getattr__(name):
         "select_workspace_bytes",
         "attention_workspace_bytes",
         "index_stride",
+        "bsa_attention_lse",
+        "bsa_attention_bwd",
+        "attention_bwd_workspace_bytes",
     }:
         from . import binding
 

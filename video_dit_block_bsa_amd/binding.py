@@ -113,6 +113,14 @@ def lib():
         L.bsa_attention.restype = ctypes.c_int32
         L.dense_attention.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.dense_attention.restype = ctypes.c_int32
+        L.bsa_attention_lse.argtypes = [P, vp, vp, vp, i32p, i32p, ctypes.c_int32, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
+        L.bsa_attention_lse.restype = ctypes.c_int32
+        L.bsa_attention_bwd_workspace_bytes.argtypes = [P]
+        L.bsa_attention_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.bsa_attention_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, i32p, ctypes.c_int32,
+                                        vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.bsa_attention_bwd.restype = ctypes.c_int32
         L.bsa_status_string.argtypes = [ctypes.c_int32]
         L.bsa_status_string.restype = ctypes.c_char_p
         L.bsa_last_error.argtypes = []
@@ -187,3 +195,27 @@ def dense_attention(problem, q, k, v, o, workspace, stream=None):
     ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
     _check(lib().dense_attention(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                  ws_ptr, _nbytes(workspace), _stream(stream)))
+
+
+def attention_bwd_workspace_bytes(problem: Problem) -> int:
+    return lib().bsa_attention_bwd_workspace_bytes(ctypes.byref(problem))
+
+
+def bsa_attention_lse(problem, q, k, v, idx, cnt, idx_stride, o, lse, workspace, stream=None):
+    """bsa_attention_lse: bsa_attention that also writes the per-query
+    log-normaliser -> o, lse."""
+    ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
+    _check(lib().bsa_attention_lse(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                   _ptr(cnt), int(idx_stride), _ptr(o), _ptr(lse), ws_ptr,
+                                   _nbytes(workspace), _stream(stream)))
+
+
+def bsa_attention_bwd(problem, q, k, v, o, dout, lse, idx, cnt, idx_stride, dq, dk, dv,
+                      workspace, stream=None):
+    """bsa_attention_bwd: gradients of sum(dout * o) for fixed selections
+    -> dq, dk, dv."""
+    ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
+    _check(lib().bsa_attention_bwd(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(dout), _ptr(lse), _ptr(idx), _ptr(cnt), int(idx_stride),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), ws_ptr, _nbytes(workspace),
+                                   _stream(stream)))

@@ -125,7 +125,7 @@ bsa_status launched(hipError_t e, const char* what) {
 
 bsa_status attention_common(const bsa_problem* problem, const void* q, const void* k,
                             const void* v, const int32_t* idx, const int32_t* cnt,
-                            int32_t idx_stride, void* o, void* workspace,
+                            int32_t idx_stride, void* o, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream, bool dense) {
   Checked c;
   bsa_status st = check_problem(problem, &c);
@@ -139,6 +139,10 @@ bsa_status attention_common(const bsa_problem* problem, const void* q, const voi
     if (idx_stride < 1) return fail(BSA_ERR_INVALID_ARG, "idx_stride must be >= 1");
   }
   if (o == q || o == k || o == v) return fail(BSA_ERR_INVALID_ARG, "o must not alias q, k or v");
+  if (lse && ((uintptr_t)lse & 3u)) return fail(BSA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (lse && ((const void*)lse == q || (const void*)lse == k || (const void*)lse == v ||
+              (const void*)lse == o))
+    return fail(BSA_ERR_INVALID_ARG, "lse must not alias q, k, v or o");
   const size_t need = attention_ws(c.g);
   if (workspace_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "attention needs %zu workspace bytes (got %zu)", need,
@@ -149,8 +153,30 @@ bsa_status attention_common(const bsa_problem* problem, const void* q, const voi
                                         static_cast<const bsa::bf16_bits*>(k),
                                         static_cast<const bsa::bf16_bits*>(v), idx, cnt,
                                         dense ? 1 : idx_stride, dense,
-                                        static_cast<bsa::bf16_bits*>(o), s),
+                                        static_cast<bsa::bf16_bits*>(o), lse, s),
                   "attention");
+}
+
+struct BwdLayout {
+  size_t stats, mask, total;
+  int nbw;
+};
+
+// Backward workspace: per (batch*head, block) 128 values lse*log2(e) and 128
+// values D (fp32), then the key-block x query-block bit mask (nb rows of
+// ceil(nb/32) words per batch*head).
+BwdLayout bwd_layout(const bsa::Geom& g) {
+  BwdLayout L;
+  L.nbw = (g.nb + 31) / 32;
+  L.stats = 0;
+  L.mask = align_up((size_t)g.bh * g.nb * 2 * bsa::kBlockTokens * sizeof(float));
+  L.total = L.mask + align_up((size_t)g.bh * g.nb * L.nbw * sizeof(uint32_t));
+  return L;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
 }
 
 }  // namespace
@@ -214,15 +240,85 @@ bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* param
 bsa_status bsa_attention(const bsa_problem* problem, const void* q, const void* k, const void* v,
                          const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* o,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  return attention_common(problem, q, k, v, idx, cnt, idx_stride, o, workspace, workspace_bytes,
-                          stream, false);
+  return attention_common(problem, q, k, v, idx, cnt, idx_stride, o, nullptr, workspace,
+                          workspace_bytes, stream, false);
+}
+
+bsa_status bsa_attention_lse(const bsa_problem* problem, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const int32_t* cnt,
+                             int32_t idx_stride, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (problem && problem->batch > 0 && problem->heads > 0 && !lse)
+    return fail(BSA_ERR_INVALID_ARG, "lse must be non-NULL");
+  return attention_common(problem, q, k, v, idx, cnt, idx_stride, o, lse, workspace,
+                          workspace_bytes, stream, false);
+}
+
+size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem) {
+  Checked c;
+  if (check_problem(problem, &c) != BSA_OK) return 0;
+  return bwd_layout(c.g).total;
+}
+
+bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const void* k,
+                             const void* v, const void* o, const void* dout, const float* lse,
+                             const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* dq,
+                             void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Checked c;
+  bsa_status st = check_problem(problem, &c);
+  if (st != BSA_OK) return st;
+  if (c.empty) return BSA_OK;
+  if (c.g.nb > kMaxBlocks)
+    return fail(BSA_ERR_UNSUPPORTED, "%d blocks per head: the backward supports at most %d",
+                c.g.nb, kMaxBlocks);
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  void* outs[3] = {dq, dk, dv};
+  for (const void* p : ins)
+    if (!p) return fail(BSA_ERR_INVALID_ARG, "q, k, v, o, dout and lse must be non-NULL");
+  for (void* p : outs)
+    if (!p) return fail(BSA_ERR_INVALID_ARG, "dq, dk and dv must be non-NULL");
+  if (!idx || !cnt) return fail(BSA_ERR_INVALID_ARG, "idx and cnt must be non-NULL");
+  if (idx_stride < 1) return fail(BSA_ERR_INVALID_ARG, "idx_stride must be >= 1");
+  for (int i = 0; i < 5; ++i)
+    if (!aligned16(ins[i]))
+      return fail(BSA_ERR_INVALID_ARG, "q, k, v, o and dout must be 16-byte aligned");
+  for (void* p : outs)
+    if (!aligned16(p)) return fail(BSA_ERR_INVALID_ARG, "dq, dk and dv must be 16-byte aligned");
+  if ((uintptr_t)lse & 3u) return fail(BSA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t tensor = (size_t)c.g.bh * c.g.S * bsa::kHeadDim * 2;
+  const size_t sizes[6] = {tensor, tensor, tensor, tensor, tensor, (size_t)c.g.bh * c.g.S * 4};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], tensor, ins[b], sizes[b]))
+        return fail(BSA_ERR_INVALID_ARG, "dq, dk and dv must not overlap the inputs");
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], tensor, outs[b], tensor))
+        return fail(BSA_ERR_INVALID_ARG, "dq, dk and dv must not overlap each other");
+  }
+  const BwdLayout L = bwd_layout(c.g);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(BSA_ERR_WORKSPACE, "backward needs %zu workspace bytes (got %zu)", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  using bsa::bf16_bits;
+  return launched(
+      bsa::launch_attention_bwd(
+          c.g, static_cast<const bf16_bits*>(q), static_cast<const bf16_bits*>(k),
+          static_cast<const bf16_bits*>(v), static_cast<const bf16_bits*>(o),
+          static_cast<const bf16_bits*>(dout), lse, idx, cnt, idx_stride,
+          reinterpret_cast<float*>(ws + L.stats), reinterpret_cast<uint32_t*>(ws + L.mask),
+          static_cast<bf16_bits*>(dq), static_cast<bf16_bits*>(dk), static_cast<bf16_bits*>(dv),
+          reinterpret_cast<hipStream_t>(stream)),
+      "attention backward");
 }
 
 bsa_status dense_attention(const bsa_problem* problem, const void* q, const void* k,
                            const void* v, void* o, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  return attention_common(problem, q, k, v, nullptr, nullptr, 1, o, workspace, workspace_bytes,
-                          stream, true);
+  return attention_common(problem, q, k, v, nullptr, nullptr, 1, o, nullptr, workspace,
+                          workspace_bytes, stream, true);
 }
 
 const char* bsa_status_string(int32_t status) {

@@ -38,49 +38,14 @@
 // 256 MB Infinity Cache).
 #include <type_traits>
 
-#include "common.h"
+#include "tile.h"
 
 namespace bsa {
-
-__device__ __forceinline__ int swap23(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-// Kernel arguments. Block ids are split into (bt, bh, bw) with multiply-high
-// division by magic numbers (exact for the ranges the host checks), so the
-// per-key-block address math stays on the scalar unit.
-struct AttnArgs {
-  Geom g;
-  int stride;
-  int nq8;           // query blocks per head rounded up to a multiple of 8
-  uint32_t mag_nw;   // floor(2^32 / nW) + 1
-  uint32_t mag_nhw;  // floor(2^32 / (nH*nW)) + 1
-  float c_log2;      // scale * log2(e)
-};
-
-// Latent-order token of the first slot of block i.
-__device__ __forceinline__ int block_origin(const AttnArgs& a, int i) {
-  const Geom& g = a.g;
-  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhw);
-  const int rem = i - bt * g.nH * g.nW;
-  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nw);
-  const int bw = rem - bh * g.nW;
-  return ((bt * g.ct) * g.H + bh * g.ch) * g.W + bw * g.cw;
-}
-
-// Offset (in tokens) of slot j inside its block.
-__device__ __forceinline__ int slot_offset(const Geom& g, int j) {
-  const int iw = j % g.cw;
-  const int r2 = j / g.cw;
-  return ((r2 / g.ch) * g.H + r2 % g.ch) * g.W + iw;
-}
 
 // Softmax rescaling is lazy: the running max m (log2 units) is only moved
 // when a tile's max exceeds it by more than this, so most tiles skip the
 // O *= alpha pass. Probabilities stay <= 2^8, well inside fp32 and bf16.
 constexpr float kRescaleSlack = 8.0f;
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Half tiles live in LDS as 64 rows of 256 bytes (16 chunks of 16 bytes)
 // with no padding. Chunk c of row r is stored at chunk c ^ swz(r), where
@@ -95,23 +60,9 @@ __device__ __forceinline__ int swz(int row) { return swap23(row & 15); }
 // V tiles are read four rows at a time (transposing reads); spreading rows
 // r..r+3 over the four 64-byte slots of a 256-byte row keeps them apart.
 __device__ __forceinline__ int swzv(int row) { return 4 * (row & 3); }
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 constexpr int kHalfRows = kBlockTokens / 2;            // key rows per half tile
 constexpr int kSlots = 5;                               // half-tile ring per workgroup
-// Word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format.
-constexpr int kBufferWord3 = 0x00020000;
-
-// Joins the workgroup without a memory fence: a fence would also wait for
-// the tile loads still in flight into other slots. Callers wait for their
-// own loads with s_waitcnt first; the empty asm statements keep the compiler
-// from moving LDS accesses across the barrier.
-__device__ __forceinline__ void workgroup_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Tiles stream through a ring of five 16 KB half-tile slots in the order
 // K_0 lo, K_0 hi, V_0 lo, V_0 hi, K_1 lo, ... (lo = key rows 0..63). Phase p
@@ -123,11 +74,15 @@ __device__ __forceinline__ void workgroup_barrier() {
 // slot is its own LDS object, and the phase loop is unrolled over the ten
 // phases after which the assignment repeats, so that each read names its
 // slot at compile time and never waits on loads into the other slots.
-template <bool kDense>
+//
+// With kLse the kernel also writes each query's softmax log-normaliser
+// (natural log, -inf for a query block with no key blocks), which the
+// backward pass uses to recompute the probabilities.
+template <bool kDense, bool kLse>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ cntp, bf16_bits* __restrict__ op) {
+    const int32_t* __restrict__ cntp, bf16_bits* __restrict__ op, float* __restrict__ lsep) {
   __shared__ __attribute__((aligned(1024))) bf16_bits slot0[kHalfRows * kHeadDim];
   __shared__ __attribute__((aligned(1024))) bf16_bits slot1[kHalfRows * kHeadDim];
   __shared__ __attribute__((aligned(1024))) bf16_bits slot2[kHalfRows * kHeadDim];
@@ -378,6 +333,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
 
   const float l = l_part + __shfl_xor(l_part, 32);
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
+  if constexpr (kLse) {
+    // sum_j exp(scale * q.k_j) = 2^m2 * l, so lse = (m2 + log2 l) * ln 2.
+    if (gs == 0)
+      lsep[(size_t)pair * g.S + qtok] = (l > 0.f) ? (m2 + log2f(l)) * 0.6931471805599453f : -INFINITY;
+  }
   bf16_bits* orow = op + hoff + (size_t)qtok * kHeadDim;
   // Accumulator value i of sub-tile u is channel 32u + 8(i/4) + 4gs + i%4.
 #pragma unroll
@@ -395,19 +355,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
 
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                             const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
-                            int stride, bool dense, bf16_bits* o, hipStream_t stream) {
-  AttnArgs a;
-  a.g = g;
-  a.stride = stride;
-  a.nq8 = (g.nb + 7) / 8 * 8;
-  a.mag_nw = (uint32_t)(0x100000000ull / (uint64_t)g.nW + 1);
-  a.mag_nhw = (uint32_t)(0x100000000ull / (uint64_t)(g.nH * g.nW) + 1);
-  a.c_log2 = g.scale * 1.4426950408889634f;
+                            int stride, bool dense, bf16_bits* o, float* lse,
+                            hipStream_t stream) {
+  const AttnArgs a = make_attn_args(g, stride);
   dim3 grid((unsigned)((size_t)g.bh * a.nq8));
   if (dense)
-    hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kThreads), 0, stream, a, q, k, v, idx, cnt, o);
+    hipLaunchKernelGGL((attn_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, q, k, v, idx,
+                       cnt, o, nullptr);
+  else if (lse)
+    hipLaunchKernelGGL((attn_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, q, k, v, idx,
+                       cnt, o, lse);
   else
-    hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kThreads), 0, stream, a, q, k, v, idx, cnt, o);
+    hipLaunchKernelGGL((attn_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, q, k, v,
+                       idx, cnt, o, nullptr);
   return hipGetLastError();
 }
 

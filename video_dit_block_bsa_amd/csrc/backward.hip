@@ -1,0 +1,528 @@
+// Backward pass of the block-restricted attention for gfx950: gradients of
+// L = sum(dO * O) with respect to Q, K and V, with the key-block selection of
+// the forward held fixed (a discrete choice, which carries no gradient). The
+// LongCat-Video deep dive, section "Block Sparse Attention", gives the
+// operator a backward pass ("Implementation details and design trade-offs")
+// and uses the selection while training ("Block selection via pooled
+// attention scores": r = N_k/8 in distillation, N_k/16 for the refinement
+// expert).
+//
+// For query block i with gathered keys K_J, values V_J, scale s and the
+// log-normaliser lse the forward wrote:
+//   P   = exp(s Q_i K_J^T - lse)            recomputed, never stored
+//   D   = rowsum(dO_i * O_i)                 one float per query
+//   dP  = dO_i V_J^T,  dS = P * (dP - D)     softmax Jacobian
+//   dQ_i += s dS K_J,  dK_J += s dS^T Q_i,  dV_J += P^T dO_i
+//
+// Four launches, all stream-ordered:
+//   bwd_prep_kernel   D and lse*log2(e) per query, stored per block in slot
+//                     order; clears the key-block -> query-block bit mask.
+//   bwd_mask_kernel   sets bit (kb, qb) of the mask for every kept pair: the
+//                     transposed selection, in a form whose bits come out in
+//                     ascending query-block order whatever order the atomics
+//                     land in, so dK and dV are deterministic.
+//   bwd_dq_kernel     one workgroup per (batch*head, query block), walking the
+//                     query block's key-block list: dQ = s sum dS K.
+//   bwd_dkdv_kernel   one workgroup per (batch*head, key block), walking the
+//                     set bits of its mask row: dK = s sum dS^T Q, dV = sum P^T dO.
+// dQ and dK/dV each recompute S and dP, so no partial sums are exchanged
+// between workgroups (no floating-point atomics) and every output is written
+// once, by one workgroup.
+//
+// MFMA layout (bf16 32x32x16, fp32 accumulate). A 128-row tile lives in LDS
+// as 128 rows of 256 bytes; chunk c (16 bytes) of row r is stored at chunk
+// c ^ f(r) with f(r) = 4 (r mod 4) + (r / 4 mod 4). The tiles of this pass
+// are read two ways: as row operands (lane n reads row swap23(n) at one
+// chunk; 16 lanes meet 16 distinct rows of a 16-row group, which f sends to
+// 16 distinct chunks) and through the transposing read ds_read_b64_tr_b16
+// (32 lanes read four consecutive rows at one 64-byte column group; f puts
+// the four rows in four different 64-byte groups). Both are free of bank
+// conflicts with this one swizzle.
+#include <type_traits>
+
+#include "tile.h"
+
+namespace bsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- prep ---
+// One workgroup per (block, batch*head). Thread t handles half (t % 2) of the
+// channels of slot t / 2; the two halves meet with one lane exchange. stats
+// holds, per (batch*head, block), 128 values lse*log2(e) followed by 128
+// values D, in slot order. A query with lse = -inf (no key block) gets +inf,
+// so that its recomputed probabilities are exp2(x - inf) = 0.
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Geom g, int nbw,
+                                                            const bf16_bits* __restrict__ o,
+                                                            const bf16_bits* __restrict__ dout,
+                                                            const float* __restrict__ lse,
+                                                            float* __restrict__ stats,
+                                                            uint32_t* __restrict__ mask) {
+  const int blk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int j = t >> 1;
+  const int half = t & 1;
+  const int tok = block_token(g, blk, j);
+  const size_t off = ((size_t)bh * g.S + tok) * kHeadDim + 64 * half;
+  u32x4 ov[8], dv[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    ov[c] = *reinterpret_cast<const u32x4*>(o + off + 8 * c);
+    dv[c] = *reinterpret_cast<const u32x4*>(dout + off + 8 * c);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = __builtin_fmaf(bf16_to_f32(ov[c][e] & 0xffffu), bf16_to_f32(dv[c][e] & 0xffffu), acc);
+      acc = __builtin_fmaf(bf16_to_f32(ov[c][e] >> 16), bf16_to_f32(dv[c][e] >> 16), acc);
+    }
+  acc += __shfl_xor(acc, 1);
+  float* st = stats + ((size_t)bh * g.nb + blk) * (2 * kBlockTokens);
+  if (half == 1) {
+    st[kBlockTokens + j] = acc;
+  } else {
+    const float l = lse[(size_t)bh * g.S + tok];
+    st[j] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
+  if (t < nbw) mask[((size_t)bh * g.nb + blk) * nbw + t] = 0u;
+}
+
+// ---------------------------------------------------------------- mask ---
+// Wave w of workgroup x handles query block 4x + w: every valid id kb of its
+// list sets bit qb of mask row kb. Ids outside [0, nb) are skipped and the
+// count is clamped to [0, stride], as in the forward.
+__global__ __launch_bounds__(kThreads) void bwd_mask_kernel(Geom g, int nbw, int stride,
+                                                            const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ cnt,
+                                                            uint32_t* __restrict__ mask) {
+  const int qb = 4 * blockIdx.x + (threadIdx.x >> 6);
+  const int bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (qb >= g.nb) return;
+  const size_t row = (size_t)bh * g.nb + qb;
+  const int count = min(max(cnt[row], 0), stride);
+  const uint32_t bit = 1u << (qb & 31);
+  for (int p = lane; p < count; p += 64) {
+    const int kb = idx[row * stride + p];
+    if (kb >= 0 && kb < g.nb)
+      atomicOr(&mask[((size_t)bh * g.nb + kb) * nbw + (qb >> 5)], bit);
+  }
+}
+
+// ------------------------------------------------------- tile addressing ---
+// Per-lane byte offsets into a swizzled 128-row tile.
+struct TileLanes {
+  // Row operand: lane (n, gs) reads row 32t + swap23(n), logical chunk
+  // 2s + gs (channels 16s + 8gs .. +7) at  t * 8192 + (ra ^ 32s).
+  int ra;
+  // Transposing read for channel group u and 16-row step k: the lane's two
+  // reads (rows +0..3 and +4..7 of its 8-row half) are at
+  //   (16k)*256 + (ta ^ 64u)  and  (16k + 4)*256 + (ta ^ 64u ^ 16).
+  int ta;
+  // Direct-to-LDS tile load i (i = 0..7) of wave w covers rows 32w + 4i .. +3;
+  // lane L writes physical chunk L % 16 of row 32w + 4i + L / 16 and fetches
+  // global byte (row token)*256 + (ld ^ 16 (i % 4)), see load_tile.
+  uint32_t ld;
+};
+
+__device__ __forceinline__ TileLanes tile_lanes(const Geom& g, int w, int lane) {
+  TileLanes t;
+  const int n = lane & 31;
+  const int gs = lane >> 5;
+  // f(swap23(n)) for the row-operand lanes: bits 0-1 of the row are n's,
+  // bits 2-3 are n's bits 3 and 2.
+  const int f_row = ((n & 3) << 2) | ((n >> 3) & 1) | (((n >> 2) & 1) << 1);
+  t.ra = swap23(n) * 256 + 16 * (gs ^ f_row);
+  // Transposing read: in each 16-lane group, lane j reads row 8gs + j/4 (+4)
+  // at channels 16*((lane/16)%2) + 4*(j%4) .. +3 of the channel group.
+  const int jj = lane & 15;
+  const int q4 = jj >> 2;
+  const int hb = (lane >> 4) & 1;
+  const int c1 = (jj & 3) >> 1;
+  t.ta = (8 * gs + q4) * 256 + 64 * q4 + 16 * ((2 * hb + c1) ^ (2 * gs)) + 8 * (jj & 1);
+  // Tile loads: row 32w + 4i + r (r = L/16) has f = 4r + i%4, so the lane
+  // fetches logical chunk (L%16) ^ 4r ^ (i%4). The slot offset is linear in
+  // the bits of the slot index (power-of-two chunk sides), so the row's token
+  // is that of slot 32w + r plus that of slot 4i.
+  const int r = lane >> 4;
+  t.ld = (uint32_t)slot_offset(g, 32 * w + r) * (kHeadDim * 2) + (uint32_t)(((lane & 15) ^ (r << 2)) << 4);
+  return t;
+}
+
+// Issues the eight direct-to-LDS loads of this wave's 32 rows of the tile of
+// block `blk` (one of Q, K, V, dO through `rs`) into `tile`.
+__device__ __forceinline__ void load_tile(const AttnArgs& a, __amdgpu_buffer_rsrc_t rs,
+                                          const TileLanes& tl, int w, int blk, bf16_bits* tile) {
+  const uint32_t base = (uint32_t)block_origin(a, blk) * (kHeadDim * 2);
+  char* dst = reinterpret_cast<char*>(tile) + 32 * w * 256;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t row_s = (uint32_t)slot_offset(a.g, 4 * i) * (kHeadDim * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 1024), 16,
+                                             tl.ld ^ (uint32_t)(16 * (i & 3)), base + row_s, 0, 0);
+  }
+}
+
+__device__ __forceinline__ bf16x8 row_operand(const char* tile, int sub, int s, const TileLanes& tl) {
+  return *reinterpret_cast<const bf16x8*>(tile + sub * 8192 + (tl.ra ^ (32 * s)));
+}
+
+// A operand X^T (channel group u, rows 16k .. 16k+15 of the tile) through two
+// transposing reads: lane l gets channel 32u + l%32 of rows 16k + 8gs + 0..7.
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, int k, int u, const TileLanes& tl) {
+  const char* p0 = tile + 16 * k * 256 + (tl.ta ^ (64 * u));
+  const char* p1 = tile + (16 * k + 4) * 256 + (tl.ta ^ (64 * u) ^ 16);
+  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0));
+  const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1));
+  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  const f32x2 v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Writes a 128-channel accumulator set (4 groups of 32 channels x 32 tokens,
+// lane column = token) times `mul` as bf16 to row `row` (lane's token).
+__device__ __forceinline__ void store_rows(bf16_bits* row, const f32x16 (&acc)[4], float mul, int gs) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const u32x2 packed = {pack_bf16(acc[u][4 * a4 + 0] * mul, acc[u][4 * a4 + 1] * mul),
+                            pack_bf16(acc[u][4 * a4 + 2] * mul, acc[u][4 * a4 + 3] * mul)};
+      *reinterpret_cast<u32x2*>(row + 32 * u + 8 * a4 + 4 * gs) = packed;
+    }
+}
+
+// XCD-aware workgroup order, as in the forward: hardware id x runs on XCD
+// x % 8; XCD c gets the blocks [c*chunk, (c+1)*chunk) of the current head.
+__device__ __forceinline__ void xcd_block(const AttnArgs& a, int& pair, int& blk) {
+  const int x = blockIdx.x;
+  pair = x / a.nq8;
+  const int r = x - pair * a.nq8;
+  const int chunk = a.nq8 >> 3;
+  blk = (r & 7) * chunk + (r >> 3);
+}
+
+// ------------------------------------------------------------------ dQ ---
+// Wave w owns queries 32w .. 32w+31 of the query block; Q^T and dO^T of its
+// queries stay in registers as B operands. Per key block and 64-key half:
+//   S^T = K Q^T, dP^T = V dO^T    (2 key sub-tiles x 8 channel steps, each)
+//   dS^T = P^T * (dP^T - D)       lane's query: one lse and one D per lane
+//   dQ^T += K^T dS^T              (4 channel groups x 4 key steps; K^T by
+//                                  transposing reads of the same K tile)
+// K and V tiles are double-buffered in LDS (two separate objects each, the
+// loop unrolled by two so every read names its buffer at compile time and
+// never waits for the loads into the other one).
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+    AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
+    const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
+    const float* __restrict__ stats, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ cntp, bf16_bits* __restrict__ dqp) {
+  __shared__ __attribute__((aligned(1024))) bf16_bits k0s[kBlockTokens * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits v0s[kBlockTokens * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits k1s[kBlockTokens * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits v1s[kBlockTokens * kHeadDim];
+  const Geom& g = a.g;
+  int pair, qb;
+  xcd_block(a, pair, qb);
+  if (qb >= g.nb) return;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n = lane & 31;
+  const int gs = lane >> 5;
+  const size_t hoff = (size_t)pair * g.S * kHeadDim;
+  const uint32_t head_bytes = (uint32_t)g.S * (kHeadDim * 2);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kp + hoff), (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(vp + hoff), (short)0, head_bytes, kBufferWord3);
+  const TileLanes tl = tile_lanes(g, w, lane);
+
+  const int qtok = block_origin(a, qb) + slot_offset(g, 32 * w + n);
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const size_t off = hoff + (size_t)qtok * kHeadDim + 16 * s + 8 * gs;
+    qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + off));
+    df[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dop + off));
+  }
+  const float* st = stats + ((size_t)pair * g.nb + qb) * (2 * kBlockTokens);
+  const float lse2 = st[32 * w + n];
+  const float dd = st[kBlockTokens + 32 * w + n];
+
+  const int32_t* list = idx + ((size_t)pair * g.nb + qb) * a.stride;
+  const int count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
+  auto next_valid = [&](int from) __attribute__((always_inline)) {
+    while (from < count) {
+      const int kb = list[from];
+      if (kb >= 0 && kb < g.nb) break;
+      ++from;
+    }
+    return from;
+  };
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) dq[u] = f32x16{};
+
+  auto compute = [&](const char* kt, const char* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) sacc[t2] = pacc[t2] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(kt, 2 * h + t2, s, tl), qf[s],
+                                                             sacc[t2], 0, 0, 0);
+          pacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, 2 * h + t2, s, tl), df[s],
+                                                             pacc[t2], 0, 0, 0);
+        }
+      // Accumulator value i of sub-tile t2 is key 64h + 32t2 + swap23(row):
+      // values 0..7 are keys +8gs .. +8gs+7, values 8..15 keys +16+8gs ..; as
+      // a B operand they are key steps 2t2 and 2t2+1 of this half.
+      bf16x8 dsf[4];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 packed;
+#pragma unroll
+          for (int j2 = 0; j2 < 4; ++j2) {
+            const int i0 = 8 * hh + 2 * j2;
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0], a.c_log2, -lse2));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0 + 1], a.c_log2, -lse2));
+            packed[j2] = pack_bf16(p0 * (pacc[t2][i0] - dd), p1 * (pacc[t2][i0 + 1] - dd));
+          }
+          dsf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, packed);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          dq[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt + h * 64 * 256, ks, u, tl),
+                                                          dsf[ks], dq[u], 0, 0, 0);
+    }
+  };
+
+  int cur = next_valid(0);
+  if (cur < count) {
+    load_tile(a, krs, tl, w, list[cur], k0s);
+    load_tile(a, vrs, tl, w, list[cur], v0s);
+    int nxt = next_valid(cur + 1);
+    auto step = [&](auto bc) __attribute__((always_inline)) -> bool {
+      constexpr int b = decltype(bc)::value;
+      bf16_bits* kt = b == 0 ? k0s : k1s;
+      bf16_bits* vt = b == 0 ? v0s : v1s;
+      bf16_bits* kn = b == 0 ? k1s : k0s;
+      bf16_bits* vn = b == 0 ? v1s : v0s;
+      // This wave's loads of the current tiles are done; after the barrier
+      // everyone's are, and everyone has finished reading the other buffer.
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      workgroup_barrier();
+      if (nxt < count) {
+        load_tile(a, krs, tl, w, list[nxt], kn);
+        load_tile(a, vrs, tl, w, list[nxt], vn);
+      }
+      compute(reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt));
+      if (nxt >= count) return false;
+      cur = nxt;
+      nxt = next_valid(cur + 1);
+      return true;
+    };
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+    }
+  }
+  store_rows(dqp + hoff + (size_t)qtok * kHeadDim, dq, g.scale, gs);
+}
+
+// ---------------------------------------------------------------- dK dV ---
+// Wave w owns keys 32w .. 32w+31 of the key block; K and V of its keys stay
+// in registers (as the B operands of S = Q K^T and dP = dO V^T). Per query
+// block in the mask row (ascending) and 64-query half:
+//   S = Q K^T, dP = dO V^T      (2 query sub-tiles x 8 channel steps, each)
+//   P, dS                       lse and D of the accumulator rows from LDS
+//   dV^T += dO^T P, dK^T += Q^T dS   (4 channel groups x 4 query steps, the
+//                               transposed tiles by transposing reads)
+// Q, dO and the stats of a query block are double-buffered in LDS.
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+    AttnArgs a, int nbw, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
+    const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
+    const float* __restrict__ stats, const uint32_t* __restrict__ mask,
+    bf16_bits* __restrict__ dkp, bf16_bits* __restrict__ dvp) {
+  __shared__ __attribute__((aligned(1024))) bf16_bits q0s[kBlockTokens * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits d0s[kBlockTokens * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits q1s[kBlockTokens * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) bf16_bits d1s[kBlockTokens * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) float st0s[2 * kBlockTokens];
+  __shared__ __attribute__((aligned(1024))) float st1s[2 * kBlockTokens];
+  __shared__ uint32_t mrow[kBlockTokens];  // nbw <= 128 words (nb <= 4096)
+  const Geom& g = a.g;
+  int pair, kb;
+  xcd_block(a, pair, kb);
+  if (kb >= g.nb) return;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n = lane & 31;
+  const int gs = lane >> 5;
+  const size_t hoff = (size_t)pair * g.S * kHeadDim;
+  const uint32_t head_bytes = (uint32_t)g.S * (kHeadDim * 2);
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(qp + hoff), (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t drs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(dop + hoff), (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(stats + (size_t)pair * g.nb * (2 * kBlockTokens)), (short)0,
+      (uint32_t)g.nb * (2 * kBlockTokens * 4), kBufferWord3);
+  const TileLanes tl = tile_lanes(g, w, lane);
+
+  const int ktok = block_origin(a, kb) + slot_offset(g, 32 * w + n);
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const size_t off = hoff + (size_t)ktok * kHeadDim + 16 * s + 8 * gs;
+    kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + off));
+    vf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + off));
+  }
+  if (t < nbw) mrow[t] = mask[((size_t)pair * g.nb + kb) * nbw + t];
+  __syncthreads();
+  // First set bit at or after position `from` (nb if none). Every lane reads
+  // the same words, so the search runs on uniform values.
+  auto next_set = [&](int from) __attribute__((always_inline)) -> int {
+    int wd = from >> 5;
+    if (wd >= nbw) return g.nb;
+    uint32_t bits = __builtin_amdgcn_readfirstlane(mrow[wd]) & (0xffffffffu << (from & 31));
+    while (bits == 0u) {
+      if (++wd >= nbw) return g.nb;
+      bits = __builtin_amdgcn_readfirstlane(mrow[wd]);
+    }
+    return wd * 32 + __builtin_ctz(bits);
+  };
+  // Stats of a query block: 1 KB, one 16-byte load per lane of wave 0.
+  auto load_stats = [&](int qb, float* dst) __attribute__((always_inline)) {
+    if (w == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)dst, 16, (uint32_t)lane * 16,
+                                               (uint32_t)qb * (2 * kBlockTokens * 4), 0, 0);
+  };
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) dk[u] = dv[u] = f32x16{};
+
+  auto compute = [&](const char* qt, const char* dt, const float* sts) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x16 sacc[2], pacc[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) sacc[t2] = pacc[t2] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, 2 * h + t2, s, tl), kf[s],
+                                                             sacc[t2], 0, 0, 0);
+          pacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(dt, 2 * h + t2, s, tl), vf[s],
+                                                             pacc[t2], 0, 0, 0);
+        }
+      // Value i of sub-tile t2 is query 64h + 32t2 + 8gs + (i % 8) + 16 (i / 8).
+      bf16x8 pf[4], dsf[4];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int q0 = 64 * h + 32 * t2 + 16 * hh + 8 * gs;
+          u32x4 pp, dp;
+#pragma unroll
+          for (int j2 = 0; j2 < 4; ++j2) {
+            const int i0 = 8 * hh + 2 * j2;
+            const f32x2 l2 = *reinterpret_cast<const f32x2*>(sts + q0 + 2 * j2);
+            const f32x2 d2 = *reinterpret_cast<const f32x2*>(sts + kBlockTokens + q0 + 2 * j2);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0], a.c_log2, -l2[0]));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0 + 1], a.c_log2, -l2[1]));
+            pp[j2] = pack_bf16(p0, p1);
+            dp[j2] = pack_bf16(p0 * (pacc[t2][i0] - d2[0]), p1 * (pacc[t2][i0 + 1] - d2[1]));
+          }
+          pf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, pp);
+          dsf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, dp);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(dt + h * 64 * 256, ks, u, tl),
+                                                          pf[ks], dv[u], 0, 0, 0);
+          dk[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt + h * 64 * 256, ks, u, tl),
+                                                          dsf[ks], dk[u], 0, 0, 0);
+        }
+    }
+  };
+
+  int cur = next_set(0);
+  if (cur < g.nb) {
+    load_tile(a, qrs, tl, w, cur, q0s);
+    load_tile(a, drs, tl, w, cur, d0s);
+    load_stats(cur, st0s);
+    int nxt = next_set(cur + 1);
+    auto step = [&](auto bc) __attribute__((always_inline)) -> bool {
+      constexpr int b = decltype(bc)::value;
+      bf16_bits* qt = b == 0 ? q0s : q1s;
+      bf16_bits* dt = b == 0 ? d0s : d1s;
+      float* sts = b == 0 ? st0s : st1s;
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      workgroup_barrier();
+      if (nxt < g.nb) {
+        load_tile(a, qrs, tl, w, nxt, b == 0 ? q1s : q0s);
+        load_tile(a, drs, tl, w, nxt, b == 0 ? d1s : d0s);
+        load_stats(nxt, b == 0 ? st1s : st0s);
+      }
+      compute(reinterpret_cast<const char*>(qt), reinterpret_cast<const char*>(dt), sts);
+      if (nxt >= g.nb) return false;
+      cur = nxt;
+      nxt = next_set(cur + 1);
+      return true;
+    };
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+    }
+  }
+  store_rows(dkp + hoff + (size_t)ktok * kHeadDim, dk, g.scale, gs);
+  store_rows(dvp + hoff + (size_t)ktok * kHeadDim, dv, 1.0f, gs);
+}
+
+hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bits* k,
+                                const bf16_bits* v, const bf16_bits* o, const bf16_bits* dout,
+                                const float* lse, const int32_t* idx, const int32_t* cnt,
+                                int stride, float* stats, uint32_t* mask, bf16_bits* dq,
+                                bf16_bits* dk, bf16_bits* dv, hipStream_t stream) {
+  const AttnArgs a = make_attn_args(g, stride);
+  const int nbw = (g.nb + 31) / 32;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(g.nb, g.bh), dim3(kThreads), 0, stream, g, nbw, o, dout,
+                     lse, stats, mask);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_mask_kernel, dim3((g.nb + 3) / 4, g.bh), dim3(kThreads), 0, stream, g, nbw,
+                     stride, idx, cnt, mask);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((size_t)g.bh * a.nq8));
+  hipLaunchKernelGGL(bwd_dq_kernel, grid, dim3(kThreads), 0, stream, a, q, k, v, dout, stats, idx,
+                     cnt, dq);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, grid, dim3(kThreads), 0, stream, a, nbw, q, k, v, dout, stats,
+                     mask, dk, dv);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -63,6 +63,12 @@ hipError_t launch_select(const Geom& g, const float* s, int mode, int k, float p
                          hipStream_t stream);
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                             const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
-                            int stride, bool dense, bf16_bits* o, hipStream_t stream);
+                            int stride, bool dense, bf16_bits* o, float* lse,
+                            hipStream_t stream);
+hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bits* k,
+                                const bf16_bits* v, const bf16_bits* o, const bf16_bits* dout,
+                                const float* lse, const int32_t* idx, const int32_t* cnt,
+                                int stride, float* stats, uint32_t* mask, bf16_bits* dq,
+                                bf16_bits* dk, bf16_bits* dv, hipStream_t stream);
 
 }  // namespace bsa

@@ -1,0 +1,73 @@
+// Tile helpers shared by the forward and backward attention kernels of
+// libbsa.so: block and slot addressing in latent order, kernel arguments with
+// the magic numbers for dividing block ids, buffer resources and a fence-free
+// workgroup barrier.
+#pragma once
+
+#include "common.h"
+
+namespace bsa {
+
+__device__ __forceinline__ int swap23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Kernel arguments. Block ids are split into (bt, bh, bw) with multiply-high
+// division by magic numbers (exact for the ranges the host checks), so the
+// per-key-block address math stays on the scalar unit.
+struct AttnArgs {
+  Geom g;
+  int stride;
+  int nq8;           // query blocks per head rounded up to a multiple of 8
+  uint32_t mag_nw;   // floor(2^32 / nW) + 1
+  uint32_t mag_nhw;  // floor(2^32 / (nH*nW)) + 1
+  float c_log2;      // scale * log2(e)
+};
+
+// Latent-order token of the first slot of block i.
+__device__ __forceinline__ int block_origin(const AttnArgs& a, int i) {
+  const Geom& g = a.g;
+  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhw);
+  const int rem = i - bt * g.nH * g.nW;
+  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nw);
+  const int bw = rem - bh * g.nW;
+  return ((bt * g.ct) * g.H + bh * g.ch) * g.W + bw * g.cw;
+}
+
+// Offset (in tokens) of slot j inside its block.
+__device__ __forceinline__ int slot_offset(const Geom& g, int j) {
+  const int iw = j % g.cw;
+  const int r2 = j / g.cw;
+  return ((r2 / g.ch) * g.H + r2 % g.ch) * g.W + iw;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
+// Word 3 of a raw buffer resource on gfx9-class GPUs: 32-bit data format.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Joins the workgroup without a memory fence: a fence would also wait for
+// the tile loads still in flight into other slots. Callers wait for their
+// own loads with s_waitcnt first; the empty asm statements keep the compiler
+// from moving LDS accesses across the barrier.
+__device__ __forceinline__ void workgroup_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Kernel arguments for a problem with index rows of `stride` entries.
+inline AttnArgs make_attn_args(const Geom& g, int stride) {
+  AttnArgs a;
+  a.g = g;
+  a.stride = stride;
+  a.nq8 = (g.nb + 7) / 8 * 8;
+  a.mag_nw = (uint32_t)(0x100000000ull / (uint64_t)g.nW + 1);
+  a.mag_nhw = (uint32_t)(0x100000000ull / (uint64_t)(g.nH * g.nW) + 1);
+  a.c_log2 = g.scale * 1.4426950408889634f;
+  return a;
+}
+
+}  // namespace bsa

@@ -15,6 +15,12 @@ Recipes
   truncated at 4 sigma, periodic boundary), then scaled to unit standard
   deviation per channel. Q = F + 0.3 N(0,1), K = F + 0.3 N(0,1), V = N(0,1).
 
+* ``make_grad``: the output gradient dL/dO of the backward workloads, i.i.d.
+  N(0, 1) per element, from its own seed sequence.
+* ``random_block_lists``: key-block lists drawn uniformly without
+  replacement (for backward tests that fix the selection instead of
+  deriving it from Q and K).
+
 All values are rounded from float32 to bfloat16 with round-to-nearest-even.
 Each (batch, head) draws from its own child of ``SeedSequence(seed)``, so any
 subset of heads can be regenerated alone and heads can be produced in
@@ -126,3 +132,40 @@ def make_qkv(
     with ThreadPoolExecutor(max_workers=max(1, n_threads)) as ex:
         list(ex.map(work, range(len(pairs))))
     return out[0], out[1], out[2]
+
+
+def make_grad(T: int, H: int, W: int, heads: int, head_dim: int = 128, batch: int = 1,
+              seed: int = 0, threads: int | None = None):
+    """Output gradient dO, uint16 bfloat16 bits [batch, heads, S, head_dim],
+    i.i.d. N(0, 1); head (b, h) draws from child b*heads + h of
+    SeedSequence([seed, 0x644F])."""
+    children = np.random.SeedSequence([seed, 0x644F]).spawn(batch * heads)
+    S = T * H * W
+    out = np.empty((batch, heads, S, head_dim), dtype=np.uint16)
+
+    def work(i):
+        b, h = divmod(i, heads)
+        x = np.random.default_rng(children[i]).standard_normal((S, head_dim), dtype=np.float32)
+        out[b, h] = f32_to_bf16_bits(x)
+
+    n_threads = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=max(1, n_threads)) as ex:
+        list(ex.map(work, range(batch * heads)))
+    return out
+
+
+def random_block_lists(allowed, stride: int, counts, seed: int = 0):
+    """Key-block lists for len(allowed) rows: row i holds counts[i] distinct
+    ids drawn uniformly from range(allowed[i]) (at most allowed[i] and
+    stride of them), in ascending order, padded with -1 to `stride`.
+    Returns (idx int32 [rows, stride], cnt int32 [rows])."""
+    rng = np.random.default_rng(seed)
+    rows = len(allowed)
+    idx = np.full((rows, stride), -1, dtype=np.int32)
+    cnt = np.zeros(rows, dtype=np.int32)
+    for i in range(rows):
+        c = int(min(counts[i], allowed[i], stride))
+        if c > 0:
+            idx[i, :c] = np.sort(rng.choice(int(allowed[i]), size=c, replace=False))
+        cnt[i] = c
+    return idx, cnt
