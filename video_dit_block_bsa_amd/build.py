@@ -28,21 +28,13 @@ HIPCC_FLAGS = [
     "-Wall",
     # Packed fp32 VALU forms are kept out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results go to arch VGPRs: every kernel feeds its accumulators to
+    # VALU code (softmax, probabilities, epilogues) and fits in 256 VGPRs per
+    # wave, so AGPR results would only add a copy per value.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE,
     "-I", CSRC,
 ]
-
-# Per-source additions. The forward attention and the pooled-score kernel
-# take MFMA results in arch VGPRs: their accumulators feed VALU code (the
-# softmax) directly, and AGPR results would cost a copy per value. The
-# backward kernels run one wave per SIMD and keep more accumulators live than
-# 256 arch VGPRs hold, so the compiler may place them in AGPRs.
-FILE_FLAGS = {
-    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "select.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "pool.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "api.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-}
 
 
 def hipcc() -> str:
@@ -57,8 +49,7 @@ def build(verbose: bool = False, save_asm: str | None = None) -> str:
     with tempfile.TemporaryDirectory(prefix="bsa_build_") as tmp:
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
-                   "-o", obj]
+            cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
             if save_asm:
                 os.makedirs(save_asm, exist_ok=True)
                 cmd += ["-save-temps"]

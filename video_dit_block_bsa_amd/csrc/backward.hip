@@ -46,6 +46,7 @@ namespace bsa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+
 // ---------------------------------------------------------------- prep ---
 // One workgroup per (block, batch*head). Thread t handles half (t % 2) of the
 // channels of slot t / 2; the two halves meet with one lane exchange. stats
@@ -113,6 +114,34 @@ __global__ __launch_bounds__(kThreads) void bwd_mask_kernel(Geom g, int nbw, int
 }
 
 // ------------------------------------------------------- tile addressing ---
+// The dQ and dK/dV kernels run 8 waves (two per SIMD) per workgroup; each
+// wave stages 16 rows of every 128-row tile.
+constexpr int kBwdWaves = 8;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kRowsPerWave = kBlockTokens / kBwdWaves;
+
+// 32-row sub-tiles whose S (and dP) are computed together before their
+// probabilities feed the next products: 2 keeps more MFMAs in flight per
+// wave, 1 keeps fewer accumulators live.
+#ifndef BSA_BWD_DQ_GROUP
+#define BSA_BWD_DQ_GROUP 2
+#endif
+#ifndef BSA_BWD_DKDV_GROUP
+#define BSA_BWD_DKDV_GROUP 1
+#endif
+#ifndef BSA_BWD_FENCES
+#define BSA_BWD_FENCES 1
+#endif
+#if BSA_BWD_FENCES
+#define BSA_BWD_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define BSA_BWD_FENCE() ((void)0)
+#endif
+constexpr int kDqGroup = BSA_BWD_DQ_GROUP;
+constexpr int kDkdvGroup = BSA_BWD_DKDV_GROUP;
+static_assert(kDqGroup == 1 || kDqGroup == 2, "dQ: groups of 1 or 2 sub-tiles");
+static_assert(kDkdvGroup == 1 || kDkdvGroup == 2 || kDkdvGroup == 4, "dK/dV: 1, 2 or 4 sub-tiles");
+
 // Per-lane byte offsets into a swizzled 128-row tile.
 struct TileLanes {
   // Row operand: lane (n, gs) reads row 32t + swap23(n), logical chunk
@@ -122,9 +151,9 @@ struct TileLanes {
   // reads (rows +0..3 and +4..7 of its 8-row half) are at
   //   (16k)*256 + (ta ^ 64u)  and  (16k + 4)*256 + (ta ^ 64u ^ 16).
   int ta;
-  // Direct-to-LDS tile load i (i = 0..7) of wave w covers rows 32w + 4i .. +3;
-  // lane L writes physical chunk L % 16 of row 32w + 4i + L / 16 and fetches
-  // global byte (row token)*256 + (ld ^ 16 (i % 4)), see load_tile.
+  // Direct-to-LDS tile load i (i = 0..3) of wave w covers rows 16w + 4i .. +3;
+  // lane L writes physical chunk L % 16 of row 16w + 4i + L / 16 and fetches
+  // global byte (row token)*256 + (ld ^ 16i), see load_tile.
   uint32_t ld;
 };
 
@@ -143,26 +172,27 @@ __device__ __forceinline__ TileLanes tile_lanes(const Geom& g, int w, int lane) 
   const int hb = (lane >> 4) & 1;
   const int c1 = (jj & 3) >> 1;
   t.ta = (8 * gs + q4) * 256 + 64 * q4 + 16 * ((2 * hb + c1) ^ (2 * gs)) + 8 * (jj & 1);
-  // Tile loads: row 32w + 4i + r (r = L/16) has f = 4r + i%4, so the lane
-  // fetches logical chunk (L%16) ^ 4r ^ (i%4). The slot offset is linear in
-  // the bits of the slot index (power-of-two chunk sides), so the row's token
-  // is that of slot 32w + r plus that of slot 4i.
+  // Tile loads: row 16w + 4i + r (r = L/16) has f = 4r + i, so the lane
+  // fetches logical chunk (L%16) ^ 4r ^ i. The slot offset is linear in the
+  // bits of the slot index (power-of-two chunk sides), so the row's token is
+  // that of slot 16w + r plus that of slot 4i.
   const int r = lane >> 4;
-  t.ld = (uint32_t)slot_offset(g, 32 * w + r) * (kHeadDim * 2) + (uint32_t)(((lane & 15) ^ (r << 2)) << 4);
+  t.ld = (uint32_t)slot_offset(g, kRowsPerWave * w + r) * (kHeadDim * 2) +
+         (uint32_t)(((lane & 15) ^ (r << 2)) << 4);
   return t;
 }
 
-// Issues the eight direct-to-LDS loads of this wave's 32 rows of the tile of
+// Issues the four direct-to-LDS loads of this wave's 16 rows of the tile of
 // block `blk` (one of Q, K, V, dO through `rs`) into `tile`.
 __device__ __forceinline__ void load_tile(const AttnArgs& a, __amdgpu_buffer_rsrc_t rs,
                                           const TileLanes& tl, int w, int blk, bf16_bits* tile) {
   const uint32_t base = (uint32_t)block_origin(a, blk) * (kHeadDim * 2);
-  char* dst = reinterpret_cast<char*>(tile) + 32 * w * 256;
+  char* dst = reinterpret_cast<char*>(tile) + kRowsPerWave * w * 256;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kRowsPerWave / 4; ++i) {
     const uint32_t row_s = (uint32_t)slot_offset(a.g, 4 * i) * (kHeadDim * 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 1024), 16,
-                                             tl.ld ^ (uint32_t)(16 * (i & 3)), base + row_s, 0, 0);
+                                             tl.ld ^ (uint32_t)(16 * i), base + row_s, 0, 0);
   }
 }
 
@@ -179,6 +209,10 @@ __device__ __forceinline__ bf16x8 tr_operand(const char* tile, int k, int u, con
   const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1));
   return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
@@ -210,16 +244,19 @@ __device__ __forceinline__ void xcd_block(const AttnArgs& a, int& pair, int& blk
 }
 
 // ------------------------------------------------------------------ dQ ---
-// Wave w owns queries 32w .. 32w+31 of the query block; Q^T and dO^T of its
-// queries stay in registers as B operands. Per key block and 64-key half:
-//   S^T = K Q^T, dP^T = V dO^T    (2 key sub-tiles x 8 channel steps, each)
+// Wave w owns queries 32(w%4) .. +31 of the query block and keys
+// 64(w/4) .. +63 of every key block: the two waves of a query slice split
+// each key block, so no product is computed twice, and their partial dQ are
+// added once at the end. Q^T and dO^T of the wave's queries stay in registers
+// as B operands. Per 32-key sub-tile:
+//   S^T = K Q^T, dP^T = V dO^T    (8 channel steps each)
 //   dS^T = P^T * (dP^T - D)       lane's query: one lse and one D per lane
-//   dQ^T += K^T dS^T              (4 channel groups x 4 key steps; K^T by
+//   dQ^T += K^T dS^T              (4 channel groups x 2 key steps; K^T by
 //                                  transposing reads of the same K tile)
 // K and V tiles are double-buffered in LDS (two separate objects each, the
 // loop unrolled by two so every read names its buffer at compile time and
 // never waits for the loads into the other one).
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
     const float* __restrict__ stats, const int32_t* __restrict__ idx,
@@ -236,6 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int qs = w & 3;   // query slice
+  const int kh = w >> 2;  // key half
   const int n = lane & 31;
   const int gs = lane >> 5;
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
@@ -246,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
       __builtin_amdgcn_make_buffer_rsrc((void*)(vp + hoff), (short)0, head_bytes, kBufferWord3);
   const TileLanes tl = tile_lanes(g, w, lane);
 
-  const int qtok = block_origin(a, qb) + slot_offset(g, 32 * w + n);
+  const int qtok = block_origin(a, qb) + slot_offset(g, 32 * qs + n);
   bf16x8 qf[8], df[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -255,8 +294,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     df[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dop + off));
   }
   const float* st = stats + ((size_t)pair * g.nb + qb) * (2 * kBlockTokens);
-  const float lse2 = st[32 * w + n];
-  const float dd = st[kBlockTokens + 32 * w + n];
+  const float lse2 = st[32 * qs + n];
+  const float dd = st[kBlockTokens + 32 * qs + n];
 
   const int32_t* list = idx + ((size_t)pair * g.nb + qb) * a.stride;
   const int count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
@@ -273,27 +312,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
 #pragma unroll
   for (int u = 0; u < 4; ++u) dq[u] = f32x16{};
 
-  auto compute = [&](const char* kt, const char* vt) __attribute__((always_inline)) {
+  // kh is a template constant inside the loop, so every LDS address is one of
+  // a few per-lane offsets plus an immediate.
+  auto compute = [&](auto khc, const char* kt, const char* vt) __attribute__((always_inline)) {
+    constexpr int kh = decltype(khc)::value;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x16 sacc[2], pacc[2];
+    for (int h = 0; h < 2 / kDqGroup; ++h) {
+      f32x16 sacc[kDqGroup], pacc[kDqGroup];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) sacc[t2] = pacc[t2] = f32x16{};
+      for (int t2 = 0; t2 < kDqGroup; ++t2) sacc[t2] = pacc[t2] = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(kt, 2 * h + t2, s, tl), qf[s],
-                                                             sacc[t2], 0, 0, 0);
-          pacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, 2 * h + t2, s, tl), df[s],
-                                                             pacc[t2], 0, 0, 0);
+        for (int t2 = 0; t2 < kDqGroup; ++t2) {
+          const int tt = 2 * kh + kDqGroup * h + t2;
+          sacc[t2] = mfma(row_operand(kt, tt, s, tl), qf[s], sacc[t2]);
+          pacc[t2] = mfma(row_operand(vt, tt, s, tl), df[s], pacc[t2]);
         }
-      // Accumulator value i of sub-tile t2 is key 64h + 32t2 + swap23(row):
-      // values 0..7 are keys +8gs .. +8gs+7, values 8..15 keys +16+8gs ..; as
-      // a B operand they are key steps 2t2 and 2t2+1 of this half.
-      bf16x8 dsf[4];
+      BSA_BWD_FENCE();
+      // Accumulator value i of sub-tile tt is key 32tt + swap23(row): values
+      // 0..7 are keys +8gs .. +8gs+7, values 8..15 keys +16+8gs ..; as a B
+      // operand they are key steps 2tt and 2tt+1.
+      bf16x8 dsf[2 * kDqGroup];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < kDqGroup; ++t2)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           u32x4 packed;
@@ -306,17 +348,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
           }
           dsf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, packed);
         }
+      BSA_BWD_FENCE();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 2 * kDqGroup; ++ks)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          dq[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt + h * 64 * 256, ks, u, tl),
-                                                          dsf[ks], dq[u], 0, 0, 0);
+          dq[u] = mfma(tr_operand(kt, 2 * (2 * kh + kDqGroup * h) + ks, u, tl), dsf[ks], dq[u]);
+      BSA_BWD_FENCE();
     }
   };
 
-  int cur = next_valid(0);
-  if (cur < count) {
+  auto run = [&](auto khc) __attribute__((always_inline)) {
+    int cur = next_valid(0);
+    if (cur >= count) return;
     load_tile(a, krs, tl, w, list[cur], k0s);
     load_tile(a, vrs, tl, w, list[cur], v0s);
     int nxt = next_valid(cur + 1);
@@ -334,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
         load_tile(a, krs, tl, w, list[nxt], kn);
         load_tile(a, vrs, tl, w, list[nxt], vn);
       }
-      compute(reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt));
+      compute(khc, reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt));
       if (nxt >= count) return false;
       cur = nxt;
       nxt = next_valid(cur + 1);
@@ -342,20 +386,43 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     };
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
+  };
+  // Both copies of the loop run the same barriers, so the halves stay in step.
+  if (kh == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+  // The key halves meet: waves 4..7 leave their partial dQ in LDS (16 KB per
+  // wave, lane-contiguous words), waves 0..3 add them in and store.
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(qs < 2 ? k0s : v0s) + (qs & 1) * (64 * 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part[(u * 16 + i) * 64 + lane] = dq[u][i];
   }
-  store_rows(dqp + hoff + (size_t)qtok * kHeadDim, dq, g.scale, gs);
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dq[u][i] += part[(u * 16 + i) * 64 + lane];
+    store_rows(dqp + hoff + (size_t)qtok * kHeadDim, dq, g.scale, gs);
+  }
 }
 
 // ---------------------------------------------------------------- dK dV ---
-// Wave w owns keys 32w .. 32w+31 of the key block; K and V of its keys stay
-// in registers (as the B operands of S = Q K^T and dP = dO V^T). Per query
-// block in the mask row (ascending) and 64-query half:
-//   S = Q K^T, dP = dO V^T      (2 query sub-tiles x 8 channel steps, each)
-//   P, dS                       lse and D of the accumulator rows from LDS
-//   dV^T += dO^T P, dK^T += Q^T dS   (4 channel groups x 4 query steps, the
-//                               transposed tiles by transposing reads)
-// Q, dO and the stats of a query block are double-buffered in LDS.
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+// Wave w owns keys 32(w%4) .. +31 of the key block, in one of two roles:
+//   w < 4  (dV):  S = Q K^T, P, dV^T += dO^T P
+//   w >= 4 (dK):  S = Q K^T, dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS
+// Splitting the roles keeps each wave within 256 registers (two waves per
+// SIMD, so one wave's exps and conversions overlap the other's MFMAs) at the
+// price of computing S twice. K (and V) of the wave's keys stay in registers
+// as B operands; Q, dO and the stats of a query block are double-buffered in
+// LDS. Query blocks come from the set bits of the key block's mask row, in
+// ascending order.
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     AttnArgs a, int nbw, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
     const float* __restrict__ stats, const uint32_t* __restrict__ mask,
@@ -375,6 +442,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int ks = w & 3;            // key slice
+  const bool dk_role = (w >> 2) != 0;
   const int n = lane & 31;
   const int gs = lane >> 5;
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
@@ -388,13 +457,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       (uint32_t)g.nb * (2 * kBlockTokens * 4), kBufferWord3);
   const TileLanes tl = tile_lanes(g, w, lane);
 
-  const int ktok = block_origin(a, kb) + slot_offset(g, 32 * w + n);
+  const int ktok = block_origin(a, kb) + slot_offset(g, 32 * ks + n);
   bf16x8 kf[8], vf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const size_t off = hoff + (size_t)ktok * kHeadDim + 16 * s + 8 * gs;
     kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + off));
-    vf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + off));
+    vf[s] = dk_role ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + off)) : bf16x8{};
   }
   if (t < nbw) mrow[t] = mask[((size_t)pair * g.nb + kb) * nbw + t];
   __syncthreads();
@@ -417,60 +486,75 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                                                (uint32_t)qb * (2 * kBlockTokens * 4), 0, 0);
   };
 
-  f32x16 dk[4], dv[4];
+  // dV (dV role) or dK (dK role) of the wave's keys.
+  f32x16 acc[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) dk[u] = dv[u] = f32x16{};
+  for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
 
-  auto compute = [&](const char* qt, const char* dt, const float* sts) __attribute__((always_inline)) {
+  // The role is a template constant inside the loop (see dQ).
+  auto compute = [&](auto rolec, const char* qt, const char* dt, const float* sts)
+                     __attribute__((always_inline)) {
+    constexpr bool dk_role = decltype(rolec)::value != 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x16 sacc[2], pacc[2];
+    for (int h = 0; h < 4 / kDkdvGroup; ++h) {
+      f32x16 sacc[kDkdvGroup], pacc[kDkdvGroup];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) sacc[t2] = pacc[t2] = f32x16{};
+      for (int t2 = 0; t2 < kDkdvGroup; ++t2) sacc[t2] = pacc[t2] = f32x16{};
+      if constexpr (dk_role) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+        for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, 2 * h + t2, s, tl), kf[s],
-                                                             sacc[t2], 0, 0, 0);
-          pacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(dt, 2 * h + t2, s, tl), vf[s],
-                                                             pacc[t2], 0, 0, 0);
-        }
-      // Value i of sub-tile t2 is query 64h + 32t2 + 8gs + (i % 8) + 16 (i / 8).
-      bf16x8 pf[4], dsf[4];
+          for (int t2 = 0; t2 < kDkdvGroup; ++t2) {
+            sacc[t2] = mfma(row_operand(qt, kDkdvGroup * h + t2, s, tl), kf[s], sacc[t2]);
+            pacc[t2] = mfma(row_operand(dt, kDkdvGroup * h + t2, s, tl), vf[s], pacc[t2]);
+          }
+      } else {
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+          for (int t2 = 0; t2 < kDkdvGroup; ++t2)
+            sacc[t2] = mfma(row_operand(qt, kDkdvGroup * h + t2, s, tl), kf[s], sacc[t2]);
+      }
+      BSA_BWD_FENCE();
+      // Value i of sub-tile tt is query 32tt + 8gs + (i % 8) + 16 (i / 8); as
+      // a B operand, values 0..7 and 8..15 are query steps 2tt and 2tt+1.
+      bf16x8 bf[2 * kDkdvGroup];
+#pragma unroll
+      for (int t2 = 0; t2 < kDkdvGroup; ++t2)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int q0 = 64 * h + 32 * t2 + 16 * hh + 8 * gs;
-          u32x4 pp, dp;
+          const int q0 = 32 * (kDkdvGroup * h + t2) + 16 * hh + 8 * gs;
+          u32x4 packed;
 #pragma unroll
           for (int j2 = 0; j2 < 4; ++j2) {
             const int i0 = 8 * hh + 2 * j2;
             const f32x2 l2 = *reinterpret_cast<const f32x2*>(sts + q0 + 2 * j2);
-            const f32x2 d2 = *reinterpret_cast<const f32x2*>(sts + kBlockTokens + q0 + 2 * j2);
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0], a.c_log2, -l2[0]));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0 + 1], a.c_log2, -l2[1]));
-            pp[j2] = pack_bf16(p0, p1);
-            dp[j2] = pack_bf16(p0 * (pacc[t2][i0] - d2[0]), p1 * (pacc[t2][i0 + 1] - d2[1]));
+            if constexpr (dk_role) {
+              const f32x2 d2 = *reinterpret_cast<const f32x2*>(sts + kBlockTokens + q0 + 2 * j2);
+              packed[j2] = pack_bf16(p0 * (pacc[t2][i0] - d2[0]), p1 * (pacc[t2][i0 + 1] - d2[1]));
+            } else {
+              packed[j2] = pack_bf16(p0, p1);
+            }
           }
-          pf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, pp);
-          dsf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, dp);
+          bf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, packed);
         }
+      // dV^T += dO^T P (dV role) or dK^T += Q^T dS (dK role).
+      const char* xt = dk_role ? qt : dt;
+      BSA_BWD_FENCE();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int k2 = 0; k2 < 2 * kDkdvGroup; ++k2)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          dv[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(dt + h * 64 * 256, ks, u, tl),
-                                                          pf[ks], dv[u], 0, 0, 0);
-          dk[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt + h * 64 * 256, ks, u, tl),
-                                                          dsf[ks], dk[u], 0, 0, 0);
-        }
+        for (int u = 0; u < 4; ++u)
+          acc[u] = mfma(tr_operand(xt, 2 * kDkdvGroup * h + k2, u, tl), bf[k2], acc[u]);
+      BSA_BWD_FENCE();
     }
   };
 
-  int cur = next_set(0);
-  if (cur < g.nb) {
+  auto run = [&](auto rolec) __attribute__((always_inline)) {
+    int cur = next_set(0);
+    if (cur >= g.nb) return;
     load_tile(a, qrs, tl, w, cur, q0s);
     load_tile(a, drs, tl, w, cur, d0s);
     load_stats(cur, st0s);
@@ -487,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         load_tile(a, drs, tl, w, nxt, b == 0 ? d1s : d0s);
         load_stats(nxt, b == 0 ? st1s : st0s);
       }
-      compute(reinterpret_cast<const char*>(qt), reinterpret_cast<const char*>(dt), sts);
+      compute(rolec, reinterpret_cast<const char*>(qt), reinterpret_cast<const char*>(dt), sts);
       if (nxt >= g.nb) return false;
       cur = nxt;
       nxt = next_set(cur + 1);
@@ -495,9 +579,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     };
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
-  }
-  store_rows(dkp + hoff + (size_t)ktok * kHeadDim, dk, g.scale, gs);
-  store_rows(dvp + hoff + (size_t)ktok * kHeadDim, dv, 1.0f, gs);
+  };
+  if (dk_role)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
+  if (dk_role)
+    store_rows(dkp + hoff + (size_t)ktok * kHeadDim, acc, g.scale, gs);
+  else
+    store_rows(dvp + hoff + (size_t)ktok * kHeadDim, acc, 1.0f, gs);
 }
 
 hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bits* k,
@@ -516,12 +606,12 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((size_t)g.bh * a.nq8));
-  hipLaunchKernelGGL(bwd_dq_kernel, grid, dim3(kThreads), 0, stream, a, q, k, v, dout, stats, idx,
-                     cnt, dq);
+  hipLaunchKernelGGL(bwd_dq_kernel, grid, dim3(kBwdThreads), 0, stream, a, q, k, v, dout, stats,
+                     idx, cnt, dq);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, grid, dim3(kThreads), 0, stream, a, nbw, q, k, v, dout, stats,
-                     mask, dk, dv);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, grid, dim3(kBwdThreads), 0, stream, a, nbw, q, k, v, dout,
+                     stats, mask, dk, dv);
   return hipGetLastError();
 }
 
