@@ -7,8 +7,9 @@ Selections are inputs here: they come from the oracle's own selection
 
 Tolerances. Every gradient element is an fp32 sum of products of bf16
 operands: P and dS are rounded to bf16 before their products (relative error
-up to 2^-9 = 0.2% each) and the result is rounded to bf16 (2^-9). dK and dV
-stay at that level:
+up to 2^-9 = 0.2% each; the dK/dV kernel also forms dS from the bf16 P) and
+the result is rounded to bf16 (2^-9). dK and dV stay at that level (measured
+up to 0.3% mean, 0.8% max):
   max |gpu - oracle| <= 1.5e-2 * max |oracle|,  mean <= 5e-3 * mean |oracle|.
 dQ carries one more error: D = rowsum(dO * O) is formed from the forward's
 bf16 O (relative error 2^-9 per element). dS = P (dP - D) cancels where the

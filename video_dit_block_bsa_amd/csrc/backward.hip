@@ -25,9 +25,9 @@
 //                     query block's key-block list: dQ = s sum dS K.
 //   bwd_dkdv_kernel   one workgroup per (batch*head, key block), walking the
 //                     set bits of its mask row: dK = s sum dS^T Q, dV = sum P^T dO.
-// dQ and dK/dV each recompute S and dP, so no partial sums are exchanged
-// between workgroups (no floating-point atomics) and every output is written
-// once, by one workgroup.
+// dQ and dK/dV each compute S and dP (P recomputed from lse), so no partial
+// sums are exchanged between workgroups (no floating-point atomics) and
+// every output is written once, by one workgroup.
 //
 // MFMA layout (bf16 32x32x16, fp32 accumulate). A 128-row tile lives in LDS
 // as 128 rows of 256 bytes; chunk c (16 bytes) of row r is stored at chunk
@@ -120,27 +120,16 @@ constexpr int kBwdWaves = 8;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kRowsPerWave = kBlockTokens / kBwdWaves;
 
-// 32-row sub-tiles whose S (and dP) are computed together before their
-// probabilities feed the next products: 2 keeps more MFMAs in flight per
-// wave, 1 keeps fewer accumulators live.
-#ifndef BSA_BWD_DQ_GROUP
-#define BSA_BWD_DQ_GROUP 2
-#endif
-#ifndef BSA_BWD_DKDV_GROUP
-#define BSA_BWD_DKDV_GROUP 1
-#endif
-#ifndef BSA_BWD_FENCES
-#define BSA_BWD_FENCES 1
-#endif
-#if BSA_BWD_FENCES
-#define BSA_BWD_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define BSA_BWD_FENCE() ((void)0)
-#endif
-constexpr int kDqGroup = BSA_BWD_DQ_GROUP;
-constexpr int kDkdvGroup = BSA_BWD_DKDV_GROUP;
-static_assert(kDqGroup == 1 || kDqGroup == 2, "dQ: groups of 1 or 2 sub-tiles");
-static_assert(kDkdvGroup == 1 || kDkdvGroup == 2 || kDkdvGroup == 4, "dK/dV: 1, 2 or 4 sub-tiles");
+// dQ: 32-key sub-tiles whose S^T and dP^T are computed together before their
+// dS^T feeds the dQ products (2 keeps more MFMAs in flight per wave; 1 was
+// measured as fast).
+constexpr int kDqGroup = 2;
+
+// Keeps the scheduler from hoisting the next phase's LDS operand reads above
+// the current phase, which would raise register pressure for no gain (the
+// second wave on the SIMD hides the latency); measured 3% faster than
+// without.
+__device__ __forceinline__ void phase_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Per-lane byte offsets into a swizzled 128-row tile.
 struct TileLanes {
@@ -329,7 +318,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
           sacc[t2] = mfma(row_operand(kt, tt, s, tl), qf[s], sacc[t2]);
           pacc[t2] = mfma(row_operand(vt, tt, s, tl), df[s], pacc[t2]);
         }
-      BSA_BWD_FENCE();
+      phase_fence();
       // Accumulator value i of sub-tile tt is key 32tt + swap23(row): values
       // 0..7 are keys +8gs .. +8gs+7, values 8..15 keys +16+8gs ..; as a B
       // operand they are key steps 2tt and 2tt+1.
@@ -348,13 +337,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
           }
           dsf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, packed);
         }
-      BSA_BWD_FENCE();
+      phase_fence();
 #pragma unroll
       for (int ks = 0; ks < 2 * kDqGroup; ++ks)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           dq[u] = mfma(tr_operand(kt, 2 * (2 * kh + kDqGroup * h) + ks, u, tl), dsf[ks], dq[u]);
-      BSA_BWD_FENCE();
+      phase_fence();
     }
   };
 
@@ -413,15 +402,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- dK dV ---
-// Wave w owns keys 32(w%4) .. +31 of the key block, in one of two roles:
-//   w < 4  (dV):  S = Q K^T, P, dV^T += dO^T P
-//   w >= 4 (dK):  S = Q K^T, dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS
-// Splitting the roles keeps each wave within 256 registers (two waves per
-// SIMD, so one wave's exps and conversions overlap the other's MFMAs) at the
-// price of computing S twice. K (and V) of the wave's keys stay in registers
-// as B operands; Q, dO and the stats of a query block are double-buffered in
-// LDS. Query blocks come from the set bits of the key block's mask row, in
-// ascending order.
+// One workgroup of 8 waves per (batch*head, key block); wave w owns keys
+// 32(w%4) .. +31, in one of two roles:
+//   w < 4  (P role):  S = Q K^T, P, dV^T += dO^T P
+//   w >= 4 (dS role): dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS
+// One wave cannot hold K, V, dK and dV (192 registers) and its working set
+// in 256 VGPRs; split this way each role keeps one operand (K or V of its
+// keys, as the B operand of S or dP) and one accumulator, no product is
+// computed twice, and both roles issue the same number of MFMAs. P goes from
+// the P-role wave to the dS-role wave of the same keys as bf16 through a
+// two-slot LDS buffer per key slice, with one barrier per 32-query sub-tile
+// (it waits for LDS traffic only, never for the tile loads in flight). Q, dO
+// and the stats of a query block are double-buffered in LDS; query blocks
+// come from the set bits of the key block's mask row, in ascending order.
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     AttnArgs a, int nbw, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
@@ -433,7 +426,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) bf16_bits d1s[kBlockTokens * kHeadDim];
   __shared__ __attribute__((aligned(1024))) float st0s[2 * kBlockTokens];
   __shared__ __attribute__((aligned(1024))) float st1s[2 * kBlockTokens];
-  __shared__ uint32_t mrow[kBlockTokens];  // nbw <= 128 words (nb <= 4096)
+  __shared__ __attribute__((aligned(1024))) char xch[4 * 2 * 2048];  // [key slice][slot][2 KB]
+  __shared__ uint32_t mrow[kBlockTokens];
   const Geom& g = a.g;
   int pair, kb;
   xcd_block(a, pair, kb);
@@ -442,8 +436,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int ks = w & 3;            // key slice
-  const bool dk_role = (w >> 2) != 0;
+  const int ks = w & 3;
+  const bool ds_role = (w >> 2) != 0;
   const int n = lane & 31;
   const int gs = lane >> 5;
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
@@ -457,18 +451,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       (uint32_t)g.nb * (2 * kBlockTokens * 4), kBufferWord3);
   const TileLanes tl = tile_lanes(g, w, lane);
 
+  // P role keeps K of its keys (B operand of S), dS role keeps V (of dP).
   const int ktok = block_origin(a, kb) + slot_offset(g, 32 * ks + n);
-  bf16x8 kf[8], vf[8];
+  bf16x8 xf[8];
+  {
+    const bf16_bits* src = ds_role ? vp : kp;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const size_t off = hoff + (size_t)ktok * kHeadDim + 16 * s + 8 * gs;
-    kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + off));
-    vf[s] = dk_role ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + off)) : bf16x8{};
+    for (int s = 0; s < 8; ++s)
+      xf[s] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(src + hoff + (size_t)ktok * kHeadDim + 16 * s + 8 * gs));
   }
   if (t < nbw) mrow[t] = mask[((size_t)pair * g.nb + kb) * nbw + t];
   __syncthreads();
-  // First set bit at or after position `from` (nb if none). Every lane reads
-  // the same words, so the search runs on uniform values.
   auto next_set = [&](int from) __attribute__((always_inline)) -> int {
     int wd = from >> 5;
     if (wd >= nbw) return g.nb;
@@ -479,76 +473,69 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     }
     return wd * 32 + __builtin_ctz(bits);
   };
-  // Stats of a query block: 1 KB, one 16-byte load per lane of wave 0.
   auto load_stats = [&](int qb, float* dst) __attribute__((always_inline)) {
     if (w == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)dst, 16, (uint32_t)lane * 16,
                                                (uint32_t)qb * (2 * kBlockTokens * 4), 0, 0);
   };
 
-  // dV (dV role) or dK (dK role) of the wave's keys.
-  f32x16 acc[4];
+  f32x16 acc[4];  // dV (P role) or dK (dS role)
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
 
-  // The role is a template constant inside the loop (see dQ).
   auto compute = [&](auto rolec, const char* qt, const char* dt, const float* sts)
                      __attribute__((always_inline)) {
-    constexpr bool dk_role = decltype(rolec)::value != 0;
+    constexpr bool dsr = decltype(rolec)::value != 0;
 #pragma unroll
-    for (int h = 0; h < 4 / kDkdvGroup; ++h) {
-      f32x16 sacc[kDkdvGroup], pacc[kDkdvGroup];
+    for (int tt = 0; tt < 4; ++tt) {
+      char* slot = xch + ks * 4096 + (tt & 1) * 2048;
+      bf16x8 bop[2];
+      if constexpr (!dsr) {
+        f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int t2 = 0; t2 < kDkdvGroup; ++t2) sacc[t2] = pacc[t2] = f32x16{};
-      if constexpr (dk_role) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-          for (int t2 = 0; t2 < kDkdvGroup; ++t2) {
-            sacc[t2] = mfma(row_operand(qt, kDkdvGroup * h + t2, s, tl), kf[s], sacc[t2]);
-            pacc[t2] = mfma(row_operand(dt, kDkdvGroup * h + t2, s, tl), vf[s], pacc[t2]);
-          }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-#pragma unroll
-          for (int t2 = 0; t2 < kDkdvGroup; ++t2)
-            sacc[t2] = mfma(row_operand(qt, kDkdvGroup * h + t2, s, tl), kf[s], sacc[t2]);
-      }
-      BSA_BWD_FENCE();
-      // Value i of sub-tile tt is query 32tt + 8gs + (i % 8) + 16 (i / 8); as
-      // a B operand, values 0..7 and 8..15 are query steps 2tt and 2tt+1.
-      bf16x8 bf[2 * kDkdvGroup];
-#pragma unroll
-      for (int t2 = 0; t2 < kDkdvGroup; ++t2)
+        for (int s = 0; s < 8; ++s) sacc = mfma(row_operand(qt, tt, s, tl), xf[s], sacc);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int q0 = 32 * (kDkdvGroup * h + t2) + 16 * hh + 8 * gs;
+          const int q0 = 32 * tt + 16 * hh + 8 * gs;
           u32x4 packed;
 #pragma unroll
           for (int j2 = 0; j2 < 4; ++j2) {
             const int i0 = 8 * hh + 2 * j2;
             const f32x2 l2 = *reinterpret_cast<const f32x2*>(sts + q0 + 2 * j2);
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0], a.c_log2, -l2[0]));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0 + 1], a.c_log2, -l2[1]));
-            if constexpr (dk_role) {
-              const f32x2 d2 = *reinterpret_cast<const f32x2*>(sts + kBlockTokens + q0 + 2 * j2);
-              packed[j2] = pack_bf16(p0 * (pacc[t2][i0] - d2[0]), p1 * (pacc[t2][i0 + 1] - d2[1]));
-            } else {
-              packed[j2] = pack_bf16(p0, p1);
-            }
+            packed[j2] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i0], a.c_log2, -l2[0])),
+                                   __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i0 + 1], a.c_log2, -l2[1])));
           }
-          bf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, packed);
+          bop[hh] = __builtin_bit_cast(bf16x8, packed);
+          *reinterpret_cast<u32x4*>(slot + hh * 1024 + lane * 16) = packed;
         }
-      // dV^T += dO^T P (dV role) or dK^T += Q^T dS (dK role).
-      const char* xt = dk_role ? qt : dt;
-      BSA_BWD_FENCE();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the hand-off is written
+        workgroup_barrier();
+      } else {
+        f32x16 pacc = f32x16{};
 #pragma unroll
-      for (int k2 = 0; k2 < 2 * kDkdvGroup; ++k2)
+        for (int s = 0; s < 8; ++s) pacc = mfma(row_operand(dt, tt, s, tl), xf[s], pacc);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done with the slot's previous use
+        workgroup_barrier();
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc[u] = mfma(tr_operand(xt, 2 * kDkdvGroup * h + k2, u, tl), bf[k2], acc[u]);
-      BSA_BWD_FENCE();
+        for (int hh = 0; hh < 2; ++hh) {
+          const int q0 = 32 * tt + 16 * hh + 8 * gs;
+          const u32x4 pb = *reinterpret_cast<const u32x4*>(slot + hh * 1024 + lane * 16);
+          u32x4 packed;
+#pragma unroll
+          for (int j2 = 0; j2 < 4; ++j2) {
+            const int i0 = 8 * hh + 2 * j2;
+            const f32x2 d2 = *reinterpret_cast<const f32x2*>(sts + kBlockTokens + q0 + 2 * j2);
+            packed[j2] = pack_bf16(bf16_to_f32(pb[j2] & 0xffffu) * (pacc[i0] - d2[0]),
+                                   bf16_to_f32(pb[j2] >> 16) * (pacc[i0 + 1] - d2[1]));
+          }
+          bop[hh] = __builtin_bit_cast(bf16x8, packed);
+        }
+      }
+      const char* xt = dsr ? qt : dt;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = mfma(tr_operand(xt, 2 * tt + k2, u, tl), bop[k2], acc[u]);
     }
   };
 
@@ -580,11 +567,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
   };
-  if (dk_role)
+  if (ds_role)
     run(std::integral_constant<int, 1>{});
   else
     run(std::integral_constant<int, 0>{});
-  if (dk_role)
+  if (ds_role)
     store_rows(dkp + hoff + (size_t)ktok * kHeadDim, acc, g.scale, gs);
   else
     store_rows(dvp + hoff + (size_t)ktok * kHeadDim, acc, 1.0f, gs);
