@@ -44,6 +44,14 @@ with its reason in the design notes of the repository):
   blocks; a noisy query block may select any block. Softmax and selection run
   over the allowed blocks only.
 * k larger than the number of allowed blocks is clamped to that number.
+* Decoupled query and key blocks ([DeepDive] "Implementation details and
+  design trade-offs" reports query blocks of 64 or 128 tokens and key blocks
+  of 64 to 1024 tokens): queries are cut with the query chunk (ct, ch, cw)
+  and keys with the key chunk (ctk, chk, cwk); each is pooled over its own
+  blocks, S_pool is N_q x N_k, and a query block attends to the tokens of the
+  key blocks it selects. Block order and intra-block order follow the same
+  [N_T, N_H, N_W] / [t, h, w] rule for both. Condition frames must be a
+  multiple of both t extents; condition key blocks are the leading ones.
 
 Backward pass (the gradients of the attention step for fixed selections):
 [DeepDive] "Implementation details and design trade-offs" states that the
@@ -82,6 +90,7 @@ __all__ = [
     "index_stride",
     "forward_lse_head",
     "backward_head",
+    "key_geometry",
 ]
 
 
@@ -102,6 +111,10 @@ class Geometry:
     ch: int = 4
     cw: int = 8
     cond_frames: int = 0
+    # Key chunk; 0 means the same as the query chunk.
+    ctk: int = 0
+    chk: int = 0
+    cwk: int = 0
 
     def __post_init__(self):
         for name in ("T", "H", "W", "ct", "ch", "cw"):
@@ -109,10 +122,40 @@ class Geometry:
                 raise ValueError(f"{name} must be positive")
         if self.T % self.ct or self.H % self.ch or self.W % self.cw:
             raise ValueError("latent grid must be divisible by the chunk shape")
+        if (self.ctk, self.chk, self.cwk) != (0, 0, 0):
+            if min(self.ctk, self.chk, self.cwk) <= 0:
+                raise ValueError("key chunk extents must all be positive (or all 0)")
+            if self.T % self.ctk or self.H % self.chk or self.W % self.cwk:
+                raise ValueError("latent grid must be divisible by the key chunk shape")
         if self.cond_frames < 0 or self.cond_frames % self.ct or (
             self.cond_frames and self.cond_frames >= self.T
         ):
             raise ValueError("cond_frames must be a multiple of ct and < T")
+        if self.cond_frames % self.key_chunk[0]:
+            raise ValueError("cond_frames must be a multiple of the key chunk's t extent")
+
+    @property
+    def key_chunk(self) -> tuple:
+        if (self.ctk, self.chk, self.cwk) == (0, 0, 0):
+            return (self.ct, self.ch, self.cw)
+        return (self.ctk, self.chk, self.cwk)
+
+    @property
+    def nk(self) -> int:
+        """Tokens per key block."""
+        a, b, c = self.key_chunk
+        return a * b * c
+
+    @property
+    def num_key_blocks(self) -> int:
+        a, b, c = self.key_chunk
+        return (self.T // a) * (self.H // b) * (self.W // c)
+
+    @property
+    def cond_key_blocks(self) -> int:
+        """Key blocks made of condition tokens (the first ones in key-block order)."""
+        a, b, c = self.key_chunk
+        return (self.cond_frames // a) * (self.H // b) * (self.W // c)
 
     @property
     def n(self) -> int:
@@ -140,8 +183,14 @@ class Geometry:
 
     @property
     def cond_blocks(self) -> int:
-        """Key blocks made of condition tokens (the first ones in block order)."""
+        """Query blocks made of condition tokens (the first ones in block order)."""
         return (self.cond_frames // self.ct) * self.nH * self.nW
+
+
+def key_geometry(g: Geometry) -> Geometry:
+    """The same grid cut with the key chunk: its blocks are g's key blocks."""
+    a, b, c = g.key_chunk
+    return Geometry(g.T, g.H, g.W, a, b, c, g.cond_frames)
 
 
 @dataclass(frozen=True)
@@ -220,11 +269,11 @@ def allowed_key_blocks(g: Geometry, i: int) -> int:
 
     Block-causal ([DeepDive-KV] "Attention structure"): condition queries see
     condition keys only; noisy queries see all keys. Condition tokens are the
-    first frames, so they occupy key blocks 0 .. cond_blocks-1.
+    first frames, so they occupy key blocks 0 .. cond_key_blocks-1.
     """
     if g.cond_frames and i < g.cond_blocks:
-        return g.cond_blocks
-    return g.num_blocks
+        return g.cond_key_blocks
+    return g.num_key_blocks
 
 
 def softmax_allowed(scores_row: np.ndarray, n_allowed: int) -> np.ndarray:
@@ -271,13 +320,12 @@ def select_head(
 ):
     """Block selection for one (batch, head).
 
-    Returns (idx, cnt, scores): idx is int32 [Nb, stride] with ascending ids
-    padded by -1, cnt is int32 [Nb], scores is the float64 [Nb, Nb] pooled
-    score matrix with -inf where a key block is not allowed.
+    Returns (idx, cnt, scores): idx is int32 [Nb, stride] with ascending
+    key-block ids padded by -1, cnt is int32 [Nb], scores is the float64
+    [Nb, Nk] pooled score matrix with -inf where a key block is not allowed.
     """
-    perm = block_token_order(g)
-    qp = pool_blocks(q, perm, g.n)
-    kp = pool_blocks(k, perm, g.n)
+    qp = pool_blocks(q, block_token_order(g), g.n)
+    kp = pool_blocks(k, block_token_order(key_geometry(g)), g.nk)
     s = pooled_scores(qp, kp, scale)
     nb = g.num_blocks
     stride = index_stride(params)
@@ -305,19 +353,23 @@ def attend_query_block(
     key_blocks,
     scale: float,
     perm: np.ndarray | None = None,
+    kperm: np.ndarray | None = None,
 ) -> np.ndarray:
     """Attention of query block i restricted to the given key blocks.
 
     [DeepDive] "Sparse attention computation": O = softmax(QK^T/sqrt(d) with
     non-selected keys at -inf) V. Keys outside the selected blocks contribute
     exp(-inf) = 0, so softmax over the gathered keys is the same thing.
-    Returns [n, d] float64 rows in the block's slot order.
+    ``perm`` / ``kperm`` are the query and key block orders (computed when
+    not given). Returns [n, d] float64 rows in the block's slot order.
     """
     if perm is None:
         perm = block_token_order(g)
-    n = g.n
+    if kperm is None:
+        kperm = block_token_order(key_geometry(g))
+    n, nk = g.n, g.nk
     qi = np.asarray(q, dtype=np.float64)[perm[i * n : (i + 1) * n]]
-    tok = np.concatenate([perm[j * n : (j + 1) * n] for j in key_blocks])
+    tok = np.concatenate([kperm[j * nk : (j + 1) * nk] for j in key_blocks])
     ks = np.asarray(k, dtype=np.float64)[tok]
     vs = np.asarray(v, dtype=np.float64)[tok]
     logits = (qi @ ks.T) * scale
@@ -339,11 +391,12 @@ def bsa_head(
     latent order, idx, cnt, scores)."""
     idx, cnt, scores = select_head(q, k, g, params, scale)
     perm = block_token_order(g)
+    kperm = block_token_order(key_geometry(g))
     out = np.zeros((g.seq_len, np.asarray(v).shape[-1]), dtype=np.float64)
     n = g.n
     for i in range(g.num_blocks):
         sel = idx[i, : cnt[i]]
-        out[perm[i * n : (i + 1) * n]] = attend_query_block(q, k, v, g, i, sel, scale, perm)
+        out[perm[i * n : (i + 1) * n]] = attend_query_block(q, k, v, g, i, sel, scale, perm, kperm)
     return out, idx, cnt, scores
 
 
@@ -351,20 +404,21 @@ def dense_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Geometry, scale: 
     """Dense softmax attention over every allowed key block (block-causal when
     cond_frames > 0), one (batch, head); [S, d] float64 in latent order."""
     perm = block_token_order(g)
+    kperm = block_token_order(key_geometry(g))
     out = np.zeros((g.seq_len, np.asarray(v).shape[-1]), dtype=np.float64)
     n = g.n
     for i in range(g.num_blocks):
         na = allowed_key_blocks(g, i)
         out[perm[i * n : (i + 1) * n]] = attend_query_block(
-            q, k, v, g, i, range(na), scale, perm
+            q, k, v, g, i, range(na), scale, perm, kperm
         )
     return out
 
 
-def _gathered(q, k, v, g, i, key_blocks, perm):
-    n = g.n
+def _gathered(q, k, v, g, i, key_blocks, perm, kperm):
+    n, nk = g.n, g.nk
     qt = perm[i * n : (i + 1) * n]
-    kt = np.concatenate([perm[j * n : (j + 1) * n] for j in key_blocks])
+    kt = np.concatenate([kperm[j * nk : (j + 1) * nk] for j in key_blocks])
     return qt, kt
 
 
@@ -375,6 +429,7 @@ def forward_lse_head(q, k, v, g: Geometry, idx, cnt, scale: float, query_blocks=
     lse [S]) in latent order, float64. With `query_blocks` given, only those
     query blocks are computed (the others stay 0 / -inf)."""
     perm = block_token_order(g)
+    kperm = block_token_order(key_geometry(g))
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -384,7 +439,7 @@ def forward_lse_head(q, k, v, g: Geometry, idx, cnt, scale: float, query_blocks=
         blocks = [int(j) for j in idx[i, : cnt[i]]]
         if not blocks:
             continue
-        qt, kt = _gathered(q, k, v, g, i, blocks, perm)
+        qt, kt = _gathered(q, k, v, g, i, blocks, perm, kperm)
         logits = (q[qt] @ k[kt].T) * scale
         m = logits.max(axis=1, keepdims=True)
         e = np.exp(logits - m)
@@ -412,6 +467,7 @@ def backward_head(q, k, v, do, g: Geometry, idx, cnt, scale: float, query_blocks
     block that only those query blocks keep (the sums above run over the
     query blocks that kept each key block)."""
     perm = block_token_order(g)
+    kperm = block_token_order(key_geometry(g))
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -423,7 +479,7 @@ def backward_head(q, k, v, do, g: Geometry, idx, cnt, scale: float, query_blocks
         blocks = [int(j) for j in idx[i, : cnt[i]]]
         if not blocks:
             continue
-        qt, kt = _gathered(q, k, v, g, i, blocks, perm)
+        qt, kt = _gathered(q, k, v, g, i, blocks, perm, kperm)
         logits = (q[qt] @ k[kt].T) * scale
         logits -= logits.max(axis=1, keepdims=True)
         p = np.exp(logits)

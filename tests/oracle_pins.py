@@ -472,6 +472,118 @@ def pin_backward_query_block_subset():
     assert np.all(l_sub[blk(1)] == -np.inf) and np.all(o_sub[blk(2)] == 0)
 
 
+# ---------------------------------------------- decoupled key chunk pins ---
+def _key_block_of_token(g):
+    """Key-block id of every latent-order token, from its grid coordinates
+    and the key chunk."""
+    a, b, c = g.key_chunk
+    t, h, w = _coords(g, np.arange(g.seq_len))
+    return ((t // a) * (g.H // b) + (h // b)) * (g.W // c) + (w // c)
+
+
+# Query chunk [4, 4, 8] (128 tokens) with key chunks of 64, 256 and 1024
+# tokens on a 8 x 16 x 32 grid, with and without condition frames.
+_KEY_CASES = (
+    (O.Geometry(8, 16, 32, ctk=2, chk=4, cwk=8), O.SelectParams("topk", k=5)),
+    (O.Geometry(8, 16, 32, ctk=4, chk=8, cwk=8, cond_frames=4),
+     O.SelectParams("cdf", p=0.7, k_min=1, k_max=6)),
+    (O.Geometry(8, 16, 32, ctk=8, chk=8, cwk=16), O.SelectParams("topk", k=2)),
+    (O.Geometry(8, 16, 32, ctk=2, chk=4, cwk=8, cond_frames=4), O.SelectParams("topk", k=7)),
+)
+
+
+def pin_key_chunk_mask_formula():
+    """Decoupled key blocks: gathered attention equals the mask formula over
+    the whole sequence, with each token's query block and key block computed
+    from its coordinates with the two chunk shapes."""
+    rng = np.random.default_rng(31)
+    for g, p in _KEY_CASES:
+        q, k, v = _rand(rng, g)
+        scale = 1 / np.sqrt(q.shape[1])
+        out, idx, cnt, _ = O.bsa_head(q, k, v, g, p, scale)
+        qb, kb = _block_of_token(g), _key_block_of_token(g)
+        sel = np.zeros((g.num_blocks, g.num_key_blocks), dtype=bool)
+        for i in range(g.num_blocks):
+            ids = idx[i, : cnt[i]]
+            assert np.all(ids < O.allowed_key_blocks(g, i))
+            sel[i, ids] = True
+        ref = _textbook_attention(q, k, v, scale, sel[qb[:, None], kb[None, :]])
+        assert np.abs(out - ref).max() < 1e-12, "gathered attention != masked attention"
+
+
+def pin_key_chunk_pooled_bruteforce():
+    """Decoupled key blocks: pooled scores from coordinate accumulation, query
+    blocks with the query chunk and key blocks with the key chunk; condition
+    rows see exactly the key blocks made of condition frames."""
+    rng = np.random.default_rng(32)
+    for g, _ in _KEY_CASES:
+        q, k, _ = _rand(rng, g)
+        scale = 0.29
+        qb, kb = _block_of_token(g), _key_block_of_token(g)
+        qs = np.zeros((g.num_blocks, q.shape[1]))
+        ks = np.zeros((g.num_key_blocks, k.shape[1]))
+        np.add.at(qs, qb, q)
+        np.add.at(ks, kb, k)
+        qs /= np.bincount(qb)[:, None]
+        ks /= np.bincount(kb)[:, None]
+        s_ref = qs @ ks.T * scale
+        _, _, scores = O.select_head(q, k, g, O.SelectParams("topk", k=1), scale)
+        assert scores.shape == (g.num_blocks, g.num_key_blocks)
+        t = _coords(g, np.arange(g.seq_len))[0]
+        cond_kb = np.unique(kb[t < g.cond_frames]) if g.cond_frames else np.array([], int)
+        for i in range(g.num_blocks):
+            na = O.allowed_key_blocks(g, i)
+            if g.cond_frames and i < g.cond_blocks:
+                assert np.array_equal(np.arange(na), cond_kb)
+            else:
+                assert na == g.num_key_blocks
+            assert np.abs(scores[i, :na] - s_ref[i, :na]).max() < 1e-12
+            assert np.all(np.isneginf(scores[i, na:]))
+
+
+def pin_key_chunk_dense():
+    """Decoupled key blocks: keeping every allowed key block gives textbook
+    attention (block-causal over the token sets when there are condition
+    frames), whatever the key chunk."""
+    rng = np.random.default_rng(33)
+    for g, _ in _KEY_CASES:
+        q, k, v = _rand(rng, g)
+        scale = 0.23
+        out, idx, cnt, _ = O.bsa_head(q, k, v, g, O.SelectParams("topk", k=g.num_key_blocks), scale)
+        cond = _coords(g, np.arange(g.seq_len))[0] < g.cond_frames
+        ref = np.zeros_like(q)
+        if cond.any():
+            ref[cond] = _textbook_attention(q[cond], k[cond], v[cond], scale)
+        ref[~cond] = _textbook_attention(q[~cond], k, v, scale)
+        assert np.abs(out - ref).max() < 1e-12
+        assert np.abs(O.dense_head(q, k, v, g, scale) - ref).max() < 1e-12
+
+
+def pin_key_chunk_backward_autograd():
+    """Decoupled key blocks: backward_head equals torch float64 autograd of
+    the mask formula (token-level mask from both chunk shapes)."""
+    import torch
+
+    rng = np.random.default_rng(34)
+    g = O.Geometry(4, 8, 16, ctk=4, chk=4, cwk=4)  # 128-token queries, 64-token keys
+    q, k, v, do = (rng.standard_normal((g.seq_len, 8)) for _ in range(4))
+    nk = g.num_key_blocks
+    idx = np.array([[0, 3, 6, -1], [1, 2, 5, 7], [4, -1, -1, -1], [0, 1, 6, 7]])
+    cnt = np.array([3, 4, 1, 4])
+    scale = 0.31
+    dq, dk, dv = O.backward_head(q, k, v, do, g, idx, cnt, scale)
+    sel = np.zeros((g.num_blocks, nk), dtype=bool)
+    for i in range(g.num_blocks):
+        sel[i, idx[i, : cnt[i]]] = True
+    allowed = torch.tensor(sel[_block_of_token(g)[:, None], _key_block_of_token(g)[None, :]])
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    logits = ((tq @ tk.T) * scale).masked_fill(~allowed, float("-inf"))
+    out = torch.softmax(logits, dim=1) @ tv
+    (out * torch.tensor(do)).sum().backward()
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.abs(mine - ref.numpy()).max() < 1e-10
+
+
 ALL_PINS = [
     pin_block_order_geometry,
     pin_handworked_golden,
@@ -493,4 +605,8 @@ ALL_PINS = [
     pin_backward_dv_total,
     pin_forward_lse,
     pin_backward_query_block_subset,
+    pin_key_chunk_mask_formula,
+    pin_key_chunk_pooled_bruteforce,
+    pin_key_chunk_dense,
+    pin_key_chunk_backward_autograd,
 ]

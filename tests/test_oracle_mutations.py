@@ -15,12 +15,12 @@ _orig_cdf = O.select_cdf
 _orig_lse = O.forward_lse_head
 
 
-def _attend_no_scale(q, k, v, g, i, key_blocks, scale, perm=None):
-    return _orig_attend(q, k, v, g, i, key_blocks, 1.0, perm)
+def _attend_no_scale(q, k, v, g, i, key_blocks, scale, perm=None, kperm=None):
+    return _orig_attend(q, k, v, g, i, key_blocks, 1.0, perm, kperm)
 
 
-def _attend_keys_as_values(q, k, v, g, i, key_blocks, scale, perm=None):
-    return _orig_attend(q, k, k, g, i, key_blocks, scale, perm)
+def _attend_keys_as_values(q, k, v, g, i, key_blocks, scale, perm=None, kperm=None):
+    return _orig_attend(q, k, k, g, i, key_blocks, scale, perm, kperm)
 
 
 def _order_hw_swapped(g):
@@ -153,6 +153,11 @@ MUTANTS = {
     "backward dK unscaled": ("backward_head", _backward_variant("dk unscaled")),
     "backward dV from P instead of P^T": ("backward_head", _backward_variant("dv from p")),
     "lse without the max": ("forward_lse_head", _lse_without_max),
+    "keys cut with the query chunk": (
+        "key_geometry", lambda g: O.Geometry(g.T, g.H, g.W, g.ct, g.ch, g.cw, g.cond_frames)),
+    "condition key blocks counted in query blocks": (
+        "allowed_key_blocks",
+        lambda g, i: g.cond_blocks if (g.cond_frames and i < g.cond_blocks) else g.num_key_blocks),
 }
 
 
