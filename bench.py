@@ -73,7 +73,9 @@ def cpu_baseline(w, q, k, v, blocks: int, seconds: float):
                        if i.get("user_api") == "blas"), default=1)
     except Exception:  # threadpoolctl missing: report the visible cores
         threads = os.cpu_count() or 1
-    g = O.Geometry(w.T, w.H, w.W, *w.chunk, cond_frames=w.cond_frames)
+    kc = tuple(w.key_chunk) if w.key_chunk else (0, 0, 0)
+    g = O.Geometry(w.T, w.H, w.W, *w.chunk, cond_frames=w.cond_frames, ctk=kc[0], chk=kc[1],
+                   cwk=kc[2])
     sp = (O.SelectParams("topk", k=w.k) if w.mode == "topk"
           else O.SelectParams("cdf", p=w.p, k_min=w.k_min, k_max=w.k_max))
     scale = 1.0 / math.sqrt(w.head_dim)
@@ -83,15 +85,16 @@ def cpu_baseline(w, q, k, v, blocks: int, seconds: float):
     t_sel = time.perf_counter() - t0
     blocks = min(blocks, g.num_blocks)
     perm = O.block_token_order(g)
+    kperm = O.block_token_order(O.key_geometry(g))
     t0 = time.perf_counter()
     done = 0
     while done < blocks and (done == 0 or time.perf_counter() - t0 < seconds):
-        O.attend_query_block(qf, kf, vf, g, done, idx[done, : cnt[done]], scale, perm)
+        O.attend_query_block(qf, kf, vf, g, done, idx[done, : cnt[done]], scale, perm, kperm)
         done += 1
     t_att = time.perf_counter() - t0
     blocks = done
     t = t_att + t_sel * blocks / g.num_blocks
-    flops = 4.0 * g.n * g.n * w.head_dim * float(cnt[:blocks].sum())
+    flops = 4.0 * g.n * g.nk * w.head_dim * float(cnt[:blocks].sum())
     return {
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
@@ -268,7 +271,7 @@ def main():
         del od
 
     bwd = None
-    if args.backward_steps > 0:
+    if args.backward_steps > 0 and not w.key_chunk:
         bwd = backward_bench(w, problem, qd, kd, vd, idx, cnt, stride, ws_att, stream, eff,
                              args.backward_steps)
 
@@ -312,7 +315,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{w.name}: latent grid {w.T}x{w.H}x{w.W} ({w.seq_len} tokens, "
-                         f"{w.num_blocks} blocks of [{ct},{ch},{cw}]), batch {w.batch}, "
+                         f"{w.num_blocks} blocks of [{ct},{ch},{cw}]"
+                         + (f", {w.num_key_blocks} key blocks of [{','.join(map(str, w.kchunk))}]"
+                            if w.key_chunk else "")
+                         + f"), batch {w.batch}, "
                          f"{w.heads} heads, head_dim {w.head_dim}, {sel_desc}"
                          + (f", cond_frames {w.cond_frames}" if w.cond_frames else "")),
             "tokens": w.seq_len,

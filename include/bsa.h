@@ -28,8 +28,10 @@
  *   S = T*H*W tokens in latent order s = (t*H + h)*W + w. Pointers are device
  *   pointers, 16-byte aligned. head_dim must be 128.
  * Blocks. nT = T/ct, nH = H/ch, nW = W/cw; block id
- *   i = (bt*nH + bh)*nW + bw; a block holds ct*ch*cw = 128 tokens. The grid
- *   must divide by the chunk shape.
+ *   i = (bt*nH + bh)*nW + bw; a query block holds ct*ch*cw = 128 tokens. The
+ *   grid must divide by the chunk shape. Key blocks are numbered the same way
+ *   with the key chunk (ctk, chk, cwk) when one is given (Nk of them), else
+ *   they are the query blocks (Nk = Nb).
  * Ownership. The caller owns every buffer. The library never allocates,
  *   frees, or synchronises; all work is enqueued on `stream` (a hipStream_t;
  *   NULL is the default stream). Workspace contents do not carry over from
@@ -73,8 +75,15 @@ typedef struct bsa_problem {
   int32_t head_dim;    /* must be 128 */
   int32_t T, H, W;     /* latent grid, each > 0; T*H*W < 2^24 */
   int32_t ct, ch, cw;  /* chunk shape; ct*ch*cw must be 128 and divide the grid */
-  int32_t cond_frames; /* 0: no block-causal mask; else a multiple of ct, < T */
+  int32_t cond_frames; /* 0: no block-causal mask; else a multiple of ct (and of
+                          ctk), < T */
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t ctk, chk, cwk; /* key chunk shape; all 0: the same as the query chunk.
+                            Otherwise ctk*chk*cwk must be 64, 128, 256, 512 or
+                            1024 and divide the grid ("Implementation details
+                            and design trade-offs": query blocks of 64-128 and
+                            key blocks of 64-1024 tokens). Key-block ids in idx
+                            then refer to these blocks. */
 } bsa_problem;
 
 /* Block-selection rule. */
@@ -91,9 +100,10 @@ typedef struct bsa_select_params {
  * (CDF). Returns -1 on invalid parameters. */
 int32_t bsa_index_stride(const bsa_select_params* params);
 
-/* Bytes of device workspace bsa_select needs (pooled Q/K and the pooled
- * score matrix: 4*(2*128 + Nb) bytes per block per (batch, head), plus
- * alignment). Returns 0 on invalid arguments. */
+/* Bytes of device workspace bsa_select needs: pooled Q (512 bytes per query
+ * block), pooled K (512 bytes per key block) and the Nb x Nk pooled score
+ * matrix (fp32), per (batch, head), each part rounded up to 256 bytes.
+ * Returns 0 on invalid arguments. */
 size_t bsa_select_workspace_bytes(const bsa_problem* problem,
                                   const bsa_select_params* params);
 
@@ -106,12 +116,13 @@ size_t bsa_attention_workspace_bytes(const bsa_problem* problem);
 /* Block selection: pooling, pooled scores, softmax and top-k / CDF selection
  * with the block-causal restriction (steps 1-3 above).
  *   q, k     bf16 [batch, heads, S, 128], read only.
- *   idx      int32 [batch, heads, Nb, stride] out: kept key-block ids of each
- *            query block in ascending order, then -1 up to stride.
+ *   idx      int32 [batch, heads, Nb, stride] out: kept key-block ids
+ *            (0 .. Nk-1) of each query block in ascending order, then -1 up
+ *            to stride.
  *   cnt      int32 [batch, heads, Nb] out: number of kept key blocks.
  *   Ties between equal pooled scores keep the lower key-block id. A
  *   condition query block only considers condition key blocks.
- * Limits: Nb <= 4096 key blocks per (batch, head) (BSA_ERR_UNSUPPORTED). */
+ * Limits: Nk <= 4096 key blocks per (batch, head) (BSA_ERR_UNSUPPORTED). */
 bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* params,
                       const void* q, const void* k, int32_t* idx, int32_t* cnt,
                       void* workspace, size_t workspace_bytes, void* stream);
@@ -120,9 +131,10 @@ bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* param
  * block, softmax(Q K_sel^T * scale) V_sel over the tokens of its kept key
  * blocks, written in latent order.
  *   idx, cnt   as written by bsa_select (any ascending or unordered list of
- *              key-block ids is accepted); ids outside [0, Nb) are skipped
+ *              key-block ids is accepted); ids outside [0, Nk) are skipped
  *              and cnt is clamped to [0, idx_stride]. A query block with no
- *              key blocks gets zeros.
+ *              key blocks gets zeros. Key blocks of 64 tokens are taken two
+ *              at a time (the last one of an odd count alone).
  *   o          bf16 [batch, heads, S, 128] out.
  * The softmax is computed in fp32 from bf16 products accumulated in fp32;
  * the probabilities are rounded to bf16 before multiplying V. */
@@ -133,8 +145,8 @@ bsa_status bsa_attention(const bsa_problem* problem, const void* q, const void* 
 
 /* Dense softmax attention over every key the query may see (all keys, or
  * condition keys only for condition queries when cond_frames > 0): the
- * baseline that BSA is measured against, using the same tile engine.
- * Arguments as for bsa_attention. */
+ * baseline that BSA is measured against, using the same tile engine. The key
+ * chunk plays no part. Arguments as for bsa_attention. */
 bsa_status dense_attention(const bsa_problem* problem, const void* q, const void* k,
                            const void* v, void* o, void* workspace,
                            size_t workspace_bytes, void* stream);
@@ -182,7 +194,8 @@ size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
  * P is recomputed in fp32 from lse; the products run in bf16 with fp32
  * accumulation (P and dS are rounded to bf16 as MFMA operands). No
  * floating-point atomics: results are bit-identical from run to run.
- * Limits: Nb <= 4096 key blocks per (batch, head) (BSA_ERR_UNSUPPORTED). */
+ * Limits: Nb <= 4096 blocks per (batch, head); the key chunk must be the
+ * query chunk (BSA_ERR_UNSUPPORTED otherwise). */
 bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const void* k,
                              const void* v, const void* o, const void* dout, const float* lse,
                              const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* dq,

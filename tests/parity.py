@@ -83,7 +83,7 @@ def run_dense(problem, q_d, k_d, v_d):
 # ------------------------------------------------------------ oracle side ---
 def geometry(problem) -> O.Geometry:
     return O.Geometry(problem.T, problem.H, problem.W, problem.ct, problem.ch, problem.cw,
-                      problem.cond_frames)
+                      problem.cond_frames, problem.ctk, problem.chk, problem.cwk)
 
 
 def oracle_params(params) -> O.SelectParams:
@@ -190,6 +190,7 @@ def compare_outputs(out_bits, q_bits, k_bits, v_bits, g, blocks_of_pair, scale, 
     grouped per (batch, head) so each head is widened to float64 once.
     Returns (max_abs, mean_abs, n_values)."""
     perm = O.block_token_order(g)
+    kperm = O.block_token_order(O.key_geometry(g))
     n = g.n
     Hh = q_bits.shape[1]
     by_pair = {}
@@ -203,7 +204,7 @@ def compare_outputs(out_bits, q_bits, k_bits, v_bits, g, blocks_of_pair, scale, 
         v = O.bf16_bits_to_f64(v_bits[b, h])
         out = []
         for i in by_pair[pair]:
-            ref = O.attend_query_block(q, k, v, g, i, blocks_of_pair(pair, i), scale, perm)
+            ref = O.attend_query_block(q, k, v, g, i, blocks_of_pair(pair, i), scale, perm, kperm)
             got = O.bf16_bits_to_f64(out_bits[b, h][perm[i * n : (i + 1) * n]])
             err = np.abs(got - ref)
             out.append((err.max(), err.sum(), err.size, bool(np.isfinite(got).all())))

@@ -230,3 +230,25 @@ def test_lse_forward_rejects_bad_lse():
     assert call(None) == INVALID
     assert call(GiB4 * 7 + 2) == INVALID
     assert call(GiB4 * 4) == INVALID  # is o
+
+
+def test_key_chunk_checks():
+    """Key chunk: all 0 or all positive, 64..1024 tokens (powers of two),
+    dividing the grid, condition frames a multiple of ctk; selection limited
+    to 4096 key blocks; the backward needs equal chunks."""
+    sp = B.SelectParams.topk(4)
+    ok = _problem(key_chunk=(4, 8, 8))
+    nb, nbk = 1680, 840
+    sel = B.select_workspace_bytes(ok, sp)
+    want = 32 * nb * 512 + 32 * nbk * 512 + 32 * nb * nbk * 4
+    assert want <= sel < want + 3 * 256
+    p = _problem()
+    p.ctk, p.chk, p.cwk = 4, 0, 8
+    assert _select(p, sp) == INVALID
+    assert _select(_problem(key_chunk=(2, 2, 8)), sp) == UNSUPPORTED     # 32 tokens
+    assert _select(_problem(key_chunk=(8, 16, 16)), sp) == UNSUPPORTED   # 2048 tokens
+    assert _select(_problem(key_chunk=(4, 4, 64)), sp) == UNSUPPORTED    # 80 % 64 != 0
+    assert _select(_problem(key_chunk=(8, 4, 8), cond_frames=4), sp) == INVALID
+    assert _select(_problem(T=4 * 100, key_chunk=(2, 4, 8)), sp) == UNSUPPORTED  # 24,000 key blocks
+    assert _bwd(_problem(key_chunk=(4, 8, 8))) == UNSUPPORTED
+    assert B.attention_bwd_workspace_bytes(_problem(key_chunk=(4, 8, 8))) > 0

@@ -240,7 +240,58 @@ def test_skips_invalid_ids_and_clamps_cnt():
             assert np.all(got == 0.0)
 
 
-@pytest.mark.parametrize("name", ["480p", "720p", "long", "vc"])
+@pytest.mark.parametrize("grid,chunk,key_chunk,params,cond", [
+    ((8, 16, 32), (4, 4, 8), (2, 4, 8), SelectParams.topk(5), 0),    # 64-token keys, odd count
+    ((8, 16, 32), (4, 4, 8), (2, 4, 8), SelectParams.topk(6), 0),    # 64-token keys, even count
+    ((8, 16, 32), (4, 4, 8), (4, 8, 8), SelectParams.topk(3), 0),    # 256
+    ((8, 16, 32), (4, 4, 8), (8, 8, 16), SelectParams.topk(2), 0),   # 1024
+    ((8, 16, 32), (2, 8, 8), (4, 8, 16), SelectParams.topk(3), 0),   # 512, another query chunk
+    ((8, 16, 32), (4, 4, 8), (4, 8, 8), SelectParams.cdf(0.8, 1, 6), 4),
+    ((8, 16, 32), (4, 4, 8), (2, 4, 8), SelectParams.cdf(0.7, 1, 9), 4),
+])
+def test_key_chunks(grid, chunk, key_chunk, params, cond):
+    """Key blocks cut with their own chunk (64 to 1024 tokens): every index
+    row and every output against the oracle."""
+    T, H, W = grid
+    q, k, v = make_qkv(T, H, W, 2, kind="field", seed=17)
+    problem = Problem.make(T, H, W, 2, chunk=chunk, cond_frames=cond, key_chunk=key_chunk)
+    _run_and_compare(problem, params, q, k, v)
+
+
+@pytest.mark.parametrize("key_chunk", [(2, 4, 8), (4, 8, 8)])
+def test_key_chunks_invalid_ids_and_clamps(key_chunk):
+    """With 64- and 256-token key blocks: ids outside [0, Nk) are skipped, cnt
+    is clamped to the stride, a lone last 64-token block is handled, and a
+    row with no valid block gives zeros."""
+    import torch
+
+    T, H, W = 8, 8, 16
+    q, k, v = make_qkv(T, H, W, 1, kind="iid", seed=23)
+    problem = Problem.make(T, H, W, 1, key_chunk=key_chunk)
+    g = PT.geometry(problem)
+    nk = g.num_key_blocks
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    rows = [[0, nk + 2, 1, nk - 1], [nk, -1, -1, -1], [1, nk - 2, 0, 0], [3, 2, 1, 0],
+            [0, 0, 0, 0], [0, 1, 2, 3], [2, -7, 2, 2], [nk - 1, 1, 0, 2]]
+    cnt_l = [4, 1, 3, 9, 0, -5, 3, 4]
+    idx = torch.tensor([[min(x, 10**6) for x in r] for r in rows], dtype=torch.int32, device="cuda")
+    cnt = torch.tensor(cnt_l, dtype=torch.int32, device="cuda")
+    out = O.bf16_bits_to_f64(PT.from_device(PT.run_attention(problem, qd, kd, vd, idx, cnt, 4)))
+    perm = O.block_token_order(g)
+    kperm = O.block_token_order(O.key_geometry(g))
+    qf, kf, vf = (O.bf16_bits_to_f64(a[0, 0]) for a in (q, k, v))
+    for i in range(g.num_blocks):
+        c = min(max(cnt_l[i], 0), 4)
+        want = [x for x in rows[i][:c] if 0 <= x < nk]
+        got = out[0, 0][perm[i * g.n:(i + 1) * g.n]]
+        if want:
+            ref = O.attend_query_block(qf, kf, vf, g, i, want, SCALE, perm, kperm)
+            assert np.abs(got - ref).max() <= PT.MAX_ABS, (i, want)
+        else:
+            assert np.all(got == 0.0)
+
+
+@pytest.mark.parametrize("name", ["480p", "720p", "long", "vc", "long_k64", "long_k256"])
 def test_full_size_workload(name):
     """Full-size workloads in the configuration the benchmark times: every
     index row against the oracle, outputs on a seeded sample."""

@@ -59,3 +59,31 @@ def test_tile_offsets_from_one_lane_offset():
                         v_direct = rowoff + (((lane & 15) ^ (4 * (row & 3))) << 4)
                         assert (k0 ^ sb64[i]) + rows_s[i] + h * half == k_direct
                         assert v0 + rows_s[i] + h * half == v_direct
+
+
+def key_chunk_shapes():
+    """Power-of-two key chunks of 64 to 1024 tokens."""
+    sides = [1 << e for e in range(11)]
+    return [(a, b, n // (a * b)) for n in (64, 128, 256, 512, 1024)
+            for a, b in itertools.product(sides, sides) if n % (a * b) == 0]
+
+
+def test_key_unit_offsets():
+    """Key blocks of 128 * m tokens are walked in units of 128 keys: the token
+    of slot 128u + 64h + 16w + 4i + r is the sum of the offsets of slots
+    128u, 64h, 16w + r and 4i (the kernel adds the first two on the scalar
+    side). Key blocks of 64 tokens use u = h = 0."""
+    shapes = key_chunk_shapes()
+    assert len(shapes) == 28 + 36 + 45 + 55 + 66  # C(k+2, 2) shapes of 2^k tokens
+    for ct, ch, cw in shapes:
+        n = ct * ch * cw
+        H, W = ch * 3, cw * 2
+        for u in range(max(1, n // 128)):
+            for h in range(2 if n >= 128 else 1):
+                for w in range(4):
+                    for i in range(4):
+                        for r in range(4):
+                            j = 128 * u + 64 * h + 16 * w + 4 * i + r
+                            parts = (slot(128 * u, ct, ch, cw, H, W) + slot(64 * h, ct, ch, cw, H, W)
+                                     + slot(16 * w + r, ct, ch, cw, H, W) + slot(4 * i, ct, ch, cw, H, W))
+                            assert slot(j, ct, ch, cw, H, W) == parts

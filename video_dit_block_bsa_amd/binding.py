@@ -35,17 +35,33 @@ class Problem(ctypes.Structure):
         ("cw", ctypes.c_int32),
         ("cond_frames", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("ctk", ctypes.c_int32),
+        ("chk", ctypes.c_int32),
+        ("cwk", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, T, H, W, heads, batch=1, head_dim=128, chunk=(4, 4, 8), cond_frames=0,
-             scale=0.0):
+             scale=0.0, key_chunk=None):
+        kc = tuple(key_chunk) if key_chunk else (0, 0, 0)
         return cls(batch, heads, head_dim, T, H, W, chunk[0], chunk[1], chunk[2], cond_frames,
-                   scale)
+                   scale, kc[0], kc[1], kc[2])
 
     @classmethod
     def from_workload(cls, w):
-        return cls.make(w.T, w.H, w.W, w.heads, w.batch, w.head_dim, w.chunk, w.cond_frames)
+        return cls.make(w.T, w.H, w.W, w.heads, w.batch, w.head_dim, w.chunk, w.cond_frames,
+                        key_chunk=w.key_chunk or None)
+
+    @property
+    def key_chunk(self):
+        if (self.ctk, self.chk, self.cwk) == (0, 0, 0):
+            return (self.ct, self.ch, self.cw)
+        return (self.ctk, self.chk, self.cwk)
+
+    @property
+    def num_key_blocks(self):
+        a, b, c = self.key_chunk
+        return (self.T // a) * (self.H // b) * (self.W // c)
 
     @property
     def seq_len(self):

@@ -56,6 +56,25 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
     return fail(BSA_ERR_INVALID_ARG, "cond_frames %d must be a multiple of ct=%d and < T=%d",
                 p->cond_frames, p->ct, p->T);
   if (!(p->scale == p->scale)) return fail(BSA_ERR_INVALID_ARG, "scale is NaN");
+  const bool own_key_chunk = p->ctk != 0 || p->chk != 0 || p->cwk != 0;
+  const int ctk = own_key_chunk ? p->ctk : p->ct;
+  const int chk = own_key_chunk ? p->chk : p->ch;
+  const int cwk = own_key_chunk ? p->cwk : p->cw;
+  if (own_key_chunk) {
+    if (ctk <= 0 || chk <= 0 || cwk <= 0)
+      return fail(BSA_ERR_INVALID_ARG, "key chunk extents must all be positive (or all 0)");
+    const long nk = (long)ctk * chk * cwk;
+    if (nk != 64 && nk != 128 && nk != 256 && nk != 512 && nk != 1024)
+      return fail(BSA_ERR_UNSUPPORTED,
+                  "key chunk %dx%dx%d: key blocks of 64, 128, 256, 512 or 1024 tokens are "
+                  "implemented", ctk, chk, cwk);
+    if (p->T % ctk || p->H % chk || p->W % cwk)
+      return fail(BSA_ERR_UNSUPPORTED, "grid %dx%dx%d is not divisible by key chunk %dx%dx%d",
+                  p->T, p->H, p->W, ctk, chk, cwk);
+    if (p->cond_frames % ctk)
+      return fail(BSA_ERR_INVALID_ARG, "cond_frames %d must be a multiple of ctk=%d",
+                  p->cond_frames, ctk);
+  }
   const long S = (long)p->T * p->H * p->W;
   // The attention kernel addresses one (batch, head) of K or V (S x 256 bytes)
   // through a buffer resource with a 32-bit size.
@@ -67,6 +86,12 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
   const long nhw = (long)(p->H / p->ch) * (p->W / p->cw);
   if ((unsigned long)nb * (unsigned long)nhw >= (1ul << 32))
     return fail(BSA_ERR_UNSUPPORTED, "block grid %ld x %ld is too large", nb, nhw);
+  {
+    const long nbk = S / ((long)ctk * chk * cwk);
+    const long nhwk = (long)(p->H / chk) * (p->W / cwk);
+    if ((unsigned long)nbk * (unsigned long)nhwk >= (1ul << 32))
+      return fail(BSA_ERR_UNSUPPORTED, "key block grid %ld x %ld is too large", nbk, nhwk);
+  }
   bsa::Geom& g = out->g;
   g.bh = (int)bh;
   g.S = (int)S;
@@ -81,6 +106,14 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
   g.nb = (int)(S / bsa::kBlockTokens);
   g.cond_blocks = (p->cond_frames / p->ct) * g.nH * g.nW;
   g.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
+  g.ctk = ctk;
+  g.chk = chk;
+  g.cwk = cwk;
+  g.nHk = p->H / chk;
+  g.nWk = p->W / cwk;
+  g.nk = ctk * chk * cwk;
+  g.nbk = (int)(S / g.nk);
+  g.cond_kblocks = (p->cond_frames / ctk) * g.nHk * g.nWk;
   out->empty = (bh == 0);
   return BSA_OK;
 }
@@ -107,11 +140,10 @@ struct SelectLayout {
 
 SelectLayout select_layout(const bsa::Geom& g) {
   SelectLayout L;
-  const size_t pooled = align_up((size_t)g.bh * g.nb * bsa::kHeadDim * sizeof(float));
   L.qp = 0;
-  L.kp = pooled;
-  L.s = 2 * pooled;
-  L.total = L.s + align_up((size_t)g.bh * g.nb * g.nb * sizeof(float));
+  L.kp = align_up((size_t)g.bh * g.nb * bsa::kHeadDim * sizeof(float));
+  L.s = L.kp + align_up((size_t)g.bh * g.nbk * bsa::kHeadDim * sizeof(float));
+  L.total = L.s + align_up((size_t)g.bh * g.nb * g.nbk * sizeof(float));
   return L;
 }
 
@@ -209,9 +241,9 @@ bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* param
   st = check_params(params);
   if (st != BSA_OK) return st;
   if (c.empty) return BSA_OK;
-  if (c.g.nb > kMaxBlocks)
-    return fail(BSA_ERR_UNSUPPORTED, "%d blocks per head: selection supports at most %d", c.g.nb,
-                kMaxBlocks);
+  if (c.g.nbk > kMaxBlocks)
+    return fail(BSA_ERR_UNSUPPORTED, "%d key blocks per head: selection supports at most %d",
+                c.g.nbk, kMaxBlocks);
   if (!q || !k || !idx || !cnt)
     return fail(BSA_ERR_INVALID_ARG, "q, k, idx and cnt must be non-NULL");
   if (!aligned16(q) || !aligned16(k)) return fail(BSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
@@ -226,9 +258,17 @@ bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* param
   float* qp = reinterpret_cast<float*>(ws + L.qp);
   float* kp = reinterpret_cast<float*>(ws + L.kp);
   float* sc = reinterpret_cast<float*>(ws + L.s);
-  st = launched(bsa::launch_pool(c.g, static_cast<const bsa::bf16_bits*>(q),
-                                 static_cast<const bsa::bf16_bits*>(k), qp, kp, s),
-                "pool");
+  if (c.g.nk == bsa::kBlockTokens && c.g.ctk == c.g.ct && c.g.chk == c.g.ch) {
+    st = launched(bsa::launch_pool(c.g, static_cast<const bsa::bf16_bits*>(q),
+                                   static_cast<const bsa::bf16_bits*>(k), qp, kp, s),
+                  "pool");
+  } else {
+    st = launched(bsa::launch_pool_queries(c.g, static_cast<const bsa::bf16_bits*>(q), qp, s),
+                  "pool");
+    if (st != BSA_OK) return st;
+    st = launched(bsa::launch_pool_keys(c.g, static_cast<const bsa::bf16_bits*>(k), kp, s),
+                  "pool");
+  }
   if (st != BSA_OK) return st;
   st = launched(bsa::launch_scores(c.g, qp, kp, sc, s), "scores");
   if (st != BSA_OK) return st;
@@ -272,6 +312,8 @@ bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const vo
   if (c.g.nb > kMaxBlocks)
     return fail(BSA_ERR_UNSUPPORTED, "%d blocks per head: the backward supports at most %d",
                 c.g.nb, kMaxBlocks);
+  if (c.g.ctk != c.g.ct || c.g.chk != c.g.ch || c.g.cwk != c.g.cw)
+    return fail(BSA_ERR_UNSUPPORTED, "the backward needs the key chunk to be the query chunk");
   const void* ins[6] = {q, k, v, o, dout, lse};
   void* outs[3] = {dq, dk, dv};
   for (const void* p : ins)

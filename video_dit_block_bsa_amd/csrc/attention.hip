@@ -78,7 +78,19 @@ constexpr int kSlots = 5;                               // half-tile ring per wo
 // With kLse the kernel also writes each query's softmax log-normaliser
 // (natural log, -inf for a query block with no key blocks), which the
 // backward pass uses to recompute the probabilities.
-template <bool kDense, bool kLse>
+//
+// Key blocks may be cut with their own chunk ("Implementation details and
+// design trade-offs": key blocks of 64 to 1024 tokens). The loop always
+// walks units of 128 keys, staged as two half tiles:
+//   kKeyMode 0: a key block is one unit (128 tokens);
+//   kKeyMode 1: a key block of 128 * 2^unit_shift tokens is that many units,
+//               unit u holding its slots 128u .. 128u+127;
+//   kKeyMode 2: key blocks of 64 tokens, two per unit (lower and upper half);
+//               when the count is odd the last unit's upper half repeats the
+//               lower one and its scores are set to -inf.
+// A unit's slot offsets are those of its first slot plus those of its slot
+// index (power-of-two chunk sides make the offset linear in the index bits).
+template <bool kDense, bool kLse, int kKeyMode>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const int32_t* __restrict__ idx,
@@ -142,10 +154,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   // it is (L%16) ^ 4r. So one lane offset k0 serves every load: load i of K
   // uses k0 ^ 64*sb(i), every load of V uses k0 ^ 80r, and the rest is scalar.
   const int r_lane = lane >> 4;
-  const uint32_t k0 = (uint32_t)slot_offset(g, 16 * w + r_lane) * (kHeadDim * 2) +
+  const uint32_t k0 = (uint32_t)key_slot_offset(g, 16 * w + r_lane) * (kHeadDim * 2) +
                       (uint32_t)(((lane & 15) ^ r_lane) << 4);
   const uint32_t vx = 80u * (uint32_t)r_lane;  // ((L%16) ^ 4r) ^ ((L%16) ^ r), in bytes
-  const uint32_t half_off = (uint32_t)slot_offset(g, kHalfRows) * (kHeadDim * 2);
+  const uint32_t half_off = (uint32_t)key_slot_offset(g, kHalfRows) * (kHeadDim * 2);
 
   int count;
   const int32_t* list = nullptr;
@@ -155,25 +167,59 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     list = idx + ((size_t)pair * g.nb + qb) * a.stride;
     count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
   }
-  // Next usable list position at or after `from` (ids outside [0, nb) are skipped).
+  // Next usable list position at or after `from` (ids outside [0, Nk) are skipped).
   auto next_valid = [&](int from) {
     if (kDense) return from;
     while (from < count) {
       const int kb = list[from];
-      if (kb >= 0 && kb < g.nb) break;
+      if (kb >= 0 && kb < g.nbk) break;
       ++from;
     }
     return from;
   };
   auto kb_at = [&](int pos) { return kDense ? pos : list[pos]; };
-  // Half tile e (0: K lo, 1: K hi, 2: V lo, 3: V hi) of key block kb into a slot.
-  auto load_half = [&](int kb, int e, bf16_bits* dst_slot) {
-    const uint32_t base = (uint32_t)block_origin(a, kb) * (kHeadDim * 2) + (e & 1) * half_off;
+  // Unit cursor: (position, unit within the key block) for kKeyMode 0 and 1,
+  // (position of the lower block, position of the upper block) for kKeyMode 2.
+  // The unit exists while .a < count.
+  struct Cursor {
+    int a, b;
+  };
+  auto first_unit = [&]() -> Cursor {
+    const int p = next_valid(0);
+    return {p, kKeyMode == 2 ? next_valid(p + 1) : 0};
+  };
+  auto next_unit = [&](Cursor c) -> Cursor {
+    if constexpr (kKeyMode == 1) {
+      if (c.b + 1 < (1 << a.unit_shift)) return {c.a, c.b + 1};
+      return {next_valid(c.a + 1), 0};
+    } else if constexpr (kKeyMode == 2) {
+      const int p = next_valid(c.b + 1);
+      return {p, next_valid(p + 1)};
+    } else {
+      return {next_valid(c.a + 1), 0};
+    }
+  };
+  // Byte offset of the first slot of half h (0: keys 0..63, 1: keys 64..127)
+  // of a unit.
+  auto unit_base = [&](Cursor c, int h) -> uint32_t {
+    if constexpr (kKeyMode == 2) {
+      const int p = (h != 0 && c.b < count) ? c.b : c.a;
+      return (uint32_t)key_block_origin(a, list[p]) * (kHeadDim * 2);
+    } else if constexpr (kKeyMode == 1) {
+      return (uint32_t)(key_block_origin(a, list[c.a]) + key_slot_offset(g, c.b * kBlockTokens)) *
+                 (kHeadDim * 2) + h * half_off;
+    } else {
+      return (uint32_t)key_block_origin(a, kb_at(c.a)) * (kHeadDim * 2) + h * half_off;
+    }
+  };
+  // Half tile e (0: K lo, 1: K hi, 2: V lo, 3: V hi) of a unit into a slot.
+  auto load_half = [&](Cursor c, int e, bf16_bits* dst_slot) {
+    const uint32_t base = unit_base(c, e & 1);
     char* dst = reinterpret_cast<char*>(dst_slot) + 16 * w * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       constexpr uint32_t sb64[4] = {0, 128, 64, 192};  // 64 * (i with its two bits swapped)
-      const uint32_t row_s = (uint32_t)slot_offset(g, 4 * i) * (kHeadDim * 2);
+      const uint32_t row_s = (uint32_t)key_slot_offset(g, 4 * i) * (kHeadDim * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(e < 2 ? krs : vrs, (lds_void*)(dst + i * 1024), 16,
                                                e < 2 ? (k0 ^ sb64[i]) : (k0 ^ vx), base + row_s, 0, 0);
     }
@@ -203,15 +249,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     va0 = (8 * gs + q) * 256 + 64 * q + 16 * c0 + 8 * (jj & 1);
   }
 
-  // Block positions: cur (the block of the current phase) and nxt (the one
-  // after it, or count).
-  int cur = next_valid(0);
-  if (cur < count) {
-    int nxt = next_valid(cur + 1);
+  // Units: cur (the unit of the current phase) and nxt (the one after it,
+  // with nxt.a == count past the last).
+  Cursor cur = first_unit();
+  if (cur.a < count) {
+    Cursor nxt = next_unit(cur);
     // Half tiles 0, 1, 2 (K_0 lo, K_0 hi, V_0 lo) into slots 0, 1, 2.
-    load_half(kb_at(cur), 0, slot0);
-    load_half(kb_at(cur), 1, slot1);
-    load_half(kb_at(cur), 2, slot2);
+    load_half(cur, 0, slot0);
+    load_half(cur, 1, slot1);
+    load_half(cur, 2, slot2);
     bf16x8 pf[8];
 
     // Phase with index pm = p mod 10 (its slots are fixed at compile time).
@@ -230,13 +276,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
       // Refill the slots of the previous phase with half tiles 2p+3, 2p+4:
       // V_j hi and K_{j+1} lo in an S phase, K_{j+1} hi and V_{j+1} lo in a
       // P V phase.
-      const int kb_next = kb_at(nxt < count ? nxt : cur);
+      const Cursor un = nxt.a < count ? nxt : cur;
       if constexpr (is_s) {
-        load_half(kb_at(cur), 3, slot_ptr(std::integral_constant<int, sc>{}));
-        load_half(kb_next, 0, slot_ptr(std::integral_constant<int, sd>{}));
+        load_half(cur, 3, slot_ptr(std::integral_constant<int, sc>{}));
+        load_half(un, 0, slot_ptr(std::integral_constant<int, sd>{}));
       } else {
-        load_half(kb_next, 1, slot_ptr(std::integral_constant<int, sc>{}));
-        load_half(kb_next, 2, slot_ptr(std::integral_constant<int, sd>{}));
+        load_half(un, 1, slot_ptr(std::integral_constant<int, sc>{}));
+        load_half(un, 2, slot_ptr(std::integral_constant<int, sd>{}));
       }
       const char* lo = reinterpret_cast<const char*>(slot_ptr(std::integral_constant<int, sa>{}));
       const char* hi = reinterpret_cast<const char*>(slot_ptr(std::integral_constant<int, sb>{}));
@@ -255,6 +301,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
             const bf16x8 af =
                 *reinterpret_cast<const bf16x8*>(kt + 32 * (tt & 1) * 256 + (ka0 ^ (32 * s)));
             sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[tt], 0, 0, 0);
+          }
+        }
+        if constexpr (kKeyMode == 2) {
+          // A lone last 64-token key block: its unit has no upper half.
+          if (cur.b >= count) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[2][i] = sacc[3][i] = -INFINITY;
           }
         }
         // Online softmax for this lane's query (both lane halves agree on m2).
@@ -313,9 +366,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
         };
         pv_half(lo, 0);
         pv_half(hi, 4);
-        if (nxt >= count) return false;
+        if (nxt.a >= count) return false;
         cur = nxt;
-        nxt = next_valid(cur + 1);
+        nxt = next_unit(cur);
         return true;
       }
     };
@@ -357,17 +410,38 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
                             const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
                             int stride, bool dense, bf16_bits* o, float* lse,
                             hipStream_t stream) {
-  const AttnArgs a = make_attn_args(g, stride);
-  dim3 grid((unsigned)((size_t)g.bh * a.nq8));
-  if (dense)
-    hipLaunchKernelGGL((attn_kernel<true, false>), grid, dim3(kThreads), 0, stream, a, q, k, v, idx,
-                       cnt, o, nullptr);
-  else if (lse)
-    hipLaunchKernelGGL((attn_kernel<false, true>), grid, dim3(kThreads), 0, stream, a, q, k, v, idx,
-                       cnt, o, lse);
-  else
-    hipLaunchKernelGGL((attn_kernel<false, false>), grid, dim3(kThreads), 0, stream, a, q, k, v,
+  dim3 grid((unsigned)((size_t)g.bh * ((g.nb + 7) / 8 * 8)));
+  if (dense) {
+    // Dense attention walks all allowed keys in blocks of the query chunk.
+    Geom gd = g;
+    gd.ctk = g.ct;
+    gd.chk = g.ch;
+    gd.cwk = g.cw;
+    gd.nHk = g.nH;
+    gd.nWk = g.nW;
+    gd.nbk = g.nb;
+    gd.nk = kBlockTokens;
+    gd.cond_kblocks = g.cond_blocks;
+    const AttnArgs a = make_attn_args(gd, 1);
+    hipLaunchKernelGGL((attn_kernel<true, false, 0>), grid, dim3(kThreads), 0, stream, a, q, k, v,
                        idx, cnt, o, nullptr);
+    return hipGetLastError();
+  }
+  const AttnArgs a = make_attn_args(g, stride);
+  const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
+#define BSA_LAUNCH_ATTN(LSE, MODE)                                                             \
+  hipLaunchKernelGGL((attn_kernel<false, LSE, MODE>), grid, dim3(kThreads), 0, stream, a, q, k, v, \
+                     idx, cnt, o, lse)
+  if (lse) {
+    if (mode == 0) BSA_LAUNCH_ATTN(true, 0);
+    else if (mode == 1) BSA_LAUNCH_ATTN(true, 1);
+    else BSA_LAUNCH_ATTN(true, 2);
+  } else {
+    if (mode == 0) BSA_LAUNCH_ATTN(false, 0);
+    else if (mode == 1) BSA_LAUNCH_ATTN(false, 1);
+    else BSA_LAUNCH_ATTN(false, 2);
+  }
+#undef BSA_LAUNCH_ATTN
   return hipGetLastError();
 }
 

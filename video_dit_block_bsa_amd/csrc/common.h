@@ -26,8 +26,15 @@ struct Geom {
   int ct, ch, cw;   // chunk shape
   int nH, nW;       // blocks along h and w
   int nb;           // blocks per (batch, head)
-  int cond_blocks;  // leading condition key blocks (0 = no block-causal mask)
+  int cond_blocks;  // leading condition query blocks (0 = no block-causal mask)
   float scale;      // softmax scale
+  // Key blocks: the grid cut with the key chunk (the query chunk unless the
+  // problem gives a separate one).
+  int ctk, chk, cwk;
+  int nHk, nWk;
+  int nbk;           // key blocks per (batch, head)
+  int nk;            // tokens per key block
+  int cond_kblocks;  // leading condition key blocks
 };
 
 // Latent-order token of slot j (0..127) of block i: blocks run in
@@ -44,7 +51,27 @@ __device__ __forceinline__ int block_token(const Geom& g, int i, int j) {
   return ((bt * g.ct + it) * g.H + bh * g.ch + ih) * g.W + bw * g.cw + iw;
 }
 
-// Number of leading key blocks query block i may see.
+// Latent-order token of slot j (0 .. nk-1) of key block i.
+__device__ __forceinline__ int key_block_token(const Geom& g, int i, int j) {
+  const int bw = i % g.nWk;
+  const int rest = i / g.nWk;
+  const int bh = rest % g.nHk;
+  const int bt = rest / g.nHk;
+  const int iw = j % g.cwk;
+  const int r2 = j / g.cwk;
+  const int ih = r2 % g.chk;
+  const int it = r2 / g.chk;
+  return ((bt * g.ctk + it) * g.H + bh * g.chk + ih) * g.W + bw * g.cwk + iw;
+}
+
+// Number of leading key blocks query block i may select (block-causal:
+// condition query blocks see the condition key blocks only).
+__device__ __forceinline__ int allowed_key_blocks(const Geom& g, int i) {
+  return (g.cond_blocks > 0 && i < g.cond_blocks) ? g.cond_kblocks : g.nbk;
+}
+
+// The same count in query-chunk blocks (the dense kernel walks all allowed
+// keys in blocks of the query chunk).
 __device__ __forceinline__ int allowed_blocks(const Geom& g, int i) {
   return (g.cond_blocks > 0 && i < g.cond_blocks) ? g.cond_blocks : g.nb;
 }
@@ -56,6 +83,8 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_pool(const Geom& g, const bf16_bits* q, const bf16_bits* k, float* qp,
                        float* kp, hipStream_t stream);
+hipError_t launch_pool_keys(const Geom& g, const bf16_bits* k, float* kp, hipStream_t stream);
+hipError_t launch_pool_queries(const Geom& g, const bf16_bits* q, float* qp, hipStream_t stream);
 hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float* s,
                          hipStream_t stream);
 hipError_t launch_select(const Geom& g, const float* s, int mode, int k, float p, int k_min,

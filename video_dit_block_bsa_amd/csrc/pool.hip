@@ -1,7 +1,8 @@
 // Block mean-pooling of Q and K ("Pooled block similarity computation" of the
 // LongCat-Video deep dive, section "Block Sparse Attention"): the pooled
-// vector of block b is the mean of the 128 tokens of b, each block being a
-// ct x ch x cw box of the latent grid.
+// vector of block b is the mean of the tokens of b, each block being a
+// ct x ch x cw box of the latent grid (keys use the key chunk when it
+// differs: "Implementation details and design trade-offs").
 //
 // One workgroup per (batch*head, block). Thread t reads channel chunk
 // t % 16 (8 bf16 = 16 bytes) of tokens 8*(t/16) .. 8*(t/16)+7 of the block,
@@ -61,6 +62,63 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Geom g, const bf16_bits*
   for (int r = 0; r < 16; ++r) s += part[which][r][c];
   float* dst = (which == 0 ? qp : kp);
   dst[((size_t)bh * g.nb + blk) * kHeadDim + c] = s * (1.0f / kBlockTokens);
+}
+
+// Pooling of one tensor when the key chunk differs from the query chunk:
+// blocks of n = 64 .. 1024 tokens (query blocks, or key blocks with kKeys).
+// Thread t adds channel chunk t % 16 of the n/16 consecutive slots
+// (t/16)*n/16 ..; the 16 partial sums meet in LDS in a fixed order, as above.
+template <bool kKeys>
+__global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, const bf16_bits* __restrict__ x,
+                                                            float* __restrict__ xp) {
+  __shared__ float part[16][kHeadDim + 4];
+  const int blk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int chunk = t & 15;
+  const int grp = t >> 4;
+  const int n = kKeys ? g.nk : kBlockTokens;
+  const int per = n >> 4;  // a multiple of 4
+  const size_t head_off = (size_t)bh * g.S * kHeadDim;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r0 = 0; r0 < per; r0 += 4) {
+    u32x4 raw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = grp * per + r0 + r;
+      const int tok = kKeys ? key_block_token(g, blk, j) : block_token(g, blk, j);
+      raw[r] = *reinterpret_cast<const u32x4*>(x + head_off + (size_t)tok * kHeadDim + chunk * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_to_f32(raw[r][e] & 0xffffu);
+        acc[2 * e + 1] += bf16_to_f32(raw[r][e] >> 16);
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[grp][chunk * 8 + e] = acc[e];
+  __syncthreads();
+  if (t < kHeadDim) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += part[r][t];
+    const int nblocks = kKeys ? g.nbk : g.nb;
+    xp[((size_t)bh * nblocks + blk) * kHeadDim + t] = sum * (1.0f / (float)n);
+  }
+}
+
+hipError_t launch_pool_queries(const Geom& g, const bf16_bits* q, float* qp, hipStream_t stream) {
+  hipLaunchKernelGGL(pool_one_kernel<false>, dim3(g.nb, g.bh), dim3(kThreads), 0, stream, g, q, qp);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_keys(const Geom& g, const bf16_bits* k, float* kp, hipStream_t stream) {
+  hipLaunchKernelGGL(pool_one_kernel<true>, dim3(g.nbk, g.bh), dim3(kThreads), 0, stream, g, k, kp);
+  return hipGetLastError();
 }
 
 hipError_t launch_pool(const Geom& g, const bf16_bits* q, const bf16_bits* k, float* qp,

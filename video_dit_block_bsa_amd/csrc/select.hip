@@ -3,7 +3,8 @@
 // and design trade-offs", LongCat-Video deep dive, section "Block Sparse
 // Attention"; combined top-k/CDF clamps from the zhaifeiyue notes, section 3).
 //
-// scores_kernel: S = (Q_pool K_pool^T) * scale per (batch, head), fp32. A
+// scores_kernel: S = (Q_pool K_pool^T) * scale per (batch, head), fp32,
+//   Nb query blocks x Nk key blocks. A
 //   64 x 64 output tile per workgroup, both operand tiles staged in LDS, fp32
 //   MFMA 32x32x2 with a fixed summation order over the 128 channels.
 // select_kernel: one wave64 per query-block row. The row's scores live in
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(Geom g, const float* _
   const int j0 = blockIdx.x * kScoreTile;
   const int t = threadIdx.x;
   const float* qb = qp + (size_t)bh * g.nb * kHeadDim;
-  const float* kb = kp + (size_t)bh * g.nb * kHeadDim;
+  const float* kb = kp + (size_t)bh * g.nbk * kHeadDim;
 
   // Stage both 64 x 128 operand tiles row-major; rows past nb are zero.
 #pragma unroll
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(Geom g, const float* _
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i0 + row < g.nb) a = *reinterpret_cast<const float4*>(qb + (size_t)(i0 + row) * kHeadDim + d4 * 4);
-    if (j0 + row < g.nb) b = *reinterpret_cast<const float4*>(kb + (size_t)(j0 + row) * kHeadDim + d4 * 4);
+    if (j0 + row < g.nbk) b = *reinterpret_cast<const float4*>(kb + (size_t)(j0 + row) * kHeadDim + d4 * 4);
     *reinterpret_cast<float4*>(&qs[row][d4 * 4]) = a;
     *reinterpret_cast<float4*>(&ks[row][d4 * 4]) = b;
   }
@@ -73,11 +74,11 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(Geom g, const float* _
   }
   // Accumulator value v holds row 8(v/4) + 4h + v%4, column m of the sub-tile.
   const int j = j0 + 32 * wc + m;
-  if (j < g.nb) {
+  if (j < g.nbk) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int i = i0 + 32 * wr + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (i < g.nb) s[((size_t)bh * g.nb + i) * g.nb + j] = acc[v] * g.scale;
+      if (i < g.nb) s[((size_t)bh * g.nb + i) * g.nbk + j] = acc[v] * g.scale;
     }
   }
 }
@@ -111,8 +112,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Geom g, const float* _
   const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= g.bh * g.nb) return;  // whole wave leaves together
   const int i = row % g.nb;
-  const int na = allowed_blocks(g, i);
-  const float* srow = s + (size_t)row * g.nb;
+  const int na = allowed_key_blocks(g, i);
+  const float* srow = s + (size_t)row * g.nbk;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   uint32_t key[R];
@@ -219,8 +220,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Geom g, const float* _
 
 hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float* s,
                          hipStream_t stream) {
-  const int tiles = (g.nb + kScoreTile - 1) / kScoreTile;
-  dim3 grid(tiles, tiles, g.bh);
+  dim3 grid((g.nbk + kScoreTile - 1) / kScoreTile, (g.nb + kScoreTile - 1) / kScoreTile, g.bh);
   hipLaunchKernelGGL(scores_kernel, grid, dim3(kThreads), 0, stream, g, qp, kp, s);
   return hipGetLastError();
 }
@@ -240,7 +240,7 @@ static hipError_t launch_select_r(const Geom& g, const float* s, int mode, int k
 hipError_t launch_select(const Geom& g, const float* s, int mode, int k, float p, int k_min,
                          int k_max, int stride, int32_t* idx, int32_t* cnt,
                          hipStream_t stream) {
-  const int chunks = (g.nb + 63) / 64;
+  const int chunks = (g.nbk + 63) / 64;
   if (chunks <= 1) return launch_select_r<1>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
   if (chunks <= 2) return launch_select_r<2>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
   if (chunks <= 4) return launch_select_r<4>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);

@@ -18,10 +18,13 @@ __device__ __forceinline__ int swap23(int m) {
 struct AttnArgs {
   Geom g;
   int stride;
-  int nq8;           // query blocks per head rounded up to a multiple of 8
-  uint32_t mag_nw;   // floor(2^32 / nW) + 1
-  uint32_t mag_nhw;  // floor(2^32 / (nH*nW)) + 1
-  float c_log2;      // scale * log2(e)
+  int nq8;            // query blocks per head rounded up to a multiple of 8
+  uint32_t mag_nw;    // floor(2^32 / nW) + 1
+  uint32_t mag_nhw;   // floor(2^32 / (nH*nW)) + 1
+  uint32_t mag_nwk;   // the same for the key-block grid
+  uint32_t mag_nhwk;
+  int unit_shift;     // log2 of the 128-key units per key block (key blocks of 256+ tokens)
+  float c_log2;       // scale * log2(e)
 };
 
 // Latent-order token of the first slot of block i.
@@ -39,6 +42,22 @@ __device__ __forceinline__ int slot_offset(const Geom& g, int j) {
   const int iw = j % g.cw;
   const int r2 = j / g.cw;
   return ((r2 / g.ch) * g.H + r2 % g.ch) * g.W + iw;
+}
+
+// The same two for key blocks (key chunk and key-block grid).
+__device__ __forceinline__ int key_block_origin(const AttnArgs& a, int i) {
+  const Geom& g = a.g;
+  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhwk);
+  const int rem = i - bt * g.nHk * g.nWk;
+  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nwk);
+  const int bw = rem - bh * g.nWk;
+  return ((bt * g.ctk) * g.H + bh * g.chk) * g.W + bw * g.cwk;
+}
+
+__device__ __forceinline__ int key_slot_offset(const Geom& g, int j) {
+  const int iw = j % g.cwk;
+  const int r2 = j / g.cwk;
+  return ((r2 / g.chk) * g.H + r2 % g.chk) * g.W + iw;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -66,6 +85,10 @@ inline AttnArgs make_attn_args(const Geom& g, int stride) {
   a.nq8 = (g.nb + 7) / 8 * 8;
   a.mag_nw = (uint32_t)(0x100000000ull / (uint64_t)g.nW + 1);
   a.mag_nhw = (uint32_t)(0x100000000ull / (uint64_t)(g.nH * g.nW) + 1);
+  a.mag_nwk = (uint32_t)(0x100000000ull / (uint64_t)g.nWk + 1);
+  a.mag_nhwk = (uint32_t)(0x100000000ull / (uint64_t)(g.nHk * g.nWk) + 1);
+  a.unit_shift = 0;
+  for (int m = g.nk / 128; m > 1; m >>= 1) ++a.unit_shift;
   a.c_log2 = g.scale * 1.4426950408889634f;
   return a;
 }

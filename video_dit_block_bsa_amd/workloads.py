@@ -30,6 +30,7 @@ class Workload:
     k_max: int = 64
     cond_frames: int = 0
     chunk: tuple = (4, 4, 8)
+    key_chunk: tuple = ()  # empty: the same as chunk
     note: str = field(default="", compare=False)
 
     @property
@@ -45,6 +46,20 @@ class Workload:
     def block_tokens(self) -> int:
         ct, ch, cw = self.chunk
         return ct * ch * cw
+
+    @property
+    def kchunk(self) -> tuple:
+        return tuple(self.key_chunk) if self.key_chunk else tuple(self.chunk)
+
+    @property
+    def key_block_tokens(self) -> int:
+        a, b, c = self.kchunk
+        return a * b * c
+
+    @property
+    def num_key_blocks(self) -> int:
+        a, b, c = self.kchunk
+        return (self.T // a) * (self.H // b) * (self.W // c)
 
     @property
     def stride(self) -> int:
@@ -63,11 +78,15 @@ WORKLOADS = {
     "vc": Workload("vc", 16, 48, 80, heads=32, seed=4, mode="cdf", p=0.90,
                    k_min=4, k_max=64, cond_frames=4,
                    note="61,440 tokens, 4 condition frames, CDF 0.90 in [4, 64]"),
+    # Decoupled key blocks on the 215K grid at the refinement ratio r = N_k/16.
+    "long_k64": Workload("long_k64", 56, 48, 80, heads=32, seed=3, k=210, key_chunk=(2, 4, 8),
+                         note="215,040 tokens, 128-token query blocks, 3,360 key blocks of 64"),
+    "long_k256": Workload("long_k256", 56, 48, 80, heads=32, seed=3, k=52, key_chunk=(4, 8, 8),
+                          note="215,040 tokens, 128-token query blocks, 840 key blocks of 256"),
 }
 
 
 def effective_flops(w: Workload, total_kept_blocks: int) -> float:
     """4 * n_q * kept_keys * d summed over heads: two matmuls of 2 flop/MAC,
     counted only over kept (query block, key block) pairs."""
-    n = w.block_tokens
-    return 4.0 * n * n * w.head_dim * float(total_kept_blocks)
+    return 4.0 * w.block_tokens * w.key_block_tokens * w.head_dim * float(total_kept_blocks)
