@@ -163,6 +163,51 @@ def backward_bench(w, problem, qd, kd, vd, idx, cnt, stride, ws_att, stream, eff
     }
 
 
+def cond_cache_bench(w, problem, params, qd, kd, vd, stride, full_ms, steps):
+    """One denoising step with the condition-KV cache: bsa_select_noisy +
+    bsa_attention_noisy over the noisy query blocks, condition pooled keys
+    from a cache filled once (untimed), against the full step above."""
+    import numpy as np
+    import torch
+
+    from video_dit_block_bsa_amd import binding as B
+
+    rows = w.batch * w.heads * w.num_blocks
+    idx = torch.empty((rows, stride), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((rows,), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(qd)
+    ws = torch.empty(B.select_workspace_bytes(problem, params), dtype=torch.uint8, device="cuda")
+    cache = torch.empty(B.cond_cache_bytes(problem) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    B.bsa_pool_cond_keys(problem, kd, cache, stream)
+
+    def one():
+        B.bsa_select_noisy(problem, params, qd, kd, cache, idx, cnt, ws, stream)
+        B.bsa_attention_noisy(problem, qd, kd, vd, idx, cnt, stride, o, ws, stream)
+
+    one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    cond_blocks = (w.cond_frames // w.chunk[0]) * (w.H // w.chunk[1]) * (w.W // w.chunk[2])
+    log(f"[bench] condition-KV cache step: {ms:.3f} ms (full step {full_ms:.3f} ms)")
+    del idx, cnt, o, ws, cache
+    return {
+        "entry_points": "bsa_select_noisy + bsa_attention_noisy (bsa_pool_cond_keys once)",
+        "steps": steps,
+        "noisy_step_ms": round(ms, 4),
+        "full_step_ms": round(full_ms, 4),
+        "speedup": round(full_ms / ms, 3),
+        "noisy_query_blocks": w.num_blocks - cond_blocks,
+        "query_blocks": w.num_blocks,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +222,9 @@ def main():
                     help="stop the CPU oracle sample after this much attention time")
     ap.add_argument("--backward-steps", type=int, default=5,
                     help="timed training forward (with lse) + backward passes (0 = skip)")
+    ap.add_argument("--cond-cache-steps", type=int, default=5,
+                    help="timed steps of the condition-KV cache path (noisy query blocks only; "
+                         "workloads with condition frames; 0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first, so that "
                          "hardware byte counters can be calibrated against a known size")
@@ -270,6 +318,11 @@ def main():
         log(f"[bench] dense_attention: {dense_ms:.2f} ms")
         del od
 
+    cache_rec = None
+    if args.cond_cache_steps > 0 and w.cond_frames > 0:
+        cache_rec = cond_cache_bench(w, problem, params, qd, kd, vd, stride, ms_per_step,
+                                     args.cond_cache_steps)
+
     bwd = None
     if args.backward_steps > 0 and not w.key_chunk:
         bwd = backward_bench(w, problem, qd, kd, vd, idx, cnt, stride, ws_att, stream, eff,
@@ -279,7 +332,7 @@ def main():
     traffic = traffic_for(w.name)
     roofline = {
         "bound": "mfma",
-        "kernel": "bsa_attention (block-sparse flash attention, attn_kernel<false>)",
+        "kernel": "bsa_attention (block-sparse flash attention, attn_kernel<false, false, KeyMode>)",
         "achieved": round(att_tflops, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
@@ -334,6 +387,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "backward": bwd,
+        "cond_cache": cache_rec,
     }
     print(json.dumps(result), flush=True)
 

@@ -202,6 +202,46 @@ bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const vo
                              void* dk, void* dv, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Condition-KV cache for multi-step inference. Condition frames are fixed
+ * over all denoising steps, so their keys and values are computed once and
+ * cached, and X_cond (condition queries over condition keys) does not change;
+ * each later step recomputes only X_noisy = Attention(Q_noisy, [K_cond,
+ * K_noisy], [V_cond, V_noisy]) (deep dive, section "Block Attention with
+ * KV-Cache for Efficient Multi-Task Inference", "Why this is efficient").
+ * The three calls below serve those steps: the caller keeps K_cond/V_cond in
+ * the leading (condition) rows of k and v, writes each step's noisy rows
+ * after them, and calls bsa_select_noisy + bsa_attention_noisy, which read
+ * and write noisy query rows only.
+ *
+ * Bytes of the pooled condition-key cache: 4*128 per condition key block per
+ * (batch, head) (0 when cond_frames is 0 or on invalid arguments). */
+size_t bsa_cond_cache_bytes(const bsa_problem* problem);
+
+/* Pools the condition key blocks of k into `cache` (fp32 [batch, heads,
+ * condition key blocks, 128]); once per sequence, when K_cond is known. The
+ * values equal the condition rows bsa_select pools for itself. */
+bsa_status bsa_pool_cond_keys(const bsa_problem* problem, const void* k, float* cache,
+                              size_t cache_bytes, void* stream);
+
+/* bsa_select for the noisy query blocks only: idx and cnt rows of condition
+ * query blocks are not written. Pooled keys of the condition key blocks come
+ * from `cache` (bsa_pool_cond_keys); those of the noisy key blocks and the
+ * pooled noisy queries are computed from k and q. Noisy rows are
+ * bit-identical to bsa_select's for the same q and k. Workspace as for
+ * bsa_select. With cond_frames = 0 it is bsa_select (cache may be NULL). */
+bsa_status bsa_select_noisy(const bsa_problem* problem, const bsa_select_params* params,
+                            const void* q, const void* k, const float* cache, size_t cache_bytes,
+                            int32_t* idx, int32_t* cnt, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* bsa_attention for the noisy query blocks only: o rows of condition tokens
+ * are not written (they keep the X_cond of an earlier step). Noisy rows are
+ * bit-identical to bsa_attention's. */
+bsa_status bsa_attention_noisy(const bsa_problem* problem, const void* q, const void* k,
+                               const void* v, const int32_t* idx, const int32_t* cnt,
+                               int32_t idx_stride, void* o, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* bsa_status_string(int32_t status);
 

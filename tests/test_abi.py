@@ -252,3 +252,26 @@ def test_key_chunk_checks():
     assert _select(_problem(T=4 * 100, key_chunk=(2, 4, 8)), sp) == UNSUPPORTED  # 24,000 key blocks
     assert _bwd(_problem(key_chunk=(4, 8, 8))) == UNSUPPORTED
     assert B.attention_bwd_workspace_bytes(_problem(key_chunk=(4, 8, 8))) > 0
+
+
+def test_cond_cache_checks():
+    p = _problem(T=16, cond_frames=4)   # 16 x 48 x 80: 480 blocks, 120 condition blocks
+    assert B.cond_cache_bytes(p) == 32 * 120 * 128 * 4
+    assert B.cond_cache_bytes(_problem(T=16)) == 0
+    assert B.cond_cache_bytes(_problem(T=16, cond_frames=4, key_chunk=(4, 8, 8))) == 32 * 60 * 512
+    lib = B.lib()
+    sp = B.SelectParams.topk(4)
+
+    def sel(cache, cache_bytes, ws_bytes=1 << 40):
+        return lib.bsa_select_noisy(ctypes.byref(p), ctypes.byref(sp), GiB4, GiB4 * 2, cache,
+                                    cache_bytes, GiB4 * 3, GiB4 * 4, GiB4 * 5, ws_bytes, None)
+
+    assert sel(None, 0) == INVALID                         # condition rows need the cache
+    assert sel(GiB4 * 6, 1024) == WORKSPACE                # cache too small
+    assert sel(GiB4 * 6 + 8, 1 << 30) == INVALID           # misaligned
+    assert sel(GiB4 * 6, 1 << 30, ws_bytes=16) == WORKSPACE
+    assert lib.bsa_pool_cond_keys(ctypes.byref(p), GiB4, None, 0, None) == INVALID
+    assert lib.bsa_pool_cond_keys(ctypes.byref(p), GiB4, GiB4 * 2, 64, None) == WORKSPACE
+    q0 = _problem(heads=0, cond_frames=4)
+    assert lib.bsa_attention_noisy(ctypes.byref(q0), None, None, None, None, None, 4, None, None,
+                                   0, None) == OK

@@ -27,6 +27,10 @@ def __getattr__(name):
         "bsa_attention_lse",
         "bsa_attention_bwd",
         "attention_bwd_workspace_bytes",
+        "cond_cache_bytes",
+        "bsa_pool_cond_keys",
+        "bsa_select_noisy",
+        "bsa_attention_noisy",
     }:
         from . import binding
 

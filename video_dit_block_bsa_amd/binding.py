@@ -137,6 +137,16 @@ def lib():
         L.bsa_attention_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, i32p, ctypes.c_int32,
                                         vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.bsa_attention_bwd.restype = ctypes.c_int32
+        L.bsa_cond_cache_bytes.argtypes = [P]
+        L.bsa_cond_cache_bytes.restype = ctypes.c_size_t
+        L.bsa_pool_cond_keys.argtypes = [P, vp, vp, ctypes.c_size_t, vp]
+        L.bsa_pool_cond_keys.restype = ctypes.c_int32
+        L.bsa_select_noisy.argtypes = [P, SP, vp, vp, vp, ctypes.c_size_t, i32p, i32p, vp,
+                                       ctypes.c_size_t, vp]
+        L.bsa_select_noisy.restype = ctypes.c_int32
+        L.bsa_attention_noisy.argtypes = [P, vp, vp, vp, i32p, i32p, ctypes.c_int32, vp, vp,
+                                          ctypes.c_size_t, vp]
+        L.bsa_attention_noisy.restype = ctypes.c_int32
         L.bsa_status_string.argtypes = [ctypes.c_int32]
         L.bsa_status_string.restype = ctypes.c_char_p
         L.bsa_last_error.argtypes = []
@@ -235,3 +245,32 @@ def bsa_attention_bwd(problem, q, k, v, o, dout, lse, idx, cnt, idx_stride, dq, 
                                    _ptr(dout), _ptr(lse), _ptr(idx), _ptr(cnt), int(idx_stride),
                                    _ptr(dq), _ptr(dk), _ptr(dv), ws_ptr, _nbytes(workspace),
                                    _stream(stream)))
+
+
+def cond_cache_bytes(problem: Problem) -> int:
+    return lib().bsa_cond_cache_bytes(ctypes.byref(problem))
+
+
+def bsa_pool_cond_keys(problem, k, cache, stream=None):
+    """bsa_pool_cond_keys: pooled condition keys -> cache (tensor or (ptr, nbytes))."""
+    cache_ptr = cache[0] if isinstance(cache, tuple) else _ptr(cache)
+    _check(lib().bsa_pool_cond_keys(ctypes.byref(problem), _ptr(k), cache_ptr, _nbytes(cache),
+                                    _stream(stream)))
+
+
+def bsa_select_noisy(problem, params, q, k, cache, idx, cnt, workspace, stream=None):
+    """bsa_select_noisy: selection for the noisy query blocks, condition
+    pooled keys from the cache."""
+    ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
+    cache_ptr = cache[0] if isinstance(cache, tuple) else _ptr(cache)
+    _check(lib().bsa_select_noisy(ctypes.byref(problem), ctypes.byref(params), _ptr(q), _ptr(k),
+                                  cache_ptr, _nbytes(cache), _ptr(idx), _ptr(cnt), ws_ptr,
+                                  _nbytes(workspace), _stream(stream)))
+
+
+def bsa_attention_noisy(problem, q, k, v, idx, cnt, idx_stride, o, workspace, stream=None):
+    """bsa_attention_noisy: attention for the noisy query blocks -> o."""
+    ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
+    _check(lib().bsa_attention_noisy(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                     _ptr(cnt), int(idx_stride), _ptr(o), ws_ptr,
+                                     _nbytes(workspace), _stream(stream)))

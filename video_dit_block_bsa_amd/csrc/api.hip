@@ -158,7 +158,8 @@ bsa_status launched(hipError_t e, const char* what) {
 bsa_status attention_common(const bsa_problem* problem, const void* q, const void* k,
                             const void* v, const int32_t* idx, const int32_t* cnt,
                             int32_t idx_stride, void* o, float* lse, void* workspace,
-                            size_t workspace_bytes, void* stream, bool dense) {
+                            size_t workspace_bytes, void* stream, bool dense,
+                            bool noisy_only = false) {
   Checked c;
   bsa_status st = check_problem(problem, &c);
   if (st != BSA_OK) return st;
@@ -185,8 +186,76 @@ bsa_status attention_common(const bsa_problem* problem, const void* q, const voi
                                         static_cast<const bsa::bf16_bits*>(k),
                                         static_cast<const bsa::bf16_bits*>(v), idx, cnt,
                                         dense ? 1 : idx_stride, dense,
-                                        static_cast<bsa::bf16_bits*>(o), lse, s),
+                                        static_cast<bsa::bf16_bits*>(o), lse,
+                                        noisy_only ? c.g.cond_blocks : 0, s),
                   "attention");
+}
+
+size_t cond_cache_bytes(const bsa::Geom& g) {
+  return (size_t)g.bh * g.cond_kblocks * bsa::kHeadDim * sizeof(float);
+}
+
+// Selection for all query blocks, or (noisy) for the noisy ones only, with
+// the condition key blocks' pooled keys taken from `cache`.
+bsa_status select_common(const bsa_problem* problem, const bsa_select_params* params,
+                         const void* q, const void* k, const float* cache, size_t cache_bytes,
+                         int32_t* idx, int32_t* cnt, void* workspace, size_t workspace_bytes,
+                         void* stream, bool noisy) {
+  Checked c;
+  bsa_status st = check_problem(problem, &c);
+  if (st != BSA_OK) return st;
+  st = check_params(params);
+  if (st != BSA_OK) return st;
+  if (c.empty) return BSA_OK;
+  if (c.g.nbk > kMaxBlocks)
+    return fail(BSA_ERR_UNSUPPORTED, "%d key blocks per head: selection supports at most %d",
+                c.g.nbk, kMaxBlocks);
+  if (!q || !k || !idx || !cnt)
+    return fail(BSA_ERR_INVALID_ARG, "q, k, idx and cnt must be non-NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(BSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  const int row0 = noisy ? c.g.cond_blocks : 0;
+  const int kb0 = noisy ? c.g.cond_kblocks : 0;
+  if (kb0 > 0) {
+    if (!cache) return fail(BSA_ERR_INVALID_ARG, "the condition cache must be non-NULL");
+    if (!aligned16(cache)) return fail(BSA_ERR_INVALID_ARG, "the condition cache must be 16-byte aligned");
+    if (cache_bytes < cond_cache_bytes(c.g))
+      return fail(BSA_ERR_WORKSPACE, "the condition cache needs %zu bytes (got %zu)",
+                  cond_cache_bytes(c.g), cache_bytes);
+  }
+  const SelectLayout L = select_layout(c.g);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(BSA_ERR_WORKSPACE, "select needs %zu workspace bytes (got %zu)", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const int stride = params->mode == BSA_TOPK ? params->k : params->k_max;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qp = reinterpret_cast<float*>(ws + L.qp);
+  float* kp = reinterpret_cast<float*>(ws + L.kp);
+  float* sc = reinterpret_cast<float*>(ws + L.s);
+  const bsa::bf16_bits* qb = static_cast<const bsa::bf16_bits*>(q);
+  const bsa::bf16_bits* kb = static_cast<const bsa::bf16_bits*>(k);
+  if (c.g.nk == bsa::kBlockTokens && c.g.ctk == c.g.ct && c.g.chk == c.g.ch) {
+    st = launched(bsa::launch_pool(c.g, qb, kb, qp, kp, row0, s), "pool");
+  } else {
+    st = launched(bsa::launch_pool_queries(c.g, qb, qp, row0, s), "pool");
+    if (st != BSA_OK) return st;
+    st = launched(bsa::launch_pool_keys(c.g, kb, kp, kb0, c.g.nbk, c.g.nbk, s), "pool");
+  }
+  if (st != BSA_OK) return st;
+  if (kb0 > 0) {
+    // Cached condition rows into the leading rows of each head's pooled keys.
+    const size_t row_bytes = (size_t)bsa::kHeadDim * sizeof(float);
+    const hipError_t e = hipMemcpy2DAsync(kp, (size_t)c.g.nbk * row_bytes, cache, kb0 * row_bytes,
+                                          kb0 * row_bytes, (size_t)c.g.bh, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess)
+      return fail(BSA_ERR_LAUNCH, "condition cache copy failed: %s", hipGetErrorString(e));
+  }
+  st = launched(bsa::launch_scores(c.g, qp, kp, sc, row0, s), "scores");
+  if (st != BSA_OK) return st;
+  return launched(bsa::launch_select(c.g, sc, params->mode, params->k, params->cdf_p,
+                                     params->k_min, params->k_max, stride, idx, cnt, row0, s),
+                  "select");
 }
 
 struct BwdLayout {
@@ -235,46 +304,40 @@ size_t bsa_attention_workspace_bytes(const bsa_problem* problem) {
 bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* params,
                       const void* q, const void* k, int32_t* idx, int32_t* cnt,
                       void* workspace, size_t workspace_bytes, void* stream) {
+  return select_common(problem, params, q, k, nullptr, 0, idx, cnt, workspace, workspace_bytes,
+                       stream, false);
+}
+
+size_t bsa_cond_cache_bytes(const bsa_problem* problem) {
+  Checked c;
+  if (check_problem(problem, &c) != BSA_OK) return 0;
+  return cond_cache_bytes(c.g);
+}
+
+bsa_status bsa_pool_cond_keys(const bsa_problem* problem, const void* k, float* cache,
+                              size_t cache_bytes, void* stream) {
   Checked c;
   bsa_status st = check_problem(problem, &c);
   if (st != BSA_OK) return st;
-  st = check_params(params);
-  if (st != BSA_OK) return st;
-  if (c.empty) return BSA_OK;
-  if (c.g.nbk > kMaxBlocks)
-    return fail(BSA_ERR_UNSUPPORTED, "%d key blocks per head: selection supports at most %d",
-                c.g.nbk, kMaxBlocks);
-  if (!q || !k || !idx || !cnt)
-    return fail(BSA_ERR_INVALID_ARG, "q, k, idx and cnt must be non-NULL");
-  if (!aligned16(q) || !aligned16(k)) return fail(BSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
-  const SelectLayout L = select_layout(c.g);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(BSA_ERR_WORKSPACE, "select needs %zu workspace bytes (got %zu)", L.total,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  const int stride = params->mode == BSA_TOPK ? params->k : params->k_max;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  float* qp = reinterpret_cast<float*>(ws + L.qp);
-  float* kp = reinterpret_cast<float*>(ws + L.kp);
-  float* sc = reinterpret_cast<float*>(ws + L.s);
-  if (c.g.nk == bsa::kBlockTokens && c.g.ctk == c.g.ct && c.g.chk == c.g.ch) {
-    st = launched(bsa::launch_pool(c.g, static_cast<const bsa::bf16_bits*>(q),
-                                   static_cast<const bsa::bf16_bits*>(k), qp, kp, s),
+  if (c.empty || c.g.cond_kblocks == 0) return BSA_OK;
+  if (!k || !cache) return fail(BSA_ERR_INVALID_ARG, "k and cache must be non-NULL");
+  if (!aligned16(k) || !aligned16(cache))
+    return fail(BSA_ERR_INVALID_ARG, "k and cache must be 16-byte aligned");
+  if (cache_bytes < cond_cache_bytes(c.g))
+    return fail(BSA_ERR_WORKSPACE, "the condition cache needs %zu bytes (got %zu)",
+                cond_cache_bytes(c.g), cache_bytes);
+  return launched(bsa::launch_pool_keys(c.g, static_cast<const bsa::bf16_bits*>(k), cache, 0,
+                                        c.g.cond_kblocks, c.g.cond_kblocks,
+                                        reinterpret_cast<hipStream_t>(stream)),
                   "pool");
-  } else {
-    st = launched(bsa::launch_pool_queries(c.g, static_cast<const bsa::bf16_bits*>(q), qp, s),
-                  "pool");
-    if (st != BSA_OK) return st;
-    st = launched(bsa::launch_pool_keys(c.g, static_cast<const bsa::bf16_bits*>(k), kp, s),
-                  "pool");
-  }
-  if (st != BSA_OK) return st;
-  st = launched(bsa::launch_scores(c.g, qp, kp, sc, s), "scores");
-  if (st != BSA_OK) return st;
-  return launched(bsa::launch_select(c.g, sc, params->mode, params->k, params->cdf_p,
-                                     params->k_min, params->k_max, stride, idx, cnt, s),
-                  "select");
+}
+
+bsa_status bsa_select_noisy(const bsa_problem* problem, const bsa_select_params* params,
+                            const void* q, const void* k, const float* cache, size_t cache_bytes,
+                            int32_t* idx, int32_t* cnt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return select_common(problem, params, q, k, cache, cache_bytes, idx, cnt, workspace,
+                       workspace_bytes, stream, true);
 }
 
 bsa_status bsa_attention(const bsa_problem* problem, const void* q, const void* k, const void* v,
@@ -292,6 +355,14 @@ bsa_status bsa_attention_lse(const bsa_problem* problem, const void* q, const vo
     return fail(BSA_ERR_INVALID_ARG, "lse must be non-NULL");
   return attention_common(problem, q, k, v, idx, cnt, idx_stride, o, lse, workspace,
                           workspace_bytes, stream, false);
+}
+
+bsa_status bsa_attention_noisy(const bsa_problem* problem, const void* q, const void* k,
+                               const void* v, const int32_t* idx, const int32_t* cnt,
+                               int32_t idx_stride, void* o, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return attention_common(problem, q, k, v, idx, cnt, idx_stride, o, nullptr, workspace,
+                          workspace_bytes, stream, false, true);
 }
 
 size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem) {

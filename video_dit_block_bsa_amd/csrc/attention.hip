@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const int pair = x / a.nq8;
   const int r = x - pair * a.nq8;
   const int chunk = a.nq8 >> 3;
-  const int qb = (r & 7) * chunk + (r >> 3);
+  const int qb = a.q_begin + (r & 7) * chunk + (r >> 3);
   if (qb >= g.nb) return;
 
   const int t = threadIdx.x;
@@ -408,9 +408,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
 
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                             const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
-                            int stride, bool dense, bf16_bits* o, float* lse,
+                            int stride, bool dense, bf16_bits* o, float* lse, int q_begin,
                             hipStream_t stream) {
-  dim3 grid((unsigned)((size_t)g.bh * ((g.nb + 7) / 8 * 8)));
+  if (q_begin >= g.nb) return hipSuccess;
+  dim3 grid((unsigned)((size_t)g.bh * ((g.nb - q_begin + 7) / 8 * 8)));
   if (dense) {
     // Dense attention walks all allowed keys in blocks of the query chunk.
     Geom gd = g;
@@ -422,12 +423,12 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
     gd.nbk = g.nb;
     gd.nk = kBlockTokens;
     gd.cond_kblocks = g.cond_blocks;
-    const AttnArgs a = make_attn_args(gd, 1);
+    const AttnArgs a = make_attn_args(gd, 1, q_begin);
     hipLaunchKernelGGL((attn_kernel<true, false, 0>), grid, dim3(kThreads), 0, stream, a, q, k, v,
                        idx, cnt, o, nullptr);
     return hipGetLastError();
   }
-  const AttnArgs a = make_attn_args(g, stride);
+  const AttnArgs a = make_attn_args(g, stride, q_begin);
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
 #define BSA_LAUNCH_ATTN(LSE, MODE)                                                             \
   hipLaunchKernelGGL((attn_kernel<false, LSE, MODE>), grid, dim3(kThreads), 0, stream, a, q, k, v, \

@@ -82,17 +82,19 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_pool(const Geom& g, const bf16_bits* q, const bf16_bits* k, float* qp,
-                       float* kp, hipStream_t stream);
-hipError_t launch_pool_keys(const Geom& g, const bf16_bits* k, float* kp, hipStream_t stream);
-hipError_t launch_pool_queries(const Geom& g, const bf16_bits* q, float* qp, hipStream_t stream);
-hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float* s,
+                       float* kp, int blk0, hipStream_t stream);
+hipError_t launch_pool_queries(const Geom& g, const bf16_bits* q, float* qp, int blk0,
+                               hipStream_t stream);
+hipError_t launch_pool_keys(const Geom& g, const bf16_bits* k, float* kp, int blk0, int blk_end,
+                            int out_rows, hipStream_t stream);
+hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float* s, int row0,
                          hipStream_t stream);
 hipError_t launch_select(const Geom& g, const float* s, int mode, int k, float p, int k_min,
-                         int k_max, int stride, int32_t* idx, int32_t* cnt,
+                         int k_max, int stride, int32_t* idx, int32_t* cnt, int row0,
                          hipStream_t stream);
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                             const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
-                            int stride, bool dense, bf16_bits* o, float* lse,
+                            int stride, bool dense, bf16_bits* o, float* lse, int q_begin,
                             hipStream_t stream);
 hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                                 const bf16_bits* v, const bf16_bits* o, const bf16_bits* dout,

@@ -15,12 +15,12 @@
 
 namespace bsa {
 
-__global__ __launch_bounds__(kThreads) void pool_kernel(Geom g, const bf16_bits* __restrict__ q,
+__global__ __launch_bounds__(kThreads) void pool_kernel(Geom g, int blk0, const bf16_bits* __restrict__ q,
                                                         const bf16_bits* __restrict__ k,
                                                         float* __restrict__ qp,
                                                         float* __restrict__ kp) {
   __shared__ float part[2][16][kHeadDim + 4];
-  const int blk = blockIdx.x;
+  const int blk = blk0 + blockIdx.x;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
   const int chunk = t & 15;
@@ -68,11 +68,14 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Geom g, const bf16_bits*
 // blocks of n = 64 .. 1024 tokens (query blocks, or key blocks with kKeys).
 // Thread t adds channel chunk t % 16 of the n/16 consecutive slots
 // (t/16)*n/16 ..; the 16 partial sums meet in LDS in a fixed order, as above.
+// Blocks blk0, blk0+1, ... of each (batch, head); pooled row blk goes to row
+// blk of an array of out_rows rows per (batch, head).
 template <bool kKeys>
-__global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, const bf16_bits* __restrict__ x,
+__global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, int blk0, int out_rows,
+                                                            const bf16_bits* __restrict__ x,
                                                             float* __restrict__ xp) {
   __shared__ float part[16][kHeadDim + 4];
-  const int blk = blockIdx.x;
+  const int blk = blk0 + blockIdx.x;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
   const int chunk = t & 15;
@@ -106,25 +109,31 @@ __global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, const bf16_b
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum += part[r][t];
-    const int nblocks = kKeys ? g.nbk : g.nb;
-    xp[((size_t)bh * nblocks + blk) * kHeadDim + t] = sum * (1.0f / (float)n);
+    xp[((size_t)bh * out_rows + blk) * kHeadDim + t] = sum * (1.0f / (float)n);
   }
 }
 
-hipError_t launch_pool_queries(const Geom& g, const bf16_bits* q, float* qp, hipStream_t stream) {
-  hipLaunchKernelGGL(pool_one_kernel<false>, dim3(g.nb, g.bh), dim3(kThreads), 0, stream, g, q, qp);
+hipError_t launch_pool_queries(const Geom& g, const bf16_bits* q, float* qp, int blk0,
+                               hipStream_t stream) {
+  if (blk0 >= g.nb) return hipSuccess;
+  hipLaunchKernelGGL(pool_one_kernel<false>, dim3(g.nb - blk0, g.bh), dim3(kThreads), 0, stream, g,
+                     blk0, g.nb, q, qp);
   return hipGetLastError();
 }
 
-hipError_t launch_pool_keys(const Geom& g, const bf16_bits* k, float* kp, hipStream_t stream) {
-  hipLaunchKernelGGL(pool_one_kernel<true>, dim3(g.nbk, g.bh), dim3(kThreads), 0, stream, g, k, kp);
+hipError_t launch_pool_keys(const Geom& g, const bf16_bits* k, float* kp, int blk0, int blk_end,
+                            int out_rows, hipStream_t stream) {
+  if (blk0 >= blk_end) return hipSuccess;
+  hipLaunchKernelGGL(pool_one_kernel<true>, dim3(blk_end - blk0, g.bh), dim3(kThreads), 0, stream, g,
+                     blk0, out_rows, k, kp);
   return hipGetLastError();
 }
 
 hipError_t launch_pool(const Geom& g, const bf16_bits* q, const bf16_bits* k, float* qp,
-                       float* kp, hipStream_t stream) {
-  dim3 grid(g.nb, g.bh);
-  hipLaunchKernelGGL(pool_kernel, grid, dim3(kThreads), 0, stream, g, q, k, qp, kp);
+                       float* kp, int blk0, hipStream_t stream) {
+  if (blk0 >= g.nb) return hipSuccess;
+  dim3 grid(g.nb - blk0, g.bh);
+  hipLaunchKernelGGL(pool_kernel, grid, dim3(kThreads), 0, stream, g, blk0, q, k, qp, kp);
   return hipGetLastError();
 }
 

@@ -28,13 +28,13 @@ constexpr int kScoreRow = kHeadDim + 4;  // padded LDS row (floats)
 // (lanes 32..63): any pairing of channels works as long as both operands use
 // the same one, and this one lets a lane read four steps of its row with one
 // 16-byte LDS load. Row stride 132 floats keeps those loads conflict-free.
-__global__ __launch_bounds__(kThreads) void scores_kernel(Geom g, const float* __restrict__ qp,
+__global__ __launch_bounds__(kThreads) void scores_kernel(Geom g, int row0, const float* __restrict__ qp,
                                                           const float* __restrict__ kp,
                                                           float* __restrict__ s) {
   __shared__ __attribute__((aligned(16))) float qs[kScoreTile][kScoreRow];
   __shared__ __attribute__((aligned(16))) float ks[kScoreTile][kScoreRow];
   const int bh = blockIdx.z;
-  const int i0 = blockIdx.y * kScoreTile;
+  const int i0 = row0 + blockIdx.y * kScoreTile;
   const int j0 = blockIdx.x * kScoreTile;
   const int t = threadIdx.x;
   const float* qb = qp + (size_t)bh * g.nb * kHeadDim;
@@ -102,16 +102,19 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Rows row0 .. nb-1 of every (batch, head).
 template <int R>
-__global__ __launch_bounds__(kThreads) void select_kernel(Geom g, const float* __restrict__ s,
+__global__ __launch_bounds__(kThreads) void select_kernel(Geom g, int row0, const float* __restrict__ s,
                                                           int mode, int k, float p, int k_min,
                                                           int k_max, int stride,
                                                           int32_t* __restrict__ idx,
                                                           int32_t* __restrict__ cnt) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= g.bh * g.nb) return;  // whole wave leaves together
-  const int i = row % g.nb;
+  const int rows_per_head = g.nb - row0;
+  const int local = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (local >= g.bh * rows_per_head) return;  // whole wave leaves together
+  const int i = row0 + local % rows_per_head;
+  const int row = (local / rows_per_head) * g.nb + i;
   const int na = allowed_key_blocks(g, i);
   const float* srow = s + (size_t)row * g.nbk;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -218,36 +221,42 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Geom g, const float* _
   if (lane == 0) cnt[row] = keep;
 }
 
-hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float* s,
+hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float* s, int row0,
                          hipStream_t stream) {
-  dim3 grid((g.nbk + kScoreTile - 1) / kScoreTile, (g.nb + kScoreTile - 1) / kScoreTile, g.bh);
-  hipLaunchKernelGGL(scores_kernel, grid, dim3(kThreads), 0, stream, g, qp, kp, s);
+  if (row0 >= g.nb) return hipSuccess;
+  dim3 grid((g.nbk + kScoreTile - 1) / kScoreTile, (g.nb - row0 + kScoreTile - 1) / kScoreTile,
+            g.bh);
+  hipLaunchKernelGGL(scores_kernel, grid, dim3(kThreads), 0, stream, g, row0, qp, kp, s);
   return hipGetLastError();
 }
 
 template <int R>
 static hipError_t launch_select_r(const Geom& g, const float* s, int mode, int k, float p,
                                   int k_min, int k_max, int stride, int32_t* idx, int32_t* cnt,
-                                  hipStream_t stream) {
-  const long rows = (long)g.bh * g.nb;
+                                  int row0, hipStream_t stream) {
+  const long rows = (long)g.bh * (g.nb - row0);
+  if (rows <= 0) return hipSuccess;
   const int rows_per_wg = kThreads / 64;
   dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
-  hipLaunchKernelGGL(select_kernel<R>, grid, dim3(kThreads), 0, stream, g, s, mode, k, p, k_min,
-                     k_max, stride, idx, cnt);
+  hipLaunchKernelGGL(select_kernel<R>, grid, dim3(kThreads), 0, stream, g, row0, s, mode, k, p,
+                     k_min, k_max, stride, idx, cnt);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const Geom& g, const float* s, int mode, int k, float p, int k_min,
-                         int k_max, int stride, int32_t* idx, int32_t* cnt,
+                         int k_max, int stride, int32_t* idx, int32_t* cnt, int row0,
                          hipStream_t stream) {
   const int chunks = (g.nbk + 63) / 64;
-  if (chunks <= 1) return launch_select_r<1>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
-  if (chunks <= 2) return launch_select_r<2>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
-  if (chunks <= 4) return launch_select_r<4>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
-  if (chunks <= 8) return launch_select_r<8>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
-  if (chunks <= 16) return launch_select_r<16>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
-  if (chunks <= 32) return launch_select_r<32>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
-  return launch_select_r<64>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, stream);
+#define BSA_SELECT_R(R) \
+  return launch_select_r<R>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, row0, stream)
+  if (chunks <= 1) BSA_SELECT_R(1);
+  if (chunks <= 2) BSA_SELECT_R(2);
+  if (chunks <= 4) BSA_SELECT_R(4);
+  if (chunks <= 8) BSA_SELECT_R(8);
+  if (chunks <= 16) BSA_SELECT_R(16);
+  if (chunks <= 32) BSA_SELECT_R(32);
+  BSA_SELECT_R(64);
+#undef BSA_SELECT_R
 }
 
 }  // namespace bsa

@@ -18,7 +18,8 @@ __device__ __forceinline__ int swap23(int m) {
 struct AttnArgs {
   Geom g;
   int stride;
-  int nq8;            // query blocks per head rounded up to a multiple of 8
+  int q_begin;        // first query block of the launch (the others are skipped)
+  int nq8;            // query blocks of the launch per head, rounded up to a multiple of 8
   uint32_t mag_nw;    // floor(2^32 / nW) + 1
   uint32_t mag_nhw;   // floor(2^32 / (nH*nW)) + 1
   uint32_t mag_nwk;   // the same for the key-block grid
@@ -78,11 +79,12 @@ __device__ __forceinline__ void workgroup_barrier() {
 }
 
 // Kernel arguments for a problem with index rows of `stride` entries.
-inline AttnArgs make_attn_args(const Geom& g, int stride) {
+inline AttnArgs make_attn_args(const Geom& g, int stride, int q_begin = 0) {
   AttnArgs a;
   a.g = g;
   a.stride = stride;
-  a.nq8 = (g.nb + 7) / 8 * 8;
+  a.q_begin = q_begin;
+  a.nq8 = (g.nb - q_begin + 7) / 8 * 8;
   a.mag_nw = (uint32_t)(0x100000000ull / (uint64_t)g.nW + 1);
   a.mag_nhw = (uint32_t)(0x100000000ull / (uint64_t)(g.nH * g.nW) + 1);
   a.mag_nwk = (uint32_t)(0x100000000ull / (uint64_t)g.nWk + 1);
