@@ -28,8 +28,8 @@
  *   S = T*H*W tokens in latent order s = (t*H + h)*W + w. Pointers are device
  *   pointers, 16-byte aligned. head_dim must be 128.
  * Blocks. nT = T/ct, nH = H/ch, nW = W/cw; block id
- *   i = (bt*nH + bh)*nW + bw; a query block holds ct*ch*cw = 128 tokens. The
- *   grid must divide by the chunk shape. Key blocks are numbered the same way
+ *   i = (bt*nH + bh)*nW + bw; a query block holds ct*ch*cw = 64 or 128 tokens.
+ *   The grid must divide by the chunk shape. Key blocks are numbered the same way
  *   with the key chunk (ctk, chk, cwk) when one is given (Nk of them), else
  *   they are the query blocks (Nk = Nb).
  * Ownership. The caller owns every buffer. The library never allocates,
@@ -74,7 +74,8 @@ typedef struct bsa_problem {
   int32_t heads;       /* >= 0 */
   int32_t head_dim;    /* must be 128 */
   int32_t T, H, W;     /* latent grid, each > 0; T*H*W < 2^24 */
-  int32_t ct, ch, cw;  /* chunk shape; ct*ch*cw must be 128 and divide the grid */
+  int32_t ct, ch, cw;  /* query chunk shape; ct*ch*cw must be 64 or 128 and divide
+                          the grid */
   int32_t cond_frames; /* 0: no block-causal mask; else a multiple of ct (and of
                           ctk), < T */
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
@@ -194,8 +195,8 @@ size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
  * P is recomputed in fp32 from lse; the products run in bf16 with fp32
  * accumulation (P and dS are rounded to bf16 as MFMA operands). No
  * floating-point atomics: results are bit-identical from run to run.
- * Limits: Nb <= 4096 blocks per (batch, head); the key chunk must be the
- * query chunk (BSA_ERR_UNSUPPORTED otherwise). */
+ * Limits: Nb <= 4096 blocks per (batch, head); query blocks of 128 tokens and
+ * the key chunk equal to the query chunk (BSA_ERR_UNSUPPORTED otherwise). */
 bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const void* k,
                              const void* v, const void* o, const void* dout, const float* lse,
                              const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* dq,

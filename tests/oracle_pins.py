@@ -489,6 +489,11 @@ _KEY_CASES = (
      O.SelectParams("cdf", p=0.7, k_min=1, k_max=6)),
     (O.Geometry(8, 16, 32, ctk=8, chk=8, cwk=16), O.SelectParams("topk", k=2)),
     (O.Geometry(8, 16, 32, ctk=2, chk=4, cwk=8, cond_frames=4), O.SelectParams("topk", k=7)),
+    # 64-token query blocks with 64-, 128- and 256-token key blocks.
+    (O.Geometry(8, 16, 32, 2, 4, 8, ctk=2, chk=4, cwk=8), O.SelectParams("topk", k=5)),
+    (O.Geometry(8, 16, 32, 2, 4, 8, cond_frames=4, ctk=4, chk=4, cwk=8),
+     O.SelectParams("cdf", p=0.7, k_min=1, k_max=6)),
+    (O.Geometry(8, 16, 32, 4, 2, 8, ctk=4, chk=8, cwk=8), O.SelectParams("topk", k=3)),
 )
 
 

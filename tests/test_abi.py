@@ -84,7 +84,8 @@ def _attn(problem, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE, stride=4, o=FAKE 
     [
         (dict(head_dim=64), UNSUPPORTED),
         (dict(head_dim=0), INVALID),
-        (dict(chunk=(4, 4, 4)), UNSUPPORTED),
+        (dict(chunk=(2, 4, 4)), UNSUPPORTED),   # 32-token query blocks
+        (dict(chunk=(4, 8, 8)), UNSUPPORTED),   # 256-token query blocks
         (dict(T=57), UNSUPPORTED),
         (dict(cond_frames=3), INVALID),
         (dict(cond_frames=56), INVALID),
@@ -275,3 +276,13 @@ def test_cond_cache_checks():
     q0 = _problem(heads=0, cond_frames=4)
     assert lib.bsa_attention_noisy(ctypes.byref(q0), None, None, None, None, None, 4, None, None,
                                    0, None) == OK
+
+
+def test_query_chunk_of_64():
+    """64-token query blocks are accepted by selection and attention; the
+    backward rejects them."""
+    p = _problem(chunk=(2, 4, 8))          # 3,360 query blocks
+    sp = B.SelectParams.topk(4)
+    assert B.select_workspace_bytes(p, sp) > 0
+    assert _bwd(p) == UNSUPPORTED
+    assert _select(_problem(T=4 * 64, chunk=(2, 4, 8)), sp) == UNSUPPORTED  # 15,360 key blocks

@@ -248,14 +248,58 @@ def test_skips_invalid_ids_and_clamps_cnt():
     ((8, 16, 32), (2, 8, 8), (4, 8, 16), SelectParams.topk(3), 0),   # 512, another query chunk
     ((8, 16, 32), (4, 4, 8), (4, 8, 8), SelectParams.cdf(0.8, 1, 6), 4),
     ((8, 16, 32), (4, 4, 8), (2, 4, 8), SelectParams.cdf(0.7, 1, 9), 4),
+    # 64-token query blocks (key-half split): with 64-, 128- and 256-token keys.
+    ((8, 16, 32), (2, 4, 8), None, SelectParams.topk(5), 0),
+    ((8, 16, 32), (2, 4, 8), (4, 4, 8), SelectParams.topk(4), 0),
+    ((8, 16, 32), (2, 4, 8), (4, 8, 8), SelectParams.topk(3), 0),
+    ((8, 16, 32), (4, 2, 8), (2, 4, 8), SelectParams.cdf(0.7, 1, 7), 4),
 ])
 def test_key_chunks(grid, chunk, key_chunk, params, cond):
-    """Key blocks cut with their own chunk (64 to 1024 tokens): every index
-    row and every output against the oracle."""
+    """Key blocks cut with their own chunk (64 to 1024 tokens), and query
+    blocks of 64 tokens: every index row and every output against the
+    oracle."""
     T, H, W = grid
     q, k, v = make_qkv(T, H, W, 2, kind="field", seed=17)
     problem = Problem.make(T, H, W, 2, chunk=chunk, cond_frames=cond, key_chunk=key_chunk)
     _run_and_compare(problem, params, q, k, v)
+
+
+def test_query_chunk_64_dense_and_lse():
+    """64-token query blocks: dense attention against the oracle's dense
+    (block-causal) attention, and bsa_attention_lse: the same o as
+    bsa_attention and lse against the oracle's."""
+    import torch
+
+    from video_dit_block_bsa_amd import binding as B
+
+    T, H, W = 8, 16, 32
+    q, k, v = make_qkv(T, H, W, 2, kind="field", seed=29)
+    problem = Problem.make(T, H, W, 2, chunk=(2, 4, 8), cond_frames=4)
+    g = PT.geometry(problem)
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    o = O.bf16_bits_to_f64(PT.from_device(PT.run_dense(problem, qd, kd, vd)).reshape(q.shape))
+    for h in range(2):
+        ref = O.dense_head(*(O.bf16_bits_to_f64(a[0, h]) for a in (q, k, v)), g, SCALE)
+        err = np.abs(o[0, h] - ref)
+        _log(f"dense q64 head {h}: max-abs {err.max():.3e}, mean-abs {err.mean():.3e}")
+        assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS
+    params = SelectParams.topk(5)
+    stride = B.index_stride(params)
+    idx_d, cnt_d = PT.run_select(problem, params, qd, kd)
+    o1 = PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, stride)
+    o2 = torch.full_like(qd, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    B.bsa_attention_lse(problem, qd, kd, vd, idx_d, cnt_d, stride, o2, lse,
+                        torch.empty(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    idx = idx_d.cpu().numpy()
+    cnt = cnt_d.cpu().numpy()
+    nb = g.num_blocks
+    for h in range(2):
+        _, lse_r = O.forward_lse_head(*(O.bf16_bits_to_f64(a[0, h]) for a in (q, k, v)), g,
+                                      idx[h * nb:(h + 1) * nb], cnt[h * nb:(h + 1) * nb], SCALE)
+        assert np.abs(lse[0, h].cpu().numpy() - lse_r).max() <= 2.5e-3
 
 
 @pytest.mark.parametrize("key_chunk", [(2, 4, 8), (4, 8, 8)])
@@ -291,7 +335,7 @@ def test_key_chunks_invalid_ids_and_clamps(key_chunk):
             assert np.all(got == 0.0)
 
 
-@pytest.mark.parametrize("name", ["480p", "720p", "long", "vc", "long_k64", "long_k256"])
+@pytest.mark.parametrize("name", ["480p", "720p", "long", "vc", "long_k64", "long_k256", "long_q64"])
 def test_full_size_workload(name):
     """Full-size workloads in the configuration the benchmark times: every
     index row against the oracle, outputs on a seeded sample."""

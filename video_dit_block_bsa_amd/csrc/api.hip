@@ -46,9 +46,11 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
   if (p->head_dim <= 0) return fail(BSA_ERR_INVALID_ARG, "head_dim must be positive");
   if (p->head_dim != bsa::kHeadDim)
     return fail(BSA_ERR_UNSUPPORTED, "head_dim %d: only 128 is implemented", p->head_dim);
-  if ((long)p->ct * p->ch * p->cw != bsa::kBlockTokens)
-    return fail(BSA_ERR_UNSUPPORTED, "chunk %dx%dx%d: blocks of exactly 128 tokens are implemented",
-                p->ct, p->ch, p->cw);
+  const long nq = (long)p->ct * p->ch * p->cw;
+  if (nq != 64 && nq != bsa::kBlockTokens)
+    return fail(BSA_ERR_UNSUPPORTED,
+                "chunk %dx%dx%d: query blocks of 64 or 128 tokens are implemented", p->ct, p->ch,
+                p->cw);
   if (p->T % p->ct || p->H % p->ch || p->W % p->cw)
     return fail(BSA_ERR_UNSUPPORTED, "grid %dx%dx%d is not divisible by chunk %dx%dx%d", p->T,
                 p->H, p->W, p->ct, p->ch, p->cw);
@@ -82,7 +84,7 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
     return fail(BSA_ERR_UNSUPPORTED, "sequence of %ld tokens is too long (at most 2^24 - 1)", S);
   const long bh = (long)p->batch * p->heads;
   if (bh > (1L << 24)) return fail(BSA_ERR_UNSUPPORTED, "batch*heads = %ld is too large", bh);
-  const long nb = S / bsa::kBlockTokens;
+  const long nb = S / nq;
   const long nhw = (long)(p->H / p->ch) * (p->W / p->cw);
   if ((unsigned long)nb * (unsigned long)nhw >= (1ul << 32))
     return fail(BSA_ERR_UNSUPPORTED, "block grid %ld x %ld is too large", nb, nhw);
@@ -103,7 +105,8 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
   g.cw = p->cw;
   g.nH = p->H / p->ch;
   g.nW = p->W / p->cw;
-  g.nb = (int)(S / bsa::kBlockTokens);
+  g.nb = (int)(S / nq);
+  g.nq = (int)nq;
   g.cond_blocks = (p->cond_frames / p->ct) * g.nH * g.nW;
   g.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
   g.ctk = ctk;
@@ -235,7 +238,8 @@ bsa_status select_common(const bsa_problem* problem, const bsa_select_params* pa
   float* sc = reinterpret_cast<float*>(ws + L.s);
   const bsa::bf16_bits* qb = static_cast<const bsa::bf16_bits*>(q);
   const bsa::bf16_bits* kb = static_cast<const bsa::bf16_bits*>(k);
-  if (c.g.nk == bsa::kBlockTokens && c.g.ctk == c.g.ct && c.g.chk == c.g.ch) {
+  if (c.g.nq == bsa::kBlockTokens && c.g.nk == bsa::kBlockTokens && c.g.ctk == c.g.ct &&
+      c.g.chk == c.g.ch) {
     st = launched(bsa::launch_pool(c.g, qb, kb, qp, kp, row0, s), "pool");
   } else {
     st = launched(bsa::launch_pool_queries(c.g, qb, qp, row0, s), "pool");
@@ -383,8 +387,9 @@ bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const vo
   if (c.g.nb > kMaxBlocks)
     return fail(BSA_ERR_UNSUPPORTED, "%d blocks per head: the backward supports at most %d",
                 c.g.nb, kMaxBlocks);
-  if (c.g.ctk != c.g.ct || c.g.chk != c.g.ch || c.g.cwk != c.g.cw)
-    return fail(BSA_ERR_UNSUPPORTED, "the backward needs the key chunk to be the query chunk");
+  if (c.g.nq != bsa::kBlockTokens || c.g.ctk != c.g.ct || c.g.chk != c.g.ch || c.g.cwk != c.g.cw)
+    return fail(BSA_ERR_UNSUPPORTED,
+                "the backward needs 128-token query blocks and the key chunk to be the query chunk");
   const void* ins[6] = {q, k, v, o, dout, lse};
   void* outs[3] = {dq, dk, dv};
   for (const void* p : ins)

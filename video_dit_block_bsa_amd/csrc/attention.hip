@@ -90,7 +90,15 @@ constexpr int kSlots = 5;                               // half-tile ring per wo
 //               lower one and its scores are set to -inf.
 // A unit's slot offsets are those of its first slot plus those of its slot
 // index (power-of-two chunk sides make the offset linear in the index bits).
-template <bool kDense, bool kLse, int kKeyMode>
+//
+// kSplit serves query blocks of 64 tokens: wave w takes queries 32(w%2) ..
+// +31 and key half w/2 (keys 0..63 or 64..127) of every unit, keeps its own
+// running max and sum over its keys, and the two key halves of a query meet
+// in LDS after the loop (O = (O_a 2^(m_a-m) + O_b 2^(m_b-m)) / (l_a 2^(m_a-m)
+// + l_b 2^(m_b-m)), m = max(m_a, m_b)). Every wave then issues half the MFMAs
+// of a unit, and the key half is a template constant inside the loop (two
+// copies), so each read still names its slot.
+template <bool kDense, bool kLse, int kKeyMode, bool kSplit>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const int32_t* __restrict__ idx,
@@ -124,6 +132,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n = lane & 31;
   const int gs = lane >> 5;
+  const int qh = kSplit ? (w & 1) : w;  // 32-query slice of the block
+  const int kh = kSplit ? (w >> 1) : 0; // key half (split mode)
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
   // K and V of this (batch, head) as buffer resources: a tile load takes one
   // 32-bit lane offset, and anything past the head reads as zero.
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(vp + hoff), (short)0, head_bytes, kBufferWord3);
 
-  const int qtok = block_origin(a, qb) + slot_offset(g, 32 * w + n);
+  const int qtok = block_origin(a, qb) + slot_offset(g, 32 * qh + n);
   bf16x8 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
@@ -204,9 +214,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   auto unit_base = [&](Cursor c, int h) -> uint32_t {
     if constexpr (kKeyMode == 2) {
       const int p = (h != 0 && c.b < count) ? c.b : c.a;
-      return (uint32_t)key_block_origin(a, list[p]) * (kHeadDim * 2);
+      return (uint32_t)key_block_origin(a, kb_at(p)) * (kHeadDim * 2);
     } else if constexpr (kKeyMode == 1) {
-      return (uint32_t)(key_block_origin(a, list[c.a]) + key_slot_offset(g, c.b * kBlockTokens)) *
+      return (uint32_t)(key_block_origin(a, kb_at(c.a)) + key_slot_offset(g, c.b * kBlockTokens)) *
                  (kHeadDim * 2) + h * half_off;
     } else {
       return (uint32_t)key_block_origin(a, kb_at(c.a)) * (kHeadDim * 2) + h * half_off;
@@ -250,7 +260,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   }
 
   // Units: cur (the unit of the current phase) and nxt (the one after it,
-  // with nxt.a == count past the last).
+  // with nxt.a == count past the last). KH is the key half in split mode.
+  auto run = [&](auto khc) {
+  constexpr int KH = decltype(khc)::value;
+  constexpr int kT = kSplit ? 2 : 4;  // 32-key sub-tiles of S per wave
   Cursor cur = first_unit();
   if (cur.a < count) {
     Cursor nxt = next_unit(cur);
@@ -290,14 +303,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
         // S^T = K Q^T for this wave's 32 queries and all 128 keys, channel
         // steps outermost (four independent accumulators between dependent
         // MFMAs).
-        f32x16 sacc[4];
+        f32x16 sacc[kT];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) sacc[tt] = f32x16{};
+        for (int tt = 0; tt < kT; ++tt) sacc[tt] = f32x16{};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const char* kt = tt < 2 ? lo : hi;
+          for (int tt = 0; tt < kT; ++tt) {
+            const char* kt = kSplit ? (KH ? hi : lo) : (tt < 2 ? lo : hi);
             const bf16x8 af =
                 *reinterpret_cast<const bf16x8*>(kt + 32 * (tt & 1) * 256 + (ka0 ^ (32 * s)));
             sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[tt], 0, 0, 0);
@@ -305,15 +318,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
         }
         if constexpr (kKeyMode == 2) {
           // A lone last 64-token key block: its unit has no upper half.
-          if (cur.b >= count) {
+          if ((!kSplit || KH == 1) && cur.b >= count) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[2][i] = sacc[3][i] = -INFINITY;
+            for (int tt = kT - 2; tt < kT; ++tt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) sacc[tt][i] = -INFINITY;
           }
         }
         // Online softmax for this lane's query (both lane halves agree on m2).
         float mx = -INFINITY;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < kT; ++tt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[tt][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c_log2;
@@ -326,16 +341,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
 #pragma unroll
           for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
         }
+        // In split mode a wave may have seen only masked keys so far (m2 still
+        // -inf): its probabilities are then exp2(-inf - 0) = 0.
+        const float msub = (kSplit && m2 == -INFINITY) ? 0.f : m2;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int tt = 0; tt < kT; ++tt) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             u32x4 packed;
 #pragma unroll
             for (int j2 = 0; j2 < 4; ++j2) {
               const f32x2 pr = {
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2], a.c_log2, -m2)),
-                  __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2 + 1], a.c_log2, -m2))};
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2], a.c_log2, -msub)),
+                  __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tt][8 * h + 2 * j2 + 1], a.c_log2, -msub))};
               const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
               l_part = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l_part, false);
               packed[j2] = __builtin_bit_cast(uint32_t, pb);
@@ -364,8 +382,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
             }
           }
         };
-        pv_half(lo, 0);
-        pv_half(hi, 4);
+        if constexpr (kSplit) {
+          pv_half(KH ? hi : lo, 0);
+        } else {
+          pv_half(lo, 0);
+          pv_half(hi, 4);
+        }
         if (nxt.a >= count) return false;
         cur = nxt;
         nxt = next_unit(cur);
@@ -380,11 +402,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
            phase(integral_constant<int, 8>{}) && phase(integral_constant<int, 9>{})) {
     }
     // The trailing loads are never read, but must land before the workgroup
-    // gives its LDS to the next one.
+    // gives its LDS to the next one (or to the merge below).
     __builtin_amdgcn_s_waitcnt(0x0070);
   }
+  };
+  if constexpr (kSplit) {
+    if (kh == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 0>{});
+  }
 
-  const float l = l_part + __shfl_xor(l_part, 32);
+  float l = l_part + __shfl_xor(l_part, 32);
+  if constexpr (kSplit) {
+    // The key halves of each query meet: waves 2, 3 leave O, m and l in LDS
+    // (the ring is idle now), waves 0, 1 merge them and write the output.
+    __syncthreads();
+    float* ob = reinterpret_cast<float*>(qh == 0 ? slot0 : slot1);  // 64 values x 64 lanes
+    float* mb = reinterpret_cast<float*>(slot2) + qh * 128;
+    if (kh == 1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ob[(u * 16 + i) * 64 + lane] = oacc[u][i];
+      mb[lane] = m2;
+      mb[64 + lane] = l;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m_b = mb[lane], l_b = mb[64 + lane];
+    const float m = fmaxf(m2, m_b);
+    const float fa = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m);
+    const float fb = (m_b == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_b - m);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[u][i] = oacc[u][i] * fa + ob[(u * 16 + i) * 64 + lane] * fb;
+    l = l * fa + l_b * fb;
+    m2 = m;
+  }
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
   if constexpr (kLse) {
     // sum_j exp(scale * q.k_j) = 2^m2 * l, so lse = (m2 + log2 l) * ln 2.
@@ -412,6 +470,7 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
                             hipStream_t stream) {
   if (q_begin >= g.nb) return hipSuccess;
   dim3 grid((unsigned)((size_t)g.bh * ((g.nb - q_begin + 7) / 8 * 8)));
+  const bool split = g.nq != kBlockTokens;
   if (dense) {
     // Dense attention walks all allowed keys in blocks of the query chunk.
     Geom gd = g;
@@ -421,27 +480,34 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
     gd.nHk = g.nH;
     gd.nWk = g.nW;
     gd.nbk = g.nb;
-    gd.nk = kBlockTokens;
+    gd.nk = g.nq;
     gd.cond_kblocks = g.cond_blocks;
     const AttnArgs a = make_attn_args(gd, 1, q_begin);
-    hipLaunchKernelGGL((attn_kernel<true, false, 0>), grid, dim3(kThreads), 0, stream, a, q, k, v,
-                       idx, cnt, o, nullptr);
+    if (split)
+      hipLaunchKernelGGL((attn_kernel<true, false, 2, true>), grid, dim3(kThreads), 0, stream, a, q,
+                         k, v, idx, cnt, o, nullptr);
+    else
+      hipLaunchKernelGGL((attn_kernel<true, false, 0, false>), grid, dim3(kThreads), 0, stream, a, q,
+                         k, v, idx, cnt, o, nullptr);
     return hipGetLastError();
   }
   const AttnArgs a = make_attn_args(g, stride, q_begin);
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
-#define BSA_LAUNCH_ATTN(LSE, MODE)                                                             \
-  hipLaunchKernelGGL((attn_kernel<false, LSE, MODE>), grid, dim3(kThreads), 0, stream, a, q, k, v, \
-                     idx, cnt, o, lse)
+#define BSA_LAUNCH_ATTN(LSE, MODE, SPLIT)                                                          \
+  hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT>), grid, dim3(kThreads), 0, stream, a, q, \
+                     k, v, idx, cnt, o, lse)
+#define BSA_LAUNCH_ATTN_MODES(LSE, SPLIT)      \
+  if (mode == 0) BSA_LAUNCH_ATTN(LSE, 0, SPLIT); \
+  else if (mode == 1) BSA_LAUNCH_ATTN(LSE, 1, SPLIT); \
+  else BSA_LAUNCH_ATTN(LSE, 2, SPLIT)
   if (lse) {
-    if (mode == 0) BSA_LAUNCH_ATTN(true, 0);
-    else if (mode == 1) BSA_LAUNCH_ATTN(true, 1);
-    else BSA_LAUNCH_ATTN(true, 2);
+    if (split) { BSA_LAUNCH_ATTN_MODES(true, true); }
+    else { BSA_LAUNCH_ATTN_MODES(true, false); }
   } else {
-    if (mode == 0) BSA_LAUNCH_ATTN(false, 0);
-    else if (mode == 1) BSA_LAUNCH_ATTN(false, 1);
-    else BSA_LAUNCH_ATTN(false, 2);
+    if (split) { BSA_LAUNCH_ATTN_MODES(false, true); }
+    else { BSA_LAUNCH_ATTN_MODES(false, false); }
   }
+#undef BSA_LAUNCH_ATTN_MODES
 #undef BSA_LAUNCH_ATTN
   return hipGetLastError();
 }

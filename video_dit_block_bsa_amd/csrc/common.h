@@ -25,7 +25,8 @@ struct Geom {
   int T, H, W;      // latent grid
   int ct, ch, cw;   // chunk shape
   int nH, nW;       // blocks along h and w
-  int nb;           // blocks per (batch, head)
+  int nb;           // query blocks per (batch, head)
+  int nq;           // tokens per query block (64 or 128)
   int cond_blocks;  // leading condition query blocks (0 = no block-causal mask)
   float scale;      // softmax scale
   // Key blocks: the grid cut with the key chunk (the query chunk unless the

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, int blk0, in
   const int t = threadIdx.x;
   const int chunk = t & 15;
   const int grp = t >> 4;
-  const int n = kKeys ? g.nk : kBlockTokens;
+  const int n = kKeys ? g.nk : g.nq;
   const int per = n >> 4;  // a multiple of 4
   const size_t head_off = (size_t)bh * g.S * kHeadDim;
   float acc[8];

@@ -83,6 +83,9 @@ WORKLOADS = {
                          note="215,040 tokens, 128-token query blocks, 3,360 key blocks of 64"),
     "long_k256": Workload("long_k256", 56, 48, 80, heads=32, seed=3, k=52, key_chunk=(4, 8, 8),
                           note="215,040 tokens, 128-token query blocks, 840 key blocks of 256"),
+    "long_q64": Workload("long_q64", 56, 48, 80, heads=32, seed=3, k=105, chunk=(2, 4, 8),
+                         key_chunk=(4, 4, 8),
+                         note="215,040 tokens, 3,360 query blocks of 64, 1,680 key blocks of 128"),
 }
 
 
