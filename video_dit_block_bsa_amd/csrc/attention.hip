@@ -5,8 +5,10 @@
 // Work decomposition
 //   One workgroup (4 x wave64) per (batch*head, query block of 128 tokens),
 //   two workgroups per CU; wave w owns queries 32w .. 32w+31 of the block.
-//   The workgroup walks the query block's key-block list; K and V tiles are
-//   staged in LDS as [token][channel] rows, in half tiles of 64 keys.
+//   The workgroup walks the query block's key-block list in units of 128
+//   keys; K and V tiles are staged in LDS as [token][channel] rows, in half
+//   tiles of 64 keys. (Query blocks of 64 tokens and key blocks of other
+//   sizes are described at the kernel.)
 //
 // Math per key block and wave (bf16 MFMA 32x32x16, fp32 accumulate)
 //   S^T = K Q^T     4 key sub-tiles x 8 channel steps = 32 MFMA. Q^T stays in
