@@ -168,8 +168,8 @@ bsa_status bsa_attention_lse(const bsa_problem* problem, const void* q, const vo
                              size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace bsa_attention_bwd needs: 1 KB of per-query
- * statistics per block and a bit mask of Nb x Nb bits per (batch, head),
- * each part rounded up to 256 bytes. Returns 0 on invalid arguments. */
+ * statistics per query block and a bit mask of Nk x Nb bits per (batch,
+ * head), each part rounded up to 256 bytes. Returns 0 on invalid arguments. */
 size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
 
 /* Backward of bsa_attention with the key-block selection held fixed (the
@@ -195,8 +195,8 @@ size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
  * P is recomputed in fp32 from lse; the products run in bf16 with fp32
  * accumulation (P and dS are rounded to bf16 as MFMA operands). No
  * floating-point atomics: results are bit-identical from run to run.
- * Limits: Nb <= 4096 blocks per (batch, head); query blocks of 128 tokens and
- * the key chunk equal to the query chunk (BSA_ERR_UNSUPPORTED otherwise). */
+ * Limits: Nb, Nk <= 4096 blocks per (batch, head); query blocks of 128
+ * tokens and key blocks of 128 to 1024 tokens (BSA_ERR_UNSUPPORTED otherwise). */
 bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const void* k,
                              const void* v, const void* o, const void* dout, const float* lse,
                              const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* dq,

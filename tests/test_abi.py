@@ -251,7 +251,7 @@ def test_key_chunk_checks():
     assert _select(_problem(key_chunk=(4, 4, 64)), sp) == UNSUPPORTED    # 80 % 64 != 0
     assert _select(_problem(key_chunk=(8, 4, 8), cond_frames=4), sp) == INVALID
     assert _select(_problem(T=4 * 100, key_chunk=(2, 4, 8)), sp) == UNSUPPORTED  # 24,000 key blocks
-    assert _bwd(_problem(key_chunk=(4, 8, 8))) == UNSUPPORTED
+    assert _bwd(_problem(key_chunk=(2, 4, 8))) == UNSUPPORTED   # 64-token key blocks
     assert B.attention_bwd_workspace_bytes(_problem(key_chunk=(4, 8, 8))) > 0
 
 

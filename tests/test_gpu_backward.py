@@ -145,8 +145,9 @@ def oracle_selection(problem, params, q, k):
 
 
 def _case(T, H, W, heads, k_sel, batch=1, chunk=(4, 4, 8), kind="iid", seed=0, cond_frames=0,
-          params=None):
-    problem = Problem.make(T, H, W, heads, batch=batch, chunk=chunk, cond_frames=cond_frames)
+          params=None, key_chunk=None):
+    problem = Problem.make(T, H, W, heads, batch=batch, chunk=chunk, cond_frames=cond_frames,
+                           key_chunk=key_chunk)
     params = params or SelectParams.topk(k_sel)
     q, k, v = make_qkv(T, H, W, heads, batch=batch, kind=kind, seed=seed)
     do = make_grad(T, H, W, heads, batch=batch, seed=seed)
@@ -184,6 +185,14 @@ def test_batch_two_three_heads():
 def test_block_causal_cdf():
     _case(16, 16, 16, 2, 0, kind="field", seed=13, cond_frames=4,
           params=SelectParams.cdf(0.9, 2, 12))
+
+
+@pytest.mark.parametrize("key_chunk,k_sel,cond", [((4, 8, 8), 3, 0), ((8, 8, 16), 2, 0),
+                                                  ((4, 8, 8), 4, 4)])
+def test_key_chunks(key_chunk, k_sel, cond):
+    """Key blocks of 256 and 1024 tokens (walked in 128-key units by dQ, one
+    dK/dV workgroup per unit), with and without condition frames."""
+    _case(8, 16, 32, 2, k_sel, kind="field", seed=19, cond_frames=cond, key_chunk=key_chunk)
 
 
 def test_many_blocks_one_key_block_popular():

@@ -267,15 +267,15 @@ struct BwdLayout {
   int nbw;
 };
 
-// Backward workspace: per (batch*head, block) 128 values lse*log2(e) and 128
-// values D (fp32), then the key-block x query-block bit mask (nb rows of
-// ceil(nb/32) words per batch*head).
+// Backward workspace: per (batch*head, query block) 128 values lse*log2(e)
+// and 128 values D (fp32), then the key-block x query-block bit mask (nbk
+// rows of ceil(nb/32) words per batch*head).
 BwdLayout bwd_layout(const bsa::Geom& g) {
   BwdLayout L;
   L.nbw = (g.nb + 31) / 32;
   L.stats = 0;
   L.mask = align_up((size_t)g.bh * g.nb * 2 * bsa::kBlockTokens * sizeof(float));
-  L.total = L.mask + align_up((size_t)g.bh * g.nb * L.nbw * sizeof(uint32_t));
+  L.total = L.mask + align_up((size_t)g.bh * g.nbk * L.nbw * sizeof(uint32_t));
   return L;
 }
 
@@ -387,9 +387,12 @@ bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const vo
   if (c.g.nb > kMaxBlocks)
     return fail(BSA_ERR_UNSUPPORTED, "%d blocks per head: the backward supports at most %d",
                 c.g.nb, kMaxBlocks);
-  if (c.g.nq != bsa::kBlockTokens || c.g.ctk != c.g.ct || c.g.chk != c.g.ch || c.g.cwk != c.g.cw)
+  if (c.g.nq != bsa::kBlockTokens || c.g.nk < bsa::kBlockTokens)
     return fail(BSA_ERR_UNSUPPORTED,
-                "the backward needs 128-token query blocks and the key chunk to be the query chunk");
+                "the backward needs query blocks of 128 tokens and key blocks of 128 to 1024");
+  if (c.g.nbk > kMaxBlocks)
+    return fail(BSA_ERR_UNSUPPORTED, "%d key blocks per head: the backward supports at most %d",
+                c.g.nbk, kMaxBlocks);
   const void* ins[6] = {q, k, v, o, dout, lse};
   void* outs[3] = {dq, dk, dv};
   for (const void* p : ins)

@@ -88,12 +88,15 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Geom g, int nbw,
     const float l = lse[(size_t)bh * g.S + tok];
     st[j] = (l == -INFINITY) ? INFINITY : l * kLog2e;
   }
-  if (t < nbw) mask[((size_t)bh * g.nb + blk) * nbw + t] = 0u;
+  // Mask rows are per key block (nbk of them); query block blk clears rows
+  // blk, blk + nb, ...
+  for (int kb = blk; kb < g.nbk; kb += g.nb)
+    if (t < nbw) mask[((size_t)bh * g.nbk + kb) * nbw + t] = 0u;
 }
 
 // ---------------------------------------------------------------- mask ---
 // Wave w of workgroup x handles query block 4x + w: every valid id kb of its
-// list sets bit qb of mask row kb. Ids outside [0, nb) are skipped and the
+// list sets bit qb of mask row kb. Ids outside [0, nbk) are skipped and the
 // count is clamped to [0, stride], as in the forward.
 __global__ __launch_bounds__(kThreads) void bwd_mask_kernel(Geom g, int nbw, int stride,
                                                             const int32_t* __restrict__ idx,
@@ -108,8 +111,8 @@ __global__ __launch_bounds__(kThreads) void bwd_mask_kernel(Geom g, int nbw, int
   const uint32_t bit = 1u << (qb & 31);
   for (int p = lane; p < count; p += 64) {
     const int kb = idx[row * stride + p];
-    if (kb >= 0 && kb < g.nb)
-      atomicOr(&mask[((size_t)bh * g.nb + kb) * nbw + (qb >> 5)], bit);
+    if (kb >= 0 && kb < g.nbk)
+      atomicOr(&mask[((size_t)bh * g.nbk + kb) * nbw + (qb >> 5)], bit);
   }
 }
 
@@ -142,8 +145,9 @@ struct TileLanes {
   int ta;
   // Direct-to-LDS tile load i (i = 0..3) of wave w covers rows 16w + 4i .. +3;
   // lane L writes physical chunk L % 16 of row 16w + 4i + L / 16 and fetches
-  // global byte (row token)*256 + (ld ^ 16i), see load_tile.
-  uint32_t ld;
+  // global byte (row token)*256 + (ld ^ 16i), see load_tile; ldk is the same
+  // for key tiles (slot offsets of the key chunk).
+  uint32_t ld, ldk;
 };
 
 __device__ __forceinline__ TileLanes tile_lanes(const Geom& g, int w, int lane) {
@@ -168,6 +172,8 @@ __device__ __forceinline__ TileLanes tile_lanes(const Geom& g, int w, int lane) 
   const int r = lane >> 4;
   t.ld = (uint32_t)slot_offset(g, kRowsPerWave * w + r) * (kHeadDim * 2) +
          (uint32_t)(((lane & 15) ^ (r << 2)) << 4);
+  t.ldk = (uint32_t)key_slot_offset(g, kRowsPerWave * w + r) * (kHeadDim * 2) +
+          (uint32_t)(((lane & 15) ^ (r << 2)) << 4);
   return t;
 }
 
@@ -182,6 +188,21 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, __amdgpu_buffer_rsr
     const uint32_t row_s = (uint32_t)slot_offset(a.g, 4 * i) * (kHeadDim * 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 1024), 16,
                                              tl.ld ^ (uint32_t)(16 * i), base + row_s, 0, 0);
+  }
+}
+
+// The same for a 128-key unit of a key block: `base_tok` is the token of the
+// unit's first slot; the rows follow the key chunk.
+__device__ __forceinline__ void load_key_tile(const AttnArgs& a, __amdgpu_buffer_rsrc_t rs,
+                                              const TileLanes& tl, int w, int base_tok,
+                                              bf16_bits* tile) {
+  const uint32_t base = (uint32_t)base_tok * (kHeadDim * 2);
+  char* dst = reinterpret_cast<char*>(tile) + kRowsPerWave * w * 256;
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave / 4; ++i) {
+    const uint32_t row_s = (uint32_t)key_slot_offset(a.g, 4 * i) * (kHeadDim * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 1024), 16,
+                                             tl.ldk ^ (uint32_t)(16 * i), base + row_s, 0, 0);
   }
 }
 
@@ -291,10 +312,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   auto next_valid = [&](int from) __attribute__((always_inline)) {
     while (from < count) {
       const int kb = list[from];
-      if (kb >= 0 && kb < g.nb) break;
+      if (kb >= 0 && kb < g.nbk) break;
       ++from;
     }
     return from;
+  };
+  // Key blocks of 128 * 2^unit_shift tokens are walked in units of 128 keys:
+  // position `pos` of the list, unit `sub` of that key block.
+  struct Unit {
+    int pos, sub;
+  };
+  auto next_unit = [&](Unit c) __attribute__((always_inline)) -> Unit {
+    if (c.sub + 1 < (1 << a.unit_shift)) return {c.pos, c.sub + 1};
+    return {next_valid(c.pos + 1), 0};
+  };
+  auto unit_tok = [&](Unit c) __attribute__((always_inline)) -> int {
+    return key_block_origin(a, list[c.pos]) + key_slot_offset(g, c.sub * kBlockTokens);
   };
 
   f32x16 dq[4];
@@ -348,11 +381,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   };
 
   auto run = [&](auto khc) __attribute__((always_inline)) {
-    int cur = next_valid(0);
-    if (cur >= count) return;
-    load_tile(a, krs, tl, w, list[cur], k0s);
-    load_tile(a, vrs, tl, w, list[cur], v0s);
-    int nxt = next_valid(cur + 1);
+    Unit cur = {next_valid(0), 0};
+    if (cur.pos >= count) return;
+    load_key_tile(a, krs, tl, w, unit_tok(cur), k0s);
+    load_key_tile(a, vrs, tl, w, unit_tok(cur), v0s);
+    Unit nxt = next_unit(cur);
     auto step = [&](auto bc) __attribute__((always_inline)) -> bool {
       constexpr int b = decltype(bc)::value;
       bf16_bits* kt = b == 0 ? k0s : k1s;
@@ -363,14 +396,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
       // everyone's are, and everyone has finished reading the other buffer.
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       workgroup_barrier();
-      if (nxt < count) {
-        load_tile(a, krs, tl, w, list[nxt], kn);
-        load_tile(a, vrs, tl, w, list[nxt], vn);
+      if (nxt.pos < count) {
+        load_key_tile(a, krs, tl, w, unit_tok(nxt), kn);
+        load_key_tile(a, vrs, tl, w, unit_tok(nxt), vn);
       }
       compute(khc, reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt));
-      if (nxt >= count) return false;
+      if (nxt.pos >= count) return false;
       cur = nxt;
-      nxt = next_valid(cur + 1);
+      nxt = next_unit(cur);
       return true;
     };
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
@@ -429,9 +462,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char xch[4 * 2 * 2048];  // [key slice][slot][2 KB]
   __shared__ uint32_t mrow[kBlockTokens];
   const Geom& g = a.g;
-  int pair, kb;
-  xcd_block(a, pair, kb);
-  if (kb >= g.nb) return;
+  int pair, unit;
+  xcd_block(a, pair, unit);
+  // Unit `sub` (128 keys) of key block kb.
+  const int kb = unit >> a.unit_shift;
+  const int sub = unit & ((1 << a.unit_shift) - 1);
+  if (kb >= g.nbk) return;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -452,7 +488,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const TileLanes tl = tile_lanes(g, w, lane);
 
   // P role keeps K of its keys (B operand of S), dS role keeps V (of dP).
-  const int ktok = block_origin(a, kb) + slot_offset(g, 32 * ks + n);
+  const int ktok = key_block_origin(a, kb) + key_slot_offset(g, sub * kBlockTokens + 32 * ks + n);
   bf16x8 xf[8];
   {
     const bf16_bits* src = ds_role ? vp : kp;
@@ -461,7 +497,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       xf[s] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4*>(src + hoff + (size_t)ktok * kHeadDim + 16 * s + 8 * gs));
   }
-  if (t < nbw) mrow[t] = mask[((size_t)pair * g.nb + kb) * nbw + t];
+  if (t < nbw) mrow[t] = mask[((size_t)pair * g.nbk + kb) * nbw + t];
   __syncthreads();
   auto next_set = [&](int from) __attribute__((always_inline)) -> int {
     int wd = from >> 5;
@@ -597,7 +633,11 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
                      idx, cnt, dq);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel, grid, dim3(kBwdThreads), 0, stream, a, nbw, q, k, v, dout,
+  // dK/dV: one workgroup per 128-key unit of every key block.
+  AttnArgs au = a;
+  au.nq8 = ((g.nbk << a.unit_shift) + 7) / 8 * 8;
+  const dim3 grid_u((unsigned)((size_t)g.bh * au.nq8));
+  hipLaunchKernelGGL(bwd_dkdv_kernel, grid_u, dim3(kBwdThreads), 0, stream, au, nbw, q, k, v, dout,
                      stats, mask, dk, dv);
   return hipGetLastError();
 }
