@@ -26,9 +26,15 @@ Technical Report and four write-ups about it):
 Readings where the pages are silent or inconsistent (each one is also listed
 with its reason in the design notes of the repository):
 
-* Block shape: (t, h, w) = (4, 4, 8) as in [Notes]; any shape whose grid
-  divides the latent grid is accepted here.
-* Pooling index: 0-based, block b covers block-ordered tokens b*n .. b*n+n-1.
+* Block shape: (t, h, w) = (4, 4, 8) as in [Notes]; any positive shape is
+  accepted here.
+* Pooling index: 0-based, block b covers block-ordered slots b*n .. b*n+n-1.
+* Partial blocks: [DeepDive] "3D block partitioning" counts blocks with
+  ceilings (N_T = ceil(T / t), ...). A block at the far edge of a grid that
+  its chunk does not divide holds only the tokens of its box that lie inside
+  the grid; there are no padding tokens. Its pooled vector is the mean of
+  the tokens it holds (the pooling equation's 1/n with n that block's token
+  count), and a query block that selects it attends to those tokens only.
 * Mask: additive -inf on non-selected keys (the prose of [DeepDive]), not a
   multiplicative (.) M.
 * Top-k ranks pooled scores (softmax is monotone, so ranking P is the same);
@@ -77,6 +83,7 @@ __all__ = [
     "SelectParams",
     "bf16_bits_to_f64",
     "block_token_order",
+    "block_tokens",
     "pool_blocks",
     "pooled_scores",
     "allowed_key_blocks",
@@ -92,6 +99,10 @@ __all__ = [
     "backward_head",
     "key_geometry",
 ]
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
 
 
 @dataclass(frozen=True)
@@ -120,13 +131,9 @@ class Geometry:
         for name in ("T", "H", "W", "ct", "ch", "cw"):
             if getattr(self, name) <= 0:
                 raise ValueError(f"{name} must be positive")
-        if self.T % self.ct or self.H % self.ch or self.W % self.cw:
-            raise ValueError("latent grid must be divisible by the chunk shape")
         if (self.ctk, self.chk, self.cwk) != (0, 0, 0):
             if min(self.ctk, self.chk, self.cwk) <= 0:
                 raise ValueError("key chunk extents must all be positive (or all 0)")
-            if self.T % self.ctk or self.H % self.chk or self.W % self.cwk:
-                raise ValueError("latent grid must be divisible by the key chunk shape")
         if self.cond_frames < 0 or self.cond_frames % self.ct or (
             self.cond_frames and self.cond_frames >= self.T
         ):
@@ -149,13 +156,13 @@ class Geometry:
     @property
     def num_key_blocks(self) -> int:
         a, b, c = self.key_chunk
-        return (self.T // a) * (self.H // b) * (self.W // c)
+        return _ceil_div(self.T, a) * _ceil_div(self.H, b) * _ceil_div(self.W, c)
 
     @property
     def cond_key_blocks(self) -> int:
         """Key blocks made of condition tokens (the first ones in key-block order)."""
         a, b, c = self.key_chunk
-        return (self.cond_frames // a) * (self.H // b) * (self.W // c)
+        return (self.cond_frames // a) * _ceil_div(self.H, b) * _ceil_div(self.W, c)
 
     @property
     def n(self) -> int:
@@ -163,15 +170,15 @@ class Geometry:
 
     @property
     def nT(self) -> int:
-        return self.T // self.ct
+        return _ceil_div(self.T, self.ct)
 
     @property
     def nH(self) -> int:
-        return self.H // self.ch
+        return _ceil_div(self.H, self.ch)
 
     @property
     def nW(self) -> int:
-        return self.W // self.cw
+        return _ceil_div(self.W, self.cw)
 
     @property
     def num_blocks(self) -> int:
@@ -230,12 +237,14 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def block_token_order(g: Geometry) -> np.ndarray:
-    """perm[i*n + j] = latent-order token index of slot j of block i.
+    """perm[i*n + j] = latent-order token index of slot j of block i, or -1
+    where slot j of a partial block lies outside the grid.
 
     [DeepDive] "3D block partitioning": tokens of a block are contiguous with
-    intra-block order [t, h, w]; blocks are in [N_T, N_H, N_W] order.
+    intra-block order [t, h, w]; blocks are in [N_T, N_H, N_W] order, with
+    N_T = ceil(T / t) and so on.
     """
-    perm = np.empty(g.seq_len, dtype=np.int64)
+    perm = np.full(g.num_blocks * g.n, -1, dtype=np.int64)
     pos = 0
     for bt in range(g.nT):
         for bh in range(g.nH):
@@ -245,17 +254,32 @@ def block_token_order(g: Geometry) -> np.ndarray:
                         t = bt * g.ct + it
                         h = bh * g.ch + ih
                         w0 = bw * g.cw
-                        row = (t * g.H + h) * g.W + w0
-                        perm[pos : pos + g.cw] = np.arange(row, row + g.cw)
+                        if t < g.T and h < g.H:
+                            run = min(g.cw, g.W - w0)
+                            row = (t * g.H + h) * g.W + w0
+                            perm[pos : pos + run] = np.arange(row, row + run)
                         pos += g.cw
     return perm
 
 
+def block_tokens(perm: np.ndarray, i: int, n: int) -> np.ndarray:
+    """Latent-order tokens of block i in slot order (slots outside the grid
+    left out)."""
+    t = perm[i * n : (i + 1) * n]
+    return t[t >= 0]
+
+
 def pool_blocks(x: np.ndarray, perm: np.ndarray, n: int) -> np.ndarray:
-    """Mean of each block's n tokens: X_pool[b] = (1/n) sum_j X[b*n + j] in
-    block order ([DeepDive] "Pooled block similarity computation")."""
-    xb = np.asarray(x, dtype=np.float64)[perm]
-    return xb.reshape(-1, n, xb.shape[-1]).mean(axis=1)
+    """Mean of each block's tokens: X_pool[b] = (1/n_b) sum_j X[b*n + j] in
+    block order, over the n_b slots of block b that lie inside the grid (all
+    n of them unless b is partial) ([DeepDive] "Pooled block similarity
+    computation")."""
+    x = np.asarray(x, dtype=np.float64)
+    nblk = perm.shape[0] // n
+    out = np.empty((nblk, x.shape[-1]))
+    for b in range(nblk):
+        out[b] = x[block_tokens(perm, b, n)].mean(axis=0)
+    return out
 
 
 def pooled_scores(q_pool: np.ndarray, k_pool: np.ndarray, scale: float) -> np.ndarray:
@@ -361,15 +385,17 @@ def attend_query_block(
     non-selected keys at -inf) V. Keys outside the selected blocks contribute
     exp(-inf) = 0, so softmax over the gathered keys is the same thing.
     ``perm`` / ``kperm`` are the query and key block orders (computed when
-    not given). Returns [n, d] float64 rows in the block's slot order.
+    not given). Returns float64 rows for the block's tokens in slot order
+    ([n, d] unless the block is partial; a partial key block contributes its
+    tokens inside the grid only).
     """
     if perm is None:
         perm = block_token_order(g)
     if kperm is None:
         kperm = block_token_order(key_geometry(g))
     n, nk = g.n, g.nk
-    qi = np.asarray(q, dtype=np.float64)[perm[i * n : (i + 1) * n]]
-    tok = np.concatenate([kperm[j * nk : (j + 1) * nk] for j in key_blocks])
+    qi = np.asarray(q, dtype=np.float64)[block_tokens(perm, i, n)]
+    tok = np.concatenate([block_tokens(kperm, j, nk) for j in key_blocks])
     ks = np.asarray(k, dtype=np.float64)[tok]
     vs = np.asarray(v, dtype=np.float64)[tok]
     logits = (qi @ ks.T) * scale
@@ -396,7 +422,7 @@ def bsa_head(
     n = g.n
     for i in range(g.num_blocks):
         sel = idx[i, : cnt[i]]
-        out[perm[i * n : (i + 1) * n]] = attend_query_block(q, k, v, g, i, sel, scale, perm, kperm)
+        out[block_tokens(perm, i, n)] = attend_query_block(q, k, v, g, i, sel, scale, perm, kperm)
     return out, idx, cnt, scores
 
 
@@ -409,7 +435,7 @@ def dense_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Geometry, scale: 
     n = g.n
     for i in range(g.num_blocks):
         na = allowed_key_blocks(g, i)
-        out[perm[i * n : (i + 1) * n]] = attend_query_block(
+        out[block_tokens(perm, i, n)] = attend_query_block(
             q, k, v, g, i, range(na), scale, perm, kperm
         )
     return out
@@ -417,8 +443,8 @@ def dense_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: Geometry, scale: 
 
 def _gathered(q, k, v, g, i, key_blocks, perm, kperm):
     n, nk = g.n, g.nk
-    qt = perm[i * n : (i + 1) * n]
-    kt = np.concatenate([kperm[j * nk : (j + 1) * nk] for j in key_blocks])
+    qt = block_tokens(perm, i, n)
+    kt = np.concatenate([block_tokens(kperm, j, nk) for j in key_blocks])
     return qt, kt
 
 

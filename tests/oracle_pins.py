@@ -478,7 +478,7 @@ def _key_block_of_token(g):
     and the key chunk."""
     a, b, c = g.key_chunk
     t, h, w = _coords(g, np.arange(g.seq_len))
-    return ((t // a) * (g.H // b) + (h // b)) * (g.W // c) + (w // c)
+    return ((t // a) * -(-g.H // b) + (h // b)) * -(-g.W // c) + (w // c)
 
 
 # Query chunk [4, 4, 8] (128 tokens) with key chunks of 64, 256 and 1024
@@ -589,6 +589,146 @@ def pin_key_chunk_backward_autograd():
         assert np.abs(mine - ref.numpy()).max() < 1e-10
 
 
+# ------------------------------------------------------ partial block pins ---
+# Grids that a chunk does not divide: [DeepDive] "3D block partitioning"
+# counts blocks with ceilings, so the last block along such an axis is cut
+# at the grid's edge and holds fewer tokens.
+_PARTIAL_CASES = (
+    # 2 x 2 x 2 blocks of [4, 4, 8], every axis cut.
+    (O.Geometry(6, 6, 12), O.SelectParams("topk", k=3)),
+    # t and h cut, condition frames.
+    (O.Geometry(10, 7, 16, cond_frames=4), O.SelectParams("cdf", p=0.7, k_min=1, k_max=5)),
+    # 64-token query blocks and 256-token key blocks, both cut along t and w.
+    (O.Geometry(5, 8, 13, 2, 4, 8, ctk=4, chk=4, cwk=16), O.SelectParams("topk", k=4)),
+    # 64-token key blocks cut along h and w.
+    (O.Geometry(6, 9, 20, ctk=2, chk=4, cwk=8), O.SelectParams("topk", k=6)),
+)
+
+
+def pin_partial_block_order():
+    """Partial grids: the slots inside the grid hold every token once; each
+    token sits in the block and slot that its coordinates give, and the
+    remaining slots (outside the grid) are marked -1."""
+    for g, _ in _PARTIAL_CASES:
+        for gg in (g, O.key_geometry(g)):
+            perm = O.block_token_order(gg)
+            assert perm.shape == (gg.num_blocks * gg.n,)
+            valid = perm >= 0
+            assert np.array_equal(np.sort(perm[valid]), np.arange(gg.seq_len)), "not a bijection"
+            pos = np.nonzero(valid)[0]
+            tok = perm[valid]
+            t, h, w = _coords(gg, tok)
+            assert np.array_equal(pos // gg.n, _block_of_token(gg)[tok]), "token in the wrong block"
+            slot = ((t % gg.ct) * gg.ch + (h % gg.ch)) * gg.cw + (w % gg.cw)
+            assert np.array_equal(pos % gg.n, slot), "token in the wrong slot"
+            assert int((~valid).sum()) == gg.num_blocks * gg.n - gg.seq_len
+
+
+def pin_partial_mask_formula():
+    """Partial grids: gathered attention equals the token-level mask formula,
+    with every token's query and key block from its coordinates."""
+    rng = np.random.default_rng(41)
+    for g, p in _PARTIAL_CASES:
+        q, k, v = _rand(rng, g)
+        scale = 1 / np.sqrt(q.shape[1])
+        out, idx, cnt, _ = O.bsa_head(q, k, v, g, p, scale)
+        qb, kb = _block_of_token(g), _key_block_of_token(g)
+        sel = np.zeros((g.num_blocks, g.num_key_blocks), dtype=bool)
+        for i in range(g.num_blocks):
+            sel[i, idx[i, : cnt[i]]] = True
+        ref = _textbook_attention(q, k, v, scale, sel[qb[:, None], kb[None, :]])
+        assert np.abs(out - ref).max() < 1e-12, "gathered attention != masked attention"
+        dense_ref = np.zeros_like(q)
+        cond = _coords(g, np.arange(g.seq_len))[0] < g.cond_frames
+        if cond.any():
+            dense_ref[cond] = _textbook_attention(q[cond], k[cond], v[cond], scale)
+        dense_ref[~cond] = _textbook_attention(q[~cond], k, v, scale)
+        assert np.abs(O.dense_head(q, k, v, g, scale) - dense_ref).max() < 1e-12
+
+
+def pin_partial_pooled_bruteforce():
+    """Partial grids: pooled scores from coordinate accumulation divided by
+    each block's own token count."""
+    rng = np.random.default_rng(42)
+    for g, _ in _PARTIAL_CASES:
+        q, k, _ = _rand(rng, g)
+        scale = 0.31
+        qb, kb = _block_of_token(g), _key_block_of_token(g)
+        qs = np.zeros((g.num_blocks, q.shape[1]))
+        ks = np.zeros((g.num_key_blocks, k.shape[1]))
+        np.add.at(qs, qb, q)
+        np.add.at(ks, kb, k)
+        qs /= np.bincount(qb, minlength=g.num_blocks)[:, None]
+        ks /= np.bincount(kb, minlength=g.num_key_blocks)[:, None]
+        s_ref = qs @ ks.T * scale
+        _, _, scores = O.select_head(q, k, g, O.SelectParams("topk", k=1), scale)
+        for i in range(g.num_blocks):
+            na = O.allowed_key_blocks(g, i)
+            assert np.abs(scores[i, :na] - s_ref[i, :na]).max() < 1e-12, "pooled score"
+
+
+def pin_partial_closed_forms():
+    """Partial grids, closed forms. (1) A channel holding each token's frame
+    index pools to bt*t + (r - 1)/2 for a block whose box keeps r frames of
+    the grid (the mean of r consecutive integers), whatever its h and w cut.
+    (2) Q = 0 ties every pooled score, so top-k keeps key blocks 0..k-1 and
+    every query's output is the mean of V over exactly the tokens of those
+    blocks."""
+    rng = np.random.default_rng(43)
+    for g, _ in _PARTIAL_CASES:
+        t = _coords(g, np.arange(g.seq_len))[0].astype(np.float64)
+        x = np.zeros((g.seq_len, 2))
+        x[:, 0] = t
+        x[:, 1] = 1.0
+        pooled = O.pool_blocks(x, O.block_token_order(g), g.n)
+        for i in range(g.num_blocks):
+            bt = i // (g.nH * g.nW)
+            r = min(g.ct, g.T - bt * g.ct)
+            assert abs(pooled[i, 0] - (bt * g.ct + (r - 1) / 2)) < 1e-12
+            assert abs(pooled[i, 1] - 1.0) < 1e-12
+        _, k, v = _rand(rng, g)
+        q = np.zeros_like(k)
+        kk = 3
+        out, idx, cnt, _ = O.bsa_head(q, k, v, g, O.SelectParams("topk", k=kk), 0.2)
+        kb = _key_block_of_token(g)
+        for i in range(g.num_blocks):
+            na = O.allowed_key_blocks(g, i)
+            want = list(range(min(kk, na)))
+            assert idx[i, : cnt[i]].tolist() == want
+            mean_v = v[np.isin(kb, want)].mean(axis=0)
+            assert np.abs(out[_block_of_token(g) == i] - mean_v).max() < 1e-12
+
+
+def pin_partial_backward_autograd():
+    """Partial grids: backward_head equals torch float64 autograd of the
+    token-level mask formula, for random selections."""
+    import torch
+
+    rng = np.random.default_rng(44)
+    for g, _ in _PARTIAL_CASES:
+        q, k, v, do = (rng.standard_normal((g.seq_len, 8)) for _ in range(4))
+        nb, nk = g.num_blocks, g.num_key_blocks
+        stride = min(3, nk)
+        idx = np.full((nb, stride), -1)
+        cnt = np.zeros(nb, dtype=np.int64)
+        for i in range(nb):
+            c = int(rng.integers(1, stride + 1))
+            idx[i, :c] = np.sort(rng.choice(nk, size=c, replace=False))
+            cnt[i] = c
+        scale = 0.33
+        dq, dk, dv = O.backward_head(q, k, v, do, g, idx, cnt, scale)
+        sel = np.zeros((nb, nk), dtype=bool)
+        for i in range(nb):
+            sel[i, idx[i, : cnt[i]]] = True
+        allowed = torch.tensor(sel[_block_of_token(g)[:, None], _key_block_of_token(g)[None, :]])
+        tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+        logits = ((tq @ tk.T) * scale).masked_fill(~allowed, float("-inf"))
+        out = torch.softmax(logits, dim=1) @ tv
+        (out * torch.tensor(do)).sum().backward()
+        for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            assert np.abs(mine - ref.numpy()).max() < 1e-10
+
+
 ALL_PINS = [
     pin_block_order_geometry,
     pin_handworked_golden,
@@ -614,4 +754,9 @@ ALL_PINS = [
     pin_key_chunk_pooled_bruteforce,
     pin_key_chunk_dense,
     pin_key_chunk_backward_autograd,
+    pin_partial_block_order,
+    pin_partial_mask_formula,
+    pin_partial_pooled_bruteforce,
+    pin_partial_closed_forms,
+    pin_partial_backward_autograd,
 ]

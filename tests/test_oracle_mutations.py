@@ -53,6 +53,36 @@ def _pool_first_token(x, perm, n):
     return xb.reshape(-1, n, xb.shape[-1])[:, 0, :].copy()
 
 
+def _pool_zero_padded(x, perm, n):
+    """Partial blocks padded with zeros and divided by n."""
+    x = np.asarray(x, dtype=np.float64)
+    xb = np.where((perm >= 0)[:, None], x[np.maximum(perm, 0)], 0.0)
+    return xb.reshape(-1, n, x.shape[-1]).sum(axis=1) / n
+
+
+def _tokens_keep_outside(perm, i, n):
+    """Slots outside the grid not dropped (-1 then indexes the last token)."""
+    return perm[i * n : (i + 1) * n]
+
+
+def _attend_zero_padded_keys(q, k, v, g, i, key_blocks, scale, perm=None, kperm=None):
+    """Slots of a partial key block outside the grid attended as zero keys
+    and values."""
+    perm = O.block_token_order(g) if perm is None else perm
+    kperm = O.block_token_order(O.key_geometry(g)) if kperm is None else kperm
+    n, nk = g.n, g.nk
+    qi = np.asarray(q, np.float64)[O.block_tokens(perm, i, n)]
+    tok = np.concatenate([kperm[j * nk : (j + 1) * nk] for j in key_blocks])
+    pad = (tok < 0)[:, None]
+    ks = np.where(pad, 0.0, np.asarray(k, np.float64)[np.maximum(tok, 0)])
+    vs = np.where(pad, 0.0, np.asarray(v, np.float64)[np.maximum(tok, 0)])
+    logits = (qi @ ks.T) * scale
+    logits -= logits.max(axis=1, keepdims=True)
+    w = np.exp(logits)
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ vs
+
+
 def _rank_ties_high(values):
     ids = np.arange(values.shape[0])
     return np.lexsort((-ids, -values))
@@ -139,6 +169,9 @@ MUTANTS = {
     "block order w before h": ("block_token_order", _order_blocks_w_major),
     "pool sums instead of means": ("pool_blocks", _pool_sum),
     "pool takes first token only": ("pool_blocks", _pool_first_token),
+    "partial blocks pooled as zero-padded means": ("pool_blocks", _pool_zero_padded),
+    "slots outside the grid kept": ("block_tokens", _tokens_keep_outside),
+    "partial key blocks padded with zero keys": ("attend_query_block", _attend_zero_padded_keys),
     "ties go to higher ids": ("_rank_order", _rank_ties_high),
     "CDF drops the crossing block": ("select_cdf", _cdf_drop_crossing),
     "CDF ignores k_min/k_max": ("select_cdf", _cdf_no_clamp),
