@@ -27,11 +27,15 @@
  * Tensors. q, k, v, o are bfloat16 [batch, heads, S, head_dim], contiguous,
  *   S = T*H*W tokens in latent order s = (t*H + h)*W + w. Pointers are device
  *   pointers, 16-byte aligned. head_dim must be 128.
- * Blocks. nT = T/ct, nH = H/ch, nW = W/cw; block id
- *   i = (bt*nH + bh)*nW + bw; a query block holds ct*ch*cw = 64 or 128 tokens.
- *   The grid must divide by the chunk shape. Key blocks are numbered the same way
- *   with the key chunk (ctk, chk, cwk) when one is given (Nk of them), else
- *   they are the query blocks (Nk = Nb).
+ * Blocks. nT = ceil(T/ct), nH = ceil(H/ch), nW = ceil(W/cw) (section "Block
+ *   Sparse Attention", "3D block partitioning"); block id
+ *   i = (bt*nH + bh)*nW + bw; a query block holds ct*ch*cw = 64 or 128 slots.
+ *   Where a chunk does not divide the grid, the last block along that axis is
+ *   partial: it holds only the tokens of its box inside the grid, is pooled
+ *   over those tokens, and a query block that selects it attends to those
+ *   tokens only. Key blocks are numbered the same way with the key chunk
+ *   (ctk, chk, cwk) when one is given (Nk of them), else they are the query
+ *   blocks (Nk = Nb).
  * Ownership. The caller owns every buffer. The library never allocates,
  *   frees, or synchronises; all work is enqueued on `stream` (a hipStream_t;
  *   NULL is the default stream). Workspace contents do not carry over from
@@ -74,14 +78,13 @@ typedef struct bsa_problem {
   int32_t heads;       /* >= 0 */
   int32_t head_dim;    /* must be 128 */
   int32_t T, H, W;     /* latent grid, each > 0; T*H*W < 2^24 */
-  int32_t ct, ch, cw;  /* query chunk shape; ct*ch*cw must be 64 or 128 and divide
-                          the grid */
+  int32_t ct, ch, cw;  /* query chunk shape; ct*ch*cw must be 64 or 128 */
   int32_t cond_frames; /* 0: no block-causal mask; else a multiple of ct (and of
                           ctk), < T */
   float scale;         /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
   int32_t ctk, chk, cwk; /* key chunk shape; all 0: the same as the query chunk.
                             Otherwise ctk*chk*cwk must be 64, 128, 256, 512 or
-                            1024 and divide the grid ("Implementation details
+                            1024 ("Implementation details
                             and design trade-offs": query blocks of 64-128 and
                             key blocks of 64-1024 tokens). Key-block ids in idx
                             then refer to these blocks. */
@@ -196,7 +199,8 @@ size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
  * accumulation (P and dS are rounded to bf16 as MFMA operands). No
  * floating-point atomics: results are bit-identical from run to run.
  * Limits: Nb, Nk <= 4096 blocks per (batch, head); query blocks of 128
- * tokens and key blocks of 128 to 1024 tokens (BSA_ERR_UNSUPPORTED otherwise). */
+ * tokens and key blocks of 128 to 1024 tokens; a grid that both chunks
+ * divide (no partial blocks) (BSA_ERR_UNSUPPORTED otherwise). */
 bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const void* k,
                              const void* v, const void* o, const void* dout, const float* lse,
                              const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* dq,

@@ -205,7 +205,7 @@ def compare_outputs(out_bits, q_bits, k_bits, v_bits, g, blocks_of_pair, scale, 
         out = []
         for i in by_pair[pair]:
             ref = O.attend_query_block(q, k, v, g, i, blocks_of_pair(pair, i), scale, perm, kperm)
-            got = O.bf16_bits_to_f64(out_bits[b, h][perm[i * n : (i + 1) * n]])
+            got = O.bf16_bits_to_f64(out_bits[b, h][O.block_tokens(perm, i, n)])
             err = np.abs(got - ref)
             out.append((err.max(), err.sum(), err.size, bool(np.isfinite(got).all())))
         return out

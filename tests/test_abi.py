@@ -86,7 +86,6 @@ def _attn(problem, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE, stride=4, o=FAKE 
         (dict(head_dim=0), INVALID),
         (dict(chunk=(2, 4, 4)), UNSUPPORTED),   # 32-token query blocks
         (dict(chunk=(4, 8, 8)), UNSUPPORTED),   # 256-token query blocks
-        (dict(T=57), UNSUPPORTED),
         (dict(cond_frames=3), INVALID),
         (dict(cond_frames=56), INVALID),
         (dict(cond_frames=-4), INVALID),
@@ -235,8 +234,8 @@ def test_lse_forward_rejects_bad_lse():
 
 def test_key_chunk_checks():
     """Key chunk: all 0 or all positive, 64..1024 tokens (powers of two),
-    dividing the grid, condition frames a multiple of ctk; selection limited
-    to 4096 key blocks; the backward needs equal chunks."""
+    condition frames a multiple of ctk; selection limited to 4096 key blocks;
+    the backward needs key blocks of 128 tokens or more."""
     sp = B.SelectParams.topk(4)
     ok = _problem(key_chunk=(4, 8, 8))
     nb, nbk = 1680, 840
@@ -248,7 +247,7 @@ def test_key_chunk_checks():
     assert _select(p, sp) == INVALID
     assert _select(_problem(key_chunk=(2, 2, 8)), sp) == UNSUPPORTED     # 32 tokens
     assert _select(_problem(key_chunk=(8, 16, 16)), sp) == UNSUPPORTED   # 2048 tokens
-    assert _select(_problem(key_chunk=(4, 4, 64)), sp) == UNSUPPORTED    # 80 % 64 != 0
+    assert _select(_problem(key_chunk=(4, 4, 12)), sp) == UNSUPPORTED    # 192 tokens
     assert _select(_problem(key_chunk=(8, 4, 8), cond_frames=4), sp) == INVALID
     assert _select(_problem(T=4 * 100, key_chunk=(2, 4, 8)), sp) == UNSUPPORTED  # 24,000 key blocks
     assert _bwd(_problem(key_chunk=(2, 4, 8))) == UNSUPPORTED   # 64-token key blocks
@@ -286,3 +285,21 @@ def test_query_chunk_of_64():
     assert B.select_workspace_bytes(p, sp) > 0
     assert _bwd(p) == UNSUPPORTED
     assert _select(_problem(T=4 * 64, chunk=(2, 4, 8)), sp) == UNSUPPORTED  # 15,360 key blocks
+
+
+def test_partial_grids():
+    """Grids a chunk does not divide have ceil(T/t) x ceil(H/h) x ceil(W/w)
+    blocks, the last ones cut at the edge: the selection workspace is sized
+    for them, and the backward rejects such grids before any launch."""
+    sp = B.SelectParams.topk(4)
+    p = _problem(T=57)                       # 15 x 12 x 10 blocks, the last t-row cut
+    nb = 15 * 12 * 10
+    assert p.num_blocks == nb
+    sel = B.select_workspace_bytes(p, sp)
+    want = 32 * nb * 512 * 2 + 32 * nb * nb * 4
+    assert want <= sel < want + 3 * 256
+    q = _problem(T=56, key_chunk=(4, 4, 64))   # W = 80: key blocks 4 x 4 x 64, the last w cut
+    assert q.num_key_blocks == 14 * 12 * 2
+    assert B.select_workspace_bytes(q, sp) > 0
+    assert _bwd(p) == UNSUPPORTED
+    assert _bwd(_problem(T=56, H=46)) == UNSUPPORTED

@@ -335,6 +335,72 @@ def test_key_chunks_invalid_ids_and_clamps(key_chunk):
             assert np.all(got == 0.0)
 
 
+# Grids that a chunk does not divide: the pages' block counts are ceilings,
+# so the last block along a cut axis holds only the tokens of its box inside
+# the grid (pooled over those tokens, attended over those tokens).
+@pytest.mark.parametrize("grid,chunk,key_chunk,params,cond", [
+    ((6, 6, 12), (4, 4, 8), None, SelectParams.topk(3), 0),          # every axis cut, 8 blocks
+    ((10, 20, 36), (4, 4, 8), None, SelectParams.topk(7), 0),
+    ((10, 20, 36), (4, 4, 8), None, SelectParams.cdf(0.8, 2, 9), 4),
+    ((10, 20, 36), (4, 4, 8), (2, 4, 8), SelectParams.topk(9), 0),    # 64-token keys
+    ((10, 20, 36), (4, 4, 8), (4, 8, 8), SelectParams.topk(4), 0),    # 256
+    ((10, 20, 36), (4, 4, 8), (8, 8, 16), SelectParams.topk(2), 0),   # 1024: whole units outside
+    ((10, 20, 36), (2, 4, 8), None, SelectParams.topk(5), 0),         # 64-token queries
+    ((10, 20, 36), (2, 4, 8), (4, 4, 8), SelectParams.topk(4), 4),
+    ((10, 20, 36), (4, 2, 8), (2, 4, 8), SelectParams.cdf(0.7, 1, 7), 4),
+    ((16, 30, 52), (4, 4, 8), None, SelectParams.topk(14), 0),        # uneven latent frame
+])
+def test_partial_blocks(grid, chunk, key_chunk, params, cond):
+    """Partial blocks at the grid's far edge: every index row and every
+    output against the oracle."""
+    T, H, W = grid
+    q, k, v = make_qkv(T, H, W, 2, kind="field", seed=37)
+    problem = Problem.make(T, H, W, 2, chunk=chunk, cond_frames=cond, key_chunk=key_chunk)
+    _run_and_compare(problem, params, q, k, v)
+
+
+@pytest.mark.parametrize("chunk", [(4, 4, 8), (2, 4, 8)])
+def test_partial_blocks_dense_and_lse(chunk):
+    """Partial grid with condition frames: dense attention against the
+    oracle's dense (block-causal) attention; bsa_attention_lse writes the same
+    o as bsa_attention and an lse within 2.5e-3 of the oracle's for every
+    token."""
+    import torch
+
+    from video_dit_block_bsa_amd import binding as B
+
+    T, H, W = 10, 20, 36
+    q, k, v = make_qkv(T, H, W, 2, kind="field", seed=41)
+    problem = Problem.make(T, H, W, 2, chunk=chunk, cond_frames=4)
+    g = PT.geometry(problem)
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    o = O.bf16_bits_to_f64(PT.from_device(PT.run_dense(problem, qd, kd, vd)).reshape(q.shape))
+    for h in range(2):
+        ref = O.dense_head(*(O.bf16_bits_to_f64(a[0, h]) for a in (q, k, v)), g, SCALE)
+        err = np.abs(o[0, h] - ref)
+        _log(f"dense partial {chunk} head {h}: max-abs {err.max():.3e}, mean-abs {err.mean():.3e}")
+        assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS
+    params = SelectParams.topk(6)
+    stride = B.index_stride(params)
+    idx_d, cnt_d = PT.run_select(problem, params, qd, kd)
+    o1 = PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, stride)
+    o2 = torch.full_like(qd, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    B.bsa_attention_lse(problem, qd, kd, vd, idx_d, cnt_d, stride, o2, lse,
+                        torch.empty(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    idx = idx_d.cpu().numpy()
+    cnt = cnt_d.cpu().numpy()
+    nb = g.num_blocks
+    for h in range(2):
+        _, lse_r = O.forward_lse_head(*(O.bf16_bits_to_f64(a[0, h]) for a in (q, k, v)), g,
+                                      idx[h * nb:(h + 1) * nb], cnt[h * nb:(h + 1) * nb], SCALE)
+        got = lse[0, h].cpu().numpy()
+        assert np.isfinite(got).all()
+        assert np.abs(got - lse_r).max() <= 2.5e-3
+
+
 @pytest.mark.parametrize("name", ["480p", "720p", "long", "vc", "long_k64", "long_k256", "long_q64"])
 def test_full_size_workload(name):
     """Full-size workloads in the configuration the benchmark times: every

@@ -87,3 +87,31 @@ def test_key_unit_offsets():
                             parts = (slot(128 * u, ct, ch, cw, H, W) + slot(64 * h, ct, ch, cw, H, W)
                                      + slot(16 * w + r, ct, ch, cw, H, W) + slot(4 * i, ct, ch, cw, H, W))
                             assert slot(j, ct, ch, cw, H, W) == parts
+
+
+def test_score_register_key_order():
+    """Accumulator value i of lane (n, gs) of a 32x32 MFMA output holds row
+    8 (i/4) + 4 gs + i%4; the K rows are read in swap23 order, so that value
+    holds key swap23(row) of the sub-tile. The partial-block mask computes
+    that key as 16 (i/8) + 8 gs + i%8 (plus 32 per sub-tile): the two agree,
+    and a lane pair (gs = 0, 1) covers each of the 32 keys once."""
+    for tl in range(2):
+        seen = []
+        for gs in range(2):
+            for i in range(16):
+                row = 8 * (i // 4) + 4 * gs + i % 4
+                key = 32 * tl + swap23(row)
+                assert key == 32 * tl + 16 * (i >> 3) + 8 * gs + (i & 7)
+                seen.append(key)
+        assert sorted(seen) == list(range(32 * tl, 32 * tl + 32))
+
+
+def test_key_slot_bits():
+    """With power-of-two key chunk sides, slot j of a key block has
+    iw = j & (cw-1), ih = (j >> log2 cw) & (ch-1), it = j >> log2(cw ch), the
+    same (t, h, w) offsets as the division form of the slot order."""
+    for ctk, chk, cwk in [(2, 4, 8), (4, 8, 8), (8, 8, 16), (1, 8, 128), (16, 8, 8)]:
+        lw, lh = cwk.bit_length() - 1, chk.bit_length() - 1
+        for j in range(ctk * chk * cwk):
+            assert (j & (cwk - 1), (j >> lw) & (chk - 1), j >> (lw + lh)) == (
+                j % cwk, (j // cwk) % chk, j // (cwk * chk))

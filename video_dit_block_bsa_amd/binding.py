@@ -20,6 +20,10 @@ BSA_TOPK = 0
 BSA_CDF = 1
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
 class Problem(ctypes.Structure):
     """Mirror of ``bsa_problem``."""
 
@@ -61,7 +65,7 @@ class Problem(ctypes.Structure):
     @property
     def num_key_blocks(self):
         a, b, c = self.key_chunk
-        return (self.T // a) * (self.H // b) * (self.W // c)
+        return _cdiv(self.T, a) * _cdiv(self.H, b) * _cdiv(self.W, c)
 
     @property
     def seq_len(self):
@@ -69,7 +73,9 @@ class Problem(ctypes.Structure):
 
     @property
     def num_blocks(self):
-        return (self.T // self.ct) * (self.H // self.ch) * (self.W // self.cw)
+        """Query blocks per (batch, head); a chunk that does not divide the
+        grid leaves partial blocks at its far edge, counted here."""
+        return _cdiv(self.T, self.ct) * _cdiv(self.H, self.ch) * _cdiv(self.W, self.cw)
 
 
 class SelectParams(ctypes.Structure):

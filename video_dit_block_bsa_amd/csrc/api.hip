@@ -51,9 +51,6 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
     return fail(BSA_ERR_UNSUPPORTED,
                 "chunk %dx%dx%d: query blocks of 64 or 128 tokens are implemented", p->ct, p->ch,
                 p->cw);
-  if (p->T % p->ct || p->H % p->ch || p->W % p->cw)
-    return fail(BSA_ERR_UNSUPPORTED, "grid %dx%dx%d is not divisible by chunk %dx%dx%d", p->T,
-                p->H, p->W, p->ct, p->ch, p->cw);
   if (p->cond_frames < 0 || p->cond_frames % p->ct || (p->cond_frames && p->cond_frames >= p->T))
     return fail(BSA_ERR_INVALID_ARG, "cond_frames %d must be a multiple of ct=%d and < T=%d",
                 p->cond_frames, p->ct, p->T);
@@ -70,9 +67,6 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
       return fail(BSA_ERR_UNSUPPORTED,
                   "key chunk %dx%dx%d: key blocks of 64, 128, 256, 512 or 1024 tokens are "
                   "implemented", ctk, chk, cwk);
-    if (p->T % ctk || p->H % chk || p->W % cwk)
-      return fail(BSA_ERR_UNSUPPORTED, "grid %dx%dx%d is not divisible by key chunk %dx%dx%d",
-                  p->T, p->H, p->W, ctk, chk, cwk);
     if (p->cond_frames % ctk)
       return fail(BSA_ERR_INVALID_ARG, "cond_frames %d must be a multiple of ctk=%d",
                   p->cond_frames, ctk);
@@ -84,16 +78,17 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
     return fail(BSA_ERR_UNSUPPORTED, "sequence of %ld tokens is too long (at most 2^24 - 1)", S);
   const long bh = (long)p->batch * p->heads;
   if (bh > (1L << 24)) return fail(BSA_ERR_UNSUPPORTED, "batch*heads = %ld is too large", bh);
-  const long nb = S / nq;
-  const long nhw = (long)(p->H / p->ch) * (p->W / p->cw);
+  // Block counts are ceilings: a chunk that does not divide the grid leaves
+  // partial blocks at its far edge.
+  auto cdiv = [](long a, long b) { return (a + b - 1) / b; };
+  const long nhw = cdiv(p->H, p->ch) * cdiv(p->W, p->cw);
+  const long nb = cdiv(p->T, p->ct) * nhw;
   if ((unsigned long)nb * (unsigned long)nhw >= (1ul << 32))
     return fail(BSA_ERR_UNSUPPORTED, "block grid %ld x %ld is too large", nb, nhw);
-  {
-    const long nbk = S / ((long)ctk * chk * cwk);
-    const long nhwk = (long)(p->H / chk) * (p->W / cwk);
-    if ((unsigned long)nbk * (unsigned long)nhwk >= (1ul << 32))
-      return fail(BSA_ERR_UNSUPPORTED, "key block grid %ld x %ld is too large", nbk, nhwk);
-  }
+  const long nhwk = cdiv(p->H, chk) * cdiv(p->W, cwk);
+  const long nbk = cdiv(p->T, ctk) * nhwk;
+  if ((unsigned long)nbk * (unsigned long)nhwk >= (1ul << 32))
+    return fail(BSA_ERR_UNSUPPORTED, "key block grid %ld x %ld is too large", nbk, nhwk);
   bsa::Geom& g = out->g;
   g.bh = (int)bh;
   g.S = (int)S;
@@ -103,20 +98,24 @@ bsa_status check_problem(const bsa_problem* p, Checked* out) {
   g.ct = p->ct;
   g.ch = p->ch;
   g.cw = p->cw;
-  g.nH = p->H / p->ch;
-  g.nW = p->W / p->cw;
-  g.nb = (int)(S / nq);
+  g.nH = (int)cdiv(p->H, p->ch);
+  g.nW = (int)cdiv(p->W, p->cw);
+  g.nb = (int)nb;
   g.nq = (int)nq;
   g.cond_blocks = (p->cond_frames / p->ct) * g.nH * g.nW;
   g.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
   g.ctk = ctk;
   g.chk = chk;
   g.cwk = cwk;
-  g.nHk = p->H / chk;
-  g.nWk = p->W / cwk;
+  g.nHk = (int)cdiv(p->H, chk);
+  g.nWk = (int)cdiv(p->W, cwk);
   g.nk = ctk * chk * cwk;
-  g.nbk = (int)(S / g.nk);
+  g.nbk = (int)nbk;
   g.cond_kblocks = (p->cond_frames / ctk) * g.nHk * g.nWk;
+  g.partial = (p->T % p->ct || p->H % p->ch || p->W % p->cw || p->T % ctk || p->H % chk ||
+               p->W % cwk)
+                  ? 1
+                  : 0;
   out->empty = (bh == 0);
   return BSA_OK;
 }
@@ -239,7 +238,7 @@ bsa_status select_common(const bsa_problem* problem, const bsa_select_params* pa
   const bsa::bf16_bits* qb = static_cast<const bsa::bf16_bits*>(q);
   const bsa::bf16_bits* kb = static_cast<const bsa::bf16_bits*>(k);
   if (c.g.nq == bsa::kBlockTokens && c.g.nk == bsa::kBlockTokens && c.g.ctk == c.g.ct &&
-      c.g.chk == c.g.ch) {
+      c.g.chk == c.g.ch && !c.g.partial) {
     st = launched(bsa::launch_pool(c.g, qb, kb, qp, kp, row0, s), "pool");
   } else {
     st = launched(bsa::launch_pool_queries(c.g, qb, qp, row0, s), "pool");
@@ -390,6 +389,8 @@ bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const vo
   if (c.g.nq != bsa::kBlockTokens || c.g.nk < bsa::kBlockTokens)
     return fail(BSA_ERR_UNSUPPORTED,
                 "the backward needs query blocks of 128 tokens and key blocks of 128 to 1024");
+  if (c.g.partial)
+    return fail(BSA_ERR_UNSUPPORTED, "the backward needs a grid that both chunks divide");
   if (c.g.nbk > kMaxBlocks)
     return fail(BSA_ERR_UNSUPPORTED, "%d key blocks per head: the backward supports at most %d",
                 c.g.nbk, kMaxBlocks);

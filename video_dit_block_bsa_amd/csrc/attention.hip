@@ -93,6 +93,12 @@ constexpr int kSlots = 5;                               // half-tile ring per wo
 // A unit's slot offsets are those of its first slot plus those of its slot
 // index (power-of-two chunk sides make the offset linear in the index bits).
 //
+// Partial blocks (a chunk that does not divide the grid: "3D block
+// partitioning" counts blocks with ceilings): a query slot outside the grid
+// computes on the block's slot 0 and is never written; the scores of key
+// slots outside the grid are set to -inf, behind a wave-uniform test per key
+// block, so blocks inside the grid cost one scalar comparison.
+//
 // kSplit serves query blocks of 64 tokens: wave w takes queries 32(w%2) ..
 // +31 and key half w/2 (keys 0..63 or 64..127) of every unit, keeps its own
 // running max and sum over its keys, and the two key halves of a query meet
@@ -145,7 +151,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(vp + hoff), (short)0, head_bytes, kBufferWord3);
 
-  const int qtok = block_origin(a, qb) + slot_offset(g, 32 * qh + n);
+  // A query slot of a partial block that lies outside the grid reads slot 0
+  // (always inside) instead, and its row is never written.
+  const bool q_inside = !g.partial || block_slot_valid(g, qb, 32 * qh + n);
+  const int qtok = block_origin(a, qb) + (q_inside ? slot_offset(g, 32 * qh + n) : 0);
   bf16x8 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
@@ -327,6 +336,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
               for (int i = 0; i < 16; ++i) sacc[tt][i] = -INFINITY;
           }
         }
+        if (g.partial) {
+          // Keys of a partial block that lie outside the grid get -inf.
+          // Half h of the unit (keys 64h .. 64h+63) holds slots base .. +63
+          // of key block kb; accumulator value i of this wave's sub-tile tl
+          // of that half is key 32 tl + 16 (i/8) + 8 gs + i%8 of the half.
+          auto mask_half = [&](int h, int kb, int base) {
+            const Extent e = key_block_extent(a, kb);
+            if (e.t == g.ctk && e.h == g.chk && e.w == g.cwk) return;
+            // The lane's offset passes through an empty asm so that nothing
+            // derived from it is hoisted out of the loop (64 live registers).
+            int lb = base + 8 * gs;
+            asm volatile("" : "+v"(lb));
+#pragma unroll
+            for (int tl = 0; tl < 2; ++tl) {
+              const int tt = kSplit ? tl : 2 * h + tl;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int j = lb + 32 * tl + 16 * (i >> 3) + (i & 7);
+                if (!key_slot_inside(a, e, j)) sacc[tt][i] = -INFINITY;
+              }
+            }
+          };
+          if constexpr (kKeyMode == 2) {
+            if (!kSplit || KH == 0) mask_half(0, kb_at(cur.a), 0);
+            if ((!kSplit || KH == 1) && cur.b < count) mask_half(1, kb_at(cur.b), 0);
+          } else {
+            const int base = kKeyMode == 1 ? cur.b * kBlockTokens : 0;
+            if (!kSplit || KH == 0) mask_half(0, kb_at(cur.a), base);
+            if (!kSplit || KH == 1) mask_half(1, kb_at(cur.a), base + kHalfRows);
+          }
+        }
         // Online softmax for this lane's query (both lane halves agree on m2).
         float mx = -INFINITY;
 #pragma unroll
@@ -343,9 +383,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
 #pragma unroll
           for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
         }
-        // In split mode a wave may have seen only masked keys so far (m2 still
-        // -inf): its probabilities are then exp2(-inf - 0) = 0.
-        const float msub = (kSplit && m2 == -INFINITY) ? 0.f : m2;
+        // A wave may have seen only masked keys so far (m2 still -inf: the
+        // empty half of a lone 64-token key block in split mode, or a unit
+        // outside the grid): its probabilities are then exp2(-inf - 0) = 0.
+        const float msub = ((kSplit || g.partial) && m2 == -INFINITY) ? 0.f : m2;
 #pragma unroll
         for (int tt = 0; tt < kT; ++tt) {
 #pragma unroll
@@ -446,6 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     m2 = m;
   }
   const float inv = (l > 0.f) ? 1.0f / l : 0.f;
+  if (!q_inside) return;
   if constexpr (kLse) {
     // sum_j exp(scale * q.k_j) = 2^m2 * l, so lse = (m2 + log2 l) * ln 2.
     if (gs == 0)

@@ -36,6 +36,10 @@ struct Geom {
   int nbk;           // key blocks per (batch, head)
   int nk;            // tokens per key block
   int cond_kblocks;  // leading condition key blocks
+  // Nonzero when a chunk does not divide the grid: block counts are then
+  // ceilings and the last block along a cut axis holds only the tokens of
+  // its box that lie inside the grid.
+  int partial;
 };
 
 // Latent-order token of slot j (0..127) of block i: blocks run in
@@ -63,6 +67,27 @@ __device__ __forceinline__ int key_block_token(const Geom& g, int i, int j) {
   const int ih = r2 % g.chk;
   const int it = r2 / g.chk;
   return ((bt * g.ctk + it) * g.H + bh * g.chk + ih) * g.W + bw * g.cwk + iw;
+}
+
+// Whether slot j (0 .. nq-1) of query block i lies inside the grid.
+__device__ __forceinline__ bool block_slot_valid(const Geom& g, int i, int j) {
+  const int bw = i % g.nW;
+  const int rest = i / g.nW;
+  const int bh = rest % g.nH;
+  const int bt = rest / g.nH;
+  const int r2 = j / g.cw;
+  return bt * g.ct + r2 / g.ch < g.T && bh * g.ch + r2 % g.ch < g.H && bw * g.cw + j % g.cw < g.W;
+}
+
+// Whether slot j (0 .. nk-1) of key block i lies inside the grid.
+__device__ __forceinline__ bool key_slot_valid(const Geom& g, int i, int j) {
+  const int bw = i % g.nWk;
+  const int rest = i / g.nWk;
+  const int bh = rest % g.nHk;
+  const int bt = rest / g.nHk;
+  const int r2 = j / g.cwk;
+  return bt * g.ctk + r2 / g.chk < g.T && bh * g.chk + r2 % g.chk < g.H &&
+         bw * g.cwk + j % g.cwk < g.W;
 }
 
 // Number of leading key blocks query block i may select (block-causal:

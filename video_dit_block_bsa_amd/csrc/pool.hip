@@ -64,12 +64,15 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(Geom g, int blk0, const 
   dst[((size_t)bh * g.nb + blk) * kHeadDim + c] = s * (1.0f / kBlockTokens);
 }
 
-// Pooling of one tensor when the key chunk differs from the query chunk:
+// Pooling of one tensor when the key chunk differs from the query chunk, or
+// when the grid has partial blocks:
 // blocks of n = 64 .. 1024 tokens (query blocks, or key blocks with kKeys).
 // Thread t adds channel chunk t % 16 of the n/16 consecutive slots
 // (t/16)*n/16 ..; the 16 partial sums meet in LDS in a fixed order, as above.
 // Blocks blk0, blk0+1, ... of each (batch, head); pooled row blk goes to row
-// blk of an array of out_rows rows per (batch, head).
+// blk of an array of out_rows rows per (batch, head). A partial block at the
+// grid's edge ("3D block partitioning" counts blocks with ceilings) is the
+// mean of its slots inside the grid; the others are not read.
 template <bool kKeys>
 __global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, int blk0, int out_rows,
                                                             const bf16_bits* __restrict__ x,
@@ -83,6 +86,13 @@ __global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, int blk0, in
   const int n = kKeys ? g.nk : g.nq;
   const int per = n >> 4;  // a multiple of 4
   const size_t head_off = (size_t)bh * g.S * kHeadDim;
+  int count = n;
+  if (g.partial) {
+    const int nw = kKeys ? g.nWk : g.nW, nh = kKeys ? g.nHk : g.nH;
+    const int ct = kKeys ? g.ctk : g.ct, ch = kKeys ? g.chk : g.ch, cw = kKeys ? g.cwk : g.cw;
+    const int bw = blk % nw, bhh = (blk / nw) % nh, bt = blk / (nw * nh);
+    count = min(ct, g.T - bt * ct) * min(ch, g.H - bhh * ch) * min(cw, g.W - bw * cw);
+  }
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -92,7 +102,10 @@ __global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, int blk0, in
     for (int r = 0; r < 4; ++r) {
       const int j = grp * per + r0 + r;
       const int tok = kKeys ? key_block_token(g, blk, j) : block_token(g, blk, j);
-      raw[r] = *reinterpret_cast<const u32x4*>(x + head_off + (size_t)tok * kHeadDim + chunk * 8);
+      if (g.partial && !(kKeys ? key_slot_valid(g, blk, j) : block_slot_valid(g, blk, j)))
+        raw[r] = u32x4{0u, 0u, 0u, 0u};
+      else
+        raw[r] = *reinterpret_cast<const u32x4*>(x + head_off + (size_t)tok * kHeadDim + chunk * 8);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -109,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void pool_one_kernel(Geom g, int blk0, in
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum += part[r][t];
-    xp[((size_t)bh * out_rows + blk) * kHeadDim + t] = sum * (1.0f / (float)n);
+    xp[((size_t)bh * out_rows + blk) * kHeadDim + t] = sum * (1.0f / (float)count);
   }
 }
 

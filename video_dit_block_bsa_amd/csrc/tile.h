@@ -25,6 +25,7 @@ struct AttnArgs {
   uint32_t mag_nwk;   // the same for the key-block grid
   uint32_t mag_nhwk;
   int unit_shift;     // log2 of the 128-key units per key block (key blocks of 256+ tokens)
+  int lcwk, lchk;     // log2 of the key chunk's w and h extents
   float c_log2;       // scale * log2(e)
 };
 
@@ -61,6 +62,27 @@ __device__ __forceinline__ int key_slot_offset(const Geom& g, int j) {
   return ((r2 / g.chk) * g.H + r2 % g.chk) * g.W + iw;
 }
 
+// Extents along t, h and w of key block i's box that lie inside the grid
+// (the chunk's own extents except for a partial block at the far edge).
+struct Extent {
+  int t, h, w;
+};
+__device__ __forceinline__ Extent key_block_extent(const AttnArgs& a, int i) {
+  const Geom& g = a.g;
+  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhwk);
+  const int rem = i - bt * g.nHk * g.nWk;
+  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nwk);
+  const int bw = rem - bh * g.nWk;
+  return {min(g.ctk, g.T - bt * g.ctk), min(g.chk, g.H - bh * g.chk), min(g.cwk, g.W - bw * g.cwk)};
+}
+
+// Whether slot j of a key block with extents e lies inside the grid (key
+// chunk sides are powers of two).
+__device__ __forceinline__ bool key_slot_inside(const AttnArgs& a, const Extent& e, int j) {
+  return (j & (a.g.cwk - 1)) < e.w && ((j >> a.lcwk) & (a.g.chk - 1)) < e.h &&
+         (j >> (a.lcwk + a.lchk)) < e.t;
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -91,6 +113,10 @@ inline AttnArgs make_attn_args(const Geom& g, int stride, int q_begin = 0) {
   a.mag_nhwk = (uint32_t)(0x100000000ull / (uint64_t)(g.nHk * g.nWk) + 1);
   a.unit_shift = 0;
   for (int m = g.nk / 128; m > 1; m >>= 1) ++a.unit_shift;
+  a.lcwk = 0;
+  for (int m = g.cwk; m > 1; m >>= 1) ++a.lcwk;
+  a.lchk = 0;
+  for (int m = g.chk; m > 1; m >>= 1) ++a.lchk;
   a.c_log2 = g.scale * 1.4426950408889634f;
   return a;
 }
