@@ -199,8 +199,8 @@ size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
  * accumulation (P and dS are rounded to bf16 as MFMA operands). No
  * floating-point atomics: results are bit-identical from run to run.
  * Limits: Nb, Nk <= 4096 blocks per (batch, head); query blocks of 128
- * tokens and key blocks of 128 to 1024 tokens; a grid that both chunks
- * divide (no partial blocks) (BSA_ERR_UNSUPPORTED otherwise). */
+ * tokens and key blocks of 128 to 1024 tokens (BSA_ERR_UNSUPPORTED
+ * otherwise). Partial blocks are supported. */
 bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const void* k,
                              const void* v, const void* o, const void* dout, const float* lse,
                              const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* dq,

@@ -16,8 +16,11 @@ bf16 O (relative error 2^-9 per element). dS = P (dP - D) cancels where the
 softmax is peaked (dP - D is small next to D), and dQ = s dS K inherits the
 absolute error s P dD K, which is a larger fraction of a smaller dQ. On the
 smooth-field inputs this doubles to triples the relative error (measured up
-to 0.6% mean, 2.2% max), so dQ takes
-  max <= 4e-2 * max |oracle|,  mean <= 1e-2 * mean |oracle|.
+to 0.6% mean, 2.2% max), and more where blocks are small and the softmax
+sharper: on the 6 x 6 x 12 grid (partial blocks of 16 to 64 tokens) a numpy
+model of exactly these roundings (bf16 P, dS, O and dQ, fp64 otherwise)
+gives 1.04-1.08% mean and 2.7% max against the float64 oracle. dQ takes
+  max <= 4e-2 * max |oracle|,  mean <= 1.5e-2 * mean |oracle|.
 lse: |gpu - oracle| <= 2.5e-3. The forward sums bf16-rounded probabilities,
 each within a relative 2^-9, so the sum and its log are off by at most
 log(1 + 2^-9) = 1.95e-3, plus fp32 rounding of the scores.
@@ -39,7 +42,7 @@ from video_dit_block_bsa_amd.inputs import make_grad, make_qkv, random_block_lis
 pytestmark = pytest.mark.gpu
 
 SCALE = 1.0 / math.sqrt(128)
-TOL = {"dq": (4e-2, 1e-2), "dk": (1.5e-2, 5e-3), "dv": (1.5e-2, 5e-3)}  # (max, mean) relative
+TOL = {"dq": (4e-2, 1.5e-2), "dk": (1.5e-2, 5e-3), "dv": (1.5e-2, 5e-3)}  # (max, mean) relative
 LSE_ABS = 2.5e-3
 
 
@@ -193,6 +196,18 @@ def test_key_chunks(key_chunk, k_sel, cond):
     """Key blocks of 256 and 1024 tokens (walked in 128-key units by dQ, one
     dK/dV workgroup per unit), with and without condition frames."""
     _case(8, 16, 32, 2, k_sel, kind="field", seed=19, cond_frames=cond, key_chunk=key_chunk)
+
+
+@pytest.mark.parametrize("grid,key_chunk,k_sel,cond", [
+    ((6, 6, 12), None, 3, 0),             # every axis cut, 8 blocks
+    ((10, 20, 36), None, 6, 4),
+    ((10, 20, 36), (4, 8, 8), 4, 0),      # 256-token keys cut along h and w
+    ((10, 20, 36), (8, 8, 16), 2, 0),     # 1024: units wholly outside the grid
+])
+def test_partial_blocks(grid, key_chunk, k_sel, cond):
+    """Partial blocks at the grid's far edge: every gradient element against
+    the oracle (slots outside the grid take no part, in queries or keys)."""
+    _case(*grid, 2, k_sel, kind="field", seed=43, cond_frames=cond, key_chunk=key_chunk)
 
 
 def test_many_blocks_one_key_block_popular():

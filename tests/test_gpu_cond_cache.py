@@ -45,19 +45,22 @@ def _step_tensors(T, H, W, heads, cond_frames, seed0, seed1):
     return a, tuple(step1)
 
 
-@pytest.mark.parametrize("chunk,key_chunk,params", [
-    ((4, 4, 8), None, SelectParams.topk(6)),
-    ((4, 4, 8), None, SelectParams.cdf(0.8, 2, 10)),
-    ((4, 4, 8), (2, 4, 8), SelectParams.topk(9)),
-    ((4, 4, 8), (4, 8, 8), SelectParams.topk(3)),
-    ((2, 4, 8), (4, 4, 8), SelectParams.topk(5)),
+@pytest.mark.parametrize("grid,chunk,key_chunk,params", [
+    ((16, 16, 32), (4, 4, 8), None, SelectParams.topk(6)),
+    ((16, 16, 32), (4, 4, 8), None, SelectParams.cdf(0.8, 2, 10)),
+    ((16, 16, 32), (4, 4, 8), (2, 4, 8), SelectParams.topk(9)),
+    ((16, 16, 32), (4, 4, 8), (4, 8, 8), SelectParams.topk(3)),
+    ((16, 16, 32), (2, 4, 8), (4, 4, 8), SelectParams.topk(5)),
+    # partial blocks along t, h and w
+    ((14, 18, 36), (4, 4, 8), None, SelectParams.topk(6)),
+    ((14, 18, 36), (4, 4, 8), (4, 8, 8), SelectParams.cdf(0.8, 1, 8)),
 ])
-def test_noisy_rows_match_full_path(chunk, key_chunk, params):
+def test_noisy_rows_match_full_path(grid, chunk, key_chunk, params):
     import torch
 
     from video_dit_block_bsa_amd import binding as B
 
-    T, H, W, heads, cond = 16, 16, 32, 2, 4
+    (T, H, W), heads, cond = grid, 2, 4
     problem = Problem.make(T, H, W, heads, chunk=chunk, cond_frames=cond, key_chunk=key_chunk)
     g = PT.geometry(problem)
     nb, cq = g.num_blocks, g.cond_blocks

@@ -64,13 +64,16 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Geom g, int nbw,
   const int t = threadIdx.x;
   const int j = t >> 1;
   const int half = t & 1;
-  const int tok = block_token(g, blk, j);
+  // A slot of a partial block outside the grid has no token: D = 0 and
+  // lse*log2(e) = +inf, so every probability recomputed for it is 0.
+  const bool inside = !g.partial || block_slot_valid(g, blk, j);
+  const int tok = inside ? block_token(g, blk, j) : 0;
   const size_t off = ((size_t)bh * g.S + tok) * kHeadDim + 64 * half;
   u32x4 ov[8], dv[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    ov[c] = *reinterpret_cast<const u32x4*>(o + off + 8 * c);
-    dv[c] = *reinterpret_cast<const u32x4*>(dout + off + 8 * c);
+    ov[c] = inside ? *reinterpret_cast<const u32x4*>(o + off + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    dv[c] = inside ? *reinterpret_cast<const u32x4*>(dout + off + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
   float acc = 0.f;
 #pragma unroll
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Geom g, int nbw,
   if (half == 1) {
     st[kBlockTokens + j] = acc;
   } else {
-    const float l = lse[(size_t)bh * g.S + tok];
+    const float l = inside ? lse[(size_t)bh * g.S + tok] : -INFINITY;
     st[j] = (l == -INFINITY) ? INFINITY : l * kLog2e;
   }
   // Mask rows are per key block (nbk of them); query block blk clears rows
@@ -295,7 +298,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
       __builtin_amdgcn_make_buffer_rsrc((void*)(vp + hoff), (short)0, head_bytes, kBufferWord3);
   const TileLanes tl = tile_lanes(g, w, lane);
 
-  const int qtok = block_origin(a, qb) + slot_offset(g, 32 * qs + n);
+  // A query slot of a partial block outside the grid computes on slot 0 (its
+  // stats make every probability 0) and is not written.
+  const bool q_inside = !g.partial || block_slot_valid(g, qb, 32 * qs + n);
+  const int qtok = block_origin(a, qb) + (q_inside ? slot_offset(g, 32 * qs + n) : 0);
   bf16x8 qf[8], df[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 
   // kh is a template constant inside the loop, so every LDS address is one of
   // a few per-lane offsets plus an immediate.
-  auto compute = [&](auto khc, const char* kt, const char* vt) __attribute__((always_inline)) {
+  auto compute = [&](auto khc, const char* kt, const char* vt, Unit un) __attribute__((always_inline)) {
     constexpr int kh = decltype(khc)::value;
 #pragma unroll
     for (int h = 0; h < 2 / kDqGroup; ++h) {
@@ -351,6 +357,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
           sacc[t2] = mfma(row_operand(kt, tt, s, tl), qf[s], sacc[t2]);
           pacc[t2] = mfma(row_operand(vt, tt, s, tl), df[s], pacc[t2]);
         }
+      if (g.partial) {
+        // Keys of a partial key block outside the grid: S = -inf, so P = 0.
+        // Value i of sub-tile tt is slot 128 sub + 32 tt + 16 (i/8) + 8 gs +
+        // i%8 of the key block; the lane part goes through an empty asm so
+        // that nothing derived from it is hoisted out of the loop.
+        const Extent e = key_block_extent(a, list[un.pos]);
+        if (e.t != g.ctk || e.h != g.chk || e.w != g.cwk) {
+          int lb = un.sub * kBlockTokens + 8 * gs;
+          asm volatile("" : "+v"(lb));
+#pragma unroll
+          for (int t2 = 0; t2 < kDqGroup; ++t2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = lb + 32 * (2 * kh + kDqGroup * h + t2) + 16 * (i >> 3) + (i & 7);
+              if (!key_slot_inside(a, e, j)) sacc[t2][i] = -INFINITY;
+            }
+        }
+      }
       phase_fence();
       // Accumulator value i of sub-tile tt is key 32tt + swap23(row): values
       // 0..7 are keys +8gs .. +8gs+7, values 8..15 keys +16+8gs ..; as a B
@@ -400,7 +424,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
         load_key_tile(a, krs, tl, w, unit_tok(nxt), kn);
         load_key_tile(a, vrs, tl, w, unit_tok(nxt), vn);
       }
-      compute(khc, reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt));
+      compute(khc, reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt), cur);
       if (nxt.pos >= count) return false;
       cur = nxt;
       nxt = next_unit(cur);
@@ -430,7 +454,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) dq[u][i] += part[(u * 16 + i) * 64 + lane];
-    store_rows(dqp + hoff + (size_t)qtok * kHeadDim, dq, g.scale, gs);
+    if (q_inside) store_rows(dqp + hoff + (size_t)qtok * kHeadDim, dq, g.scale, gs);
   }
 }
 
@@ -487,8 +511,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       (uint32_t)g.nb * (2 * kBlockTokens * 4), kBufferWord3);
   const TileLanes tl = tile_lanes(g, w, lane);
 
-  // P role keeps K of its keys (B operand of S), dS role keeps V (of dP).
-  const int ktok = key_block_origin(a, kb) + key_slot_offset(g, sub * kBlockTokens + 32 * ks + n);
+  // P role keeps K of its keys (B operand of S), dS role keeps V (of dP). A
+  // key slot of a partial block outside the grid computes on the block's
+  // slot 0 and is not written; query slots outside the grid have zero
+  // probabilities (their stats), so they add nothing to dK or dV.
+  const bool k_inside = !g.partial || key_slot_valid(g, kb, sub * kBlockTokens + 32 * ks + n);
+  const int ktok = key_block_origin(a, kb) +
+                   (k_inside ? key_slot_offset(g, sub * kBlockTokens + 32 * ks + n) : 0);
   bf16x8 xf[8];
   {
     const bf16_bits* src = ds_role ? vp : kp;
@@ -607,6 +636,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     run(std::integral_constant<int, 1>{});
   else
     run(std::integral_constant<int, 0>{});
+  if (!k_inside) return;
   if (ds_role)
     store_rows(dkp + hoff + (size_t)ktok * kHeadDim, acc, g.scale, gs);
   else
