@@ -324,7 +324,7 @@ def main():
                                      args.cond_cache_steps)
 
     bwd = None
-    if args.backward_steps > 0 and not w.key_chunk:
+    if args.backward_steps > 0:
         bwd = backward_bench(w, problem, qd, kd, vd, idx, cnt, stride, ws_att, stream, eff,
                              args.backward_steps)
 

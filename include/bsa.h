@@ -198,9 +198,9 @@ size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
  * P is recomputed in fp32 from lse; the products run in bf16 with fp32
  * accumulation (P and dS are rounded to bf16 as MFMA operands). No
  * floating-point atomics: results are bit-identical from run to run.
- * Limits: Nb, Nk <= 4096 blocks per (batch, head); query blocks of 128
- * tokens and key blocks of 128 to 1024 tokens (BSA_ERR_UNSUPPORTED
- * otherwise). Partial blocks are supported. */
+ * Limits: Nb, Nk <= 4096 blocks per (batch, head) (BSA_ERR_UNSUPPORTED
+ * otherwise). Every chunk shape of the forward is supported: query blocks of
+ * 64 or 128 tokens, key blocks of 64 to 1024 tokens, partial blocks. */
 bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const void* k,
                              const void* v, const void* o, const void* dout, const float* lse,
                              const int32_t* idx, const int32_t* cnt, int32_t idx_stride, void* dq,

@@ -250,7 +250,7 @@ def test_key_chunk_checks():
     assert _select(_problem(key_chunk=(4, 4, 12)), sp) == UNSUPPORTED    # 192 tokens
     assert _select(_problem(key_chunk=(8, 4, 8), cond_frames=4), sp) == INVALID
     assert _select(_problem(T=4 * 100, key_chunk=(2, 4, 8)), sp) == UNSUPPORTED  # 24,000 key blocks
-    assert _bwd(_problem(key_chunk=(2, 4, 8))) == UNSUPPORTED   # 64-token key blocks
+    assert B.attention_bwd_workspace_bytes(_problem(key_chunk=(2, 4, 8))) > 0  # 64-token keys
     assert B.attention_bwd_workspace_bytes(_problem(key_chunk=(4, 8, 8))) > 0
 
 
@@ -278,12 +278,13 @@ def test_cond_cache_checks():
 
 
 def test_query_chunk_of_64():
-    """64-token query blocks are accepted by selection and attention; the
-    backward rejects them."""
+    """64-token query blocks are accepted by selection, attention and the
+    backward (up to 4,096 query blocks per head)."""
     p = _problem(chunk=(2, 4, 8))          # 3,360 query blocks
     sp = B.SelectParams.topk(4)
     assert B.select_workspace_bytes(p, sp) > 0
-    assert _bwd(p) == UNSUPPORTED
+    assert B.attention_bwd_workspace_bytes(p) > 0
+    assert _bwd(_problem(T=4 * 40, chunk=(2, 4, 8))) == UNSUPPORTED  # 9,600 query blocks
     assert _select(_problem(T=4 * 64, chunk=(2, 4, 8)), sp) == UNSUPPORTED  # 15,360 key blocks
 
 

@@ -74,13 +74,13 @@ def run_backward(problem, q, k, v, do, idx, cnt, stride):
             lse.cpu().numpy(), *(PT.from_device(t).reshape(q.shape) for t in grads))
 
 
-def clean_lists(idx, cnt, nb, stride):
-    """The valid ids of each row (the forward skips ids outside [0, nb) and
-    clamps cnt to [0, stride])."""
+def clean_lists(idx, cnt, nbk, stride):
+    """The valid ids of each row (the forward skips ids outside [0, nbk), nbk
+    the number of key blocks, and clamps cnt to [0, stride])."""
     out = []
     for r in range(idx.shape[0]):
         c = min(max(int(cnt[r]), 0), stride)
-        out.append([int(x) for x in idx[r, :c] if 0 <= x < nb])
+        out.append([int(x) for x in idx[r, :c] if 0 <= x < nbk])
     return out
 
 
@@ -118,7 +118,7 @@ def compare_all(problem, q, k, v, do, idx, cnt, stride):
     nb = g.num_blocks
     o, o_plain, lse, dq, dk, dv = run_backward(problem, q, k, v, do, idx, cnt, stride)
     assert np.array_equal(o, o_plain), "bsa_attention_lse changed o"
-    lists = clean_lists(idx, cnt, nb, stride)
+    lists = clean_lists(idx, cnt, g.num_key_blocks, stride)
     for b in range(q.shape[0]):
         for h in range(q.shape[1]):
             out_r, lse_r, dq_r, dk_r, dv_r = oracle_pair(q, k, v, do, g, lists, b, h)
@@ -208,6 +208,22 @@ def test_partial_blocks(grid, key_chunk, k_sel, cond):
     """Partial blocks at the grid's far edge: every gradient element against
     the oracle (slots outside the grid take no part, in queries or keys)."""
     _case(*grid, 2, k_sel, kind="field", seed=43, cond_frames=cond, key_chunk=key_chunk)
+
+
+@pytest.mark.parametrize("grid,chunk,key_chunk,k_sel,cond", [
+    ((8, 16, 32), (4, 4, 8), (2, 4, 8), 5, 0),     # 64-token keys, odd counts
+    ((8, 16, 32), (4, 4, 8), (2, 4, 8), 6, 4),     # even counts, condition frames
+    ((8, 16, 32), (2, 4, 8), None, 5, 0),          # 64-token queries and keys
+    ((8, 16, 32), (2, 4, 8), (4, 4, 8), 4, 4),     # 64-token queries, 128-token keys
+    ((8, 16, 32), (4, 2, 8), (4, 8, 8), 3, 0),     # 64-token queries, 256-token keys
+    ((6, 12, 24), (2, 4, 8), (2, 4, 8), 4, 0),     # odd block counts, partial blocks
+])
+def test_64_token_blocks(grid, chunk, key_chunk, k_sel, cond):
+    """Query blocks of 64 tokens (dQ: four key parts per query slice; dK/dV:
+    two query blocks per step) and key blocks of 64 tokens (two per dQ unit
+    and per dK/dV workgroup), every gradient element against the oracle."""
+    _case(*grid, 2, k_sel, chunk=chunk, kind="field", seed=47, cond_frames=cond,
+          key_chunk=key_chunk)
 
 
 def test_many_blocks_one_key_block_popular():

@@ -386,9 +386,6 @@ bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const vo
   if (c.g.nb > kMaxBlocks)
     return fail(BSA_ERR_UNSUPPORTED, "%d blocks per head: the backward supports at most %d",
                 c.g.nb, kMaxBlocks);
-  if (c.g.nq != bsa::kBlockTokens || c.g.nk < bsa::kBlockTokens)
-    return fail(BSA_ERR_UNSUPPORTED,
-                "the backward needs query blocks of 128 tokens and key blocks of 128 to 1024");
   if (c.g.nbk > kMaxBlocks)
     return fail(BSA_ERR_UNSUPPORTED, "%d key blocks per head: the backward supports at most %d",
                 c.g.nbk, kMaxBlocks);

@@ -51,8 +51,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // One workgroup per (block, batch*head). Thread t handles half (t % 2) of the
 // channels of slot t / 2; the two halves meet with one lane exchange. stats
 // holds, per (batch*head, block), 128 values lse*log2(e) followed by 128
-// values D, in slot order. A query with lse = -inf (no key block) gets +inf,
-// so that its recomputed probabilities are exp2(x - inf) = 0.
+// values D, in slot order (64-token blocks fill the first 64 of each). A
+// query with lse = -inf (no key block) gets +inf, so that its recomputed
+// probabilities are exp2(x - inf) = 0.
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Geom g, int nbw,
                                                             const bf16_bits* __restrict__ o,
                                                             const bf16_bits* __restrict__ dout,
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Geom g, int nbw,
   const int half = t & 1;
   // A slot of a partial block outside the grid has no token: D = 0 and
   // lse*log2(e) = +inf, so every probability recomputed for it is 0.
-  const bool inside = !g.partial || block_slot_valid(g, blk, j);
+  const bool inside = j < g.nq && (!g.partial || block_slot_valid(g, blk, j));
   const int tok = inside ? block_token(g, blk, j) : 0;
   const size_t off = ((size_t)bh * g.S + tok) * kHeadDim + 64 * half;
   u32x4 ov[8], dv[8];
@@ -85,7 +86,9 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Geom g, int nbw,
     }
   acc += __shfl_xor(acc, 1);
   float* st = stats + ((size_t)bh * g.nb + blk) * (2 * kBlockTokens);
-  if (half == 1) {
+  if (j >= g.nq) {
+    // 64-token blocks use the first 64 entries of each half.
+  } else if (half == 1) {
     st[kBlockTokens + j] = acc;
   } else {
     const float l = inside ? lse[(size_t)bh * g.S + tok] : -INFINITY;
@@ -125,11 +128,7 @@ __global__ __launch_bounds__(kThreads) void bwd_mask_kernel(Geom g, int nbw, int
 constexpr int kBwdWaves = 8;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kRowsPerWave = kBlockTokens / kBwdWaves;
-
-// dQ: 32-key sub-tiles whose S^T and dP^T are computed together before their
-// dS^T feeds the dQ products (2 keeps more MFMAs in flight per wave; 1 was
-// measured as fast).
-constexpr int kDqGroup = 2;
+constexpr int kHalfTile = kBlockTokens / 2;
 
 // Keeps the scheduler from hoisting the next phase's LDS operand reads above
 // the current phase, which would raise register pressure for no gain (the
@@ -172,10 +171,13 @@ __device__ __forceinline__ TileLanes tile_lanes(const Geom& g, int w, int lane) 
   // fetches logical chunk (L%16) ^ 4r ^ i. The slot offset is linear in the
   // bits of the slot index (power-of-two chunk sides), so the row's token is
   // that of slot 16w + r plus that of slot 4i.
+  // With 64-token blocks, rows 64..127 of a tile hold a second block, so the
+  // slot of row x is x mod 64.
   const int r = lane >> 4;
-  t.ld = (uint32_t)slot_offset(g, kRowsPerWave * w + r) * (kHeadDim * 2) +
+  const int row = kRowsPerWave * w + r;
+  t.ld = (uint32_t)slot_offset(g, row & (g.nq - 1)) * (kHeadDim * 2) +
          (uint32_t)(((lane & 15) ^ (r << 2)) << 4);
-  t.ldk = (uint32_t)key_slot_offset(g, kRowsPerWave * w + r) * (kHeadDim * 2) +
+  t.ldk = (uint32_t)key_slot_offset(g, g.nk == 64 ? (row & 63) : row) * (kHeadDim * 2) +
           (uint32_t)(((lane & 15) ^ (r << 2)) << 4);
   return t;
 }
@@ -257,18 +259,24 @@ __device__ __forceinline__ void xcd_block(const AttnArgs& a, int& pair, int& blk
 }
 
 // ------------------------------------------------------------------ dQ ---
-// Wave w owns queries 32(w%4) .. +31 of the query block and keys
-// 64(w/4) .. +63 of every key block: the two waves of a query slice split
-// each key block, so no product is computed twice, and their partial dQ are
-// added once at the end. Q^T and dO^T of the wave's queries stay in registers
-// as B operands. Per 32-key sub-tile:
+// Query blocks of 128 tokens: wave w owns queries 32(w%4) .. +31 and
+// sub-tiles 2(w/4), 2(w/4)+1 (keys 64(w/4) .. +63) of every 128-key unit.
+// Query blocks of 64 tokens (kSplit): wave w owns queries 32(w%2) .. +31 and
+// sub-tile w/2 (keys 32(w/2) .. +31) of every unit. Either way no product is
+// computed twice, and the waves of a query slice add their partial dQ once at
+// the end, in a fixed order. Q^T and dO^T of the wave's queries stay in
+// registers as B operands. Per 32-key sub-tile:
 //   S^T = K Q^T, dP^T = V dO^T    (8 channel steps each)
 //   dS^T = P^T * (dP^T - D)       lane's query: one lse and one D per lane
 //   dQ^T += K^T dS^T              (4 channel groups x 2 key steps; K^T by
 //                                  transposing reads of the same K tile)
-// K and V tiles are double-buffered in LDS (two separate objects each, the
-// loop unrolled by two so every read names its buffer at compile time and
-// never waits for the loads into the other one).
+// Units are walked as in the forward (kKeyMode 0: a 128-token key block;
+// 1: unit `b` of a key block of 256+ tokens; 2: two 64-token key blocks,
+// the lower one's keys in rows 0..63, the upper one's in rows 64..127). K and
+// V tiles are double-buffered in LDS (two separate objects each, the loop
+// unrolled by two so every read names its buffer at compile time and never
+// waits for the loads into the other one).
+template <int kKeyMode, bool kSplit>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
@@ -286,8 +294,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int qs = w & 3;   // query slice
-  const int kh = w >> 2;  // key half
+  const int qs = kSplit ? (w & 1) : (w & 3);  // query slice
+  const int kpart = kSplit ? (w >> 1) : (w >> 2);
   const int n = lane & 31;
   const int gs = lane >> 5;
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
@@ -323,93 +331,114 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     }
     return from;
   };
-  // Key blocks of 128 * 2^unit_shift tokens are walked in units of 128 keys:
-  // position `pos` of the list, unit `sub` of that key block.
-  struct Unit {
-    int pos, sub;
+  // Unit cursor, as in the forward: (position, unit within the key block)
+  // for kKeyMode 0 and 1, (position of the lower block, position of the upper
+  // block) for kKeyMode 2. The unit exists while .a < count.
+  struct Cursor {
+    int a, b;
   };
-  auto next_unit = [&](Unit c) __attribute__((always_inline)) -> Unit {
-    if (c.sub + 1 < (1 << a.unit_shift)) return {c.pos, c.sub + 1};
-    return {next_valid(c.pos + 1), 0};
+  auto first_unit = [&]() __attribute__((always_inline)) -> Cursor {
+    const int p = next_valid(0);
+    return {p, kKeyMode == 2 ? next_valid(p + 1) : 0};
   };
-  auto unit_tok = [&](Unit c) __attribute__((always_inline)) -> int {
-    return key_block_origin(a, list[c.pos]) + key_slot_offset(g, c.sub * kBlockTokens);
+  auto next_unit = [&](Cursor c) __attribute__((always_inline)) -> Cursor {
+    if constexpr (kKeyMode == 1) {
+      if (c.b + 1 < (1 << a.unit_shift)) return {c.a, c.b + 1};
+      return {next_valid(c.a + 1), 0};
+    } else if constexpr (kKeyMode == 2) {
+      const int p = next_valid(c.b + 1);
+      return {p, next_valid(p + 1)};
+    } else {
+      return {next_valid(c.a + 1), 0};
+    }
+  };
+  // Token of the first slot that this wave's tile rows count from: waves 4..7
+  // stage rows 64..127, which in kKeyMode 2 are the upper block's (the lower
+  // one again when it is missing: those rows are never used).
+  auto wave_base = [&](Cursor c) __attribute__((always_inline)) -> int {
+    if constexpr (kKeyMode == 2) {
+      return key_block_origin(a, list[(w >= 4 && c.b < count) ? c.b : c.a]);
+    } else if constexpr (kKeyMode == 1) {
+      return key_block_origin(a, list[c.a]) + key_slot_offset(g, c.b * kBlockTokens);
+    } else {
+      return key_block_origin(a, list[c.a]);
+    }
   };
 
   f32x16 dq[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) dq[u] = f32x16{};
 
-  // kh is a template constant inside the loop, so every LDS address is one of
-  // a few per-lane offsets plus an immediate.
-  auto compute = [&](auto khc, const char* kt, const char* vt, Unit un) __attribute__((always_inline)) {
-    constexpr int kh = decltype(khc)::value;
-#pragma unroll
-    for (int h = 0; h < 2 / kDqGroup; ++h) {
-      f32x16 sacc[kDqGroup], pacc[kDqGroup];
-#pragma unroll
-      for (int t2 = 0; t2 < kDqGroup; ++t2) sacc[t2] = pacc[t2] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int t2 = 0; t2 < kDqGroup; ++t2) {
-          const int tt = 2 * kh + kDqGroup * h + t2;
-          sacc[t2] = mfma(row_operand(kt, tt, s, tl), qf[s], sacc[t2]);
-          pacc[t2] = mfma(row_operand(vt, tt, s, tl), df[s], pacc[t2]);
-        }
-      if (g.partial) {
-        // Keys of a partial key block outside the grid: S = -inf, so P = 0.
-        // Value i of sub-tile tt is slot 128 sub + 32 tt + 16 (i/8) + 8 gs +
-        // i%8 of the key block; the lane part goes through an empty asm so
-        // that nothing derived from it is hoisted out of the loop.
-        const Extent e = key_block_extent(a, list[un.pos]);
-        if (e.t != g.ctk || e.h != g.chk || e.w != g.cwk) {
-          int lb = un.sub * kBlockTokens + 8 * gs;
-          asm volatile("" : "+v"(lb));
-#pragma unroll
-          for (int t2 = 0; t2 < kDqGroup; ++t2)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = lb + 32 * (2 * kh + kDqGroup * h + t2) + 16 * (i >> 3) + (i & 7);
-              if (!key_slot_inside(a, e, j)) sacc[t2][i] = -INFINITY;
-            }
-        }
-      }
-      phase_fence();
-      // Accumulator value i of sub-tile tt is key 32tt + swap23(row): values
-      // 0..7 are keys +8gs .. +8gs+7, values 8..15 keys +16+8gs ..; as a B
-      // operand they are key steps 2tt and 2tt+1.
-      bf16x8 dsf[2 * kDqGroup];
-#pragma unroll
-      for (int t2 = 0; t2 < kDqGroup; ++t2)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 packed;
-#pragma unroll
-          for (int j2 = 0; j2 < 4; ++j2) {
-            const int i0 = 8 * hh + 2 * j2;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0], a.c_log2, -lse2));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0 + 1], a.c_log2, -lse2));
-            packed[j2] = pack_bf16(p0 * (pacc[t2][i0] - dd), p1 * (pacc[t2][i0 + 1] - dd));
-          }
-          dsf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, packed);
-        }
-      phase_fence();
-#pragma unroll
-      for (int ks = 0; ks < 2 * kDqGroup; ++ks)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          dq[u] = mfma(tr_operand(kt, 2 * (2 * kh + kDqGroup * h) + ks, u, tl), dsf[ks], dq[u]);
-      phase_fence();
+  // The wave's key part is a template constant inside the loop, so every LDS
+  // address is one of a few per-lane offsets plus an immediate.
+  auto compute = [&](auto kpc, const char* kt, const char* vt, Cursor un) __attribute__((always_inline)) {
+    constexpr int NS = kSplit ? 1 : 2;                          // sub-tiles per wave
+    constexpr int TT0 = kSplit ? decltype(kpc)::value : 2 * decltype(kpc)::value;
+    constexpr bool kUpper = kKeyMode == 2 && TT0 >= 2;          // rows of the upper block
+    if constexpr (kUpper) {
+      if (un.b >= count) return;  // a lone last 64-token block: no upper half
     }
+    f32x16 sacc[NS], pacc[NS];
+#pragma unroll
+    for (int t2 = 0; t2 < NS; ++t2) sacc[t2] = pacc[t2] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t2 = 0; t2 < NS; ++t2) {
+        sacc[t2] = mfma(row_operand(kt, TT0 + t2, s, tl), qf[s], sacc[t2]);
+        pacc[t2] = mfma(row_operand(vt, TT0 + t2, s, tl), df[s], pacc[t2]);
+      }
+    if (g.partial) {
+      // Keys of a partial key block outside the grid: S = -inf, so P = 0.
+      // Value i of sub-tile tt is key 32 tt + 16 (i/8) + 8 gs + i%8 of the
+      // unit; the lane part goes through an empty asm so that nothing
+      // derived from it is hoisted out of the loop.
+      const Extent e = key_block_extent(a, list[kUpper ? un.b : un.a]);
+      if (e.t != g.ctk || e.h != g.chk || e.w != g.cwk) {
+        int lb = (kKeyMode == 1 ? un.b * kBlockTokens : 0) - (kUpper ? kHalfTile : 0) + 8 * gs;
+        asm volatile("" : "+v"(lb));
+#pragma unroll
+        for (int t2 = 0; t2 < NS; ++t2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = lb + 32 * (TT0 + t2) + 16 * (i >> 3) + (i & 7);
+            if (!key_slot_inside(a, e, j)) sacc[t2][i] = -INFINITY;
+          }
+      }
+    }
+    phase_fence();
+    // Accumulator value i of sub-tile tt is key 32tt + swap23(row): values
+    // 0..7 are keys +8gs .. +8gs+7, values 8..15 keys +16+8gs ..; as a B
+    // operand they are key steps 2tt and 2tt+1.
+    bf16x8 dsf[2 * NS];
+#pragma unroll
+    for (int t2 = 0; t2 < NS; ++t2)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        u32x4 packed;
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) {
+          const int i0 = 8 * hh + 2 * j2;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0], a.c_log2, -lse2));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t2][i0 + 1], a.c_log2, -lse2));
+          packed[j2] = pack_bf16(p0 * (pacc[t2][i0] - dd), p1 * (pacc[t2][i0 + 1] - dd));
+        }
+        dsf[2 * t2 + hh] = __builtin_bit_cast(bf16x8, packed);
+      }
+    phase_fence();
+#pragma unroll
+    for (int ks = 0; ks < 2 * NS; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dq[u] = mfma(tr_operand(kt, 2 * TT0 + ks, u, tl), dsf[ks], dq[u]);
+    phase_fence();
   };
 
-  auto run = [&](auto khc) __attribute__((always_inline)) {
-    Unit cur = {next_valid(0), 0};
-    if (cur.pos >= count) return;
-    load_key_tile(a, krs, tl, w, unit_tok(cur), k0s);
-    load_key_tile(a, vrs, tl, w, unit_tok(cur), v0s);
-    Unit nxt = next_unit(cur);
+  auto run = [&](auto kpc) __attribute__((always_inline)) {
+    Cursor cur = first_unit();
+    if (cur.a >= count) return;
+    load_key_tile(a, krs, tl, w, wave_base(cur), k0s);
+    load_key_tile(a, vrs, tl, w, wave_base(cur), v0s);
+    Cursor nxt = next_unit(cur);
     auto step = [&](auto bc) __attribute__((always_inline)) -> bool {
       constexpr int b = decltype(bc)::value;
       bf16_bits* kt = b == 0 ? k0s : k1s;
@@ -420,12 +449,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
       // everyone's are, and everyone has finished reading the other buffer.
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       workgroup_barrier();
-      if (nxt.pos < count) {
-        load_key_tile(a, krs, tl, w, unit_tok(nxt), kn);
-        load_key_tile(a, vrs, tl, w, unit_tok(nxt), vn);
+      if (nxt.a < count) {
+        load_key_tile(a, krs, tl, w, wave_base(nxt), kn);
+        load_key_tile(a, vrs, tl, w, wave_base(nxt), vn);
       }
-      compute(khc, reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt), cur);
-      if (nxt.pos >= count) return false;
+      compute(kpc, reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt), cur);
+      if (nxt.a >= count) return false;
       cur = nxt;
       nxt = next_unit(cur);
       return true;
@@ -433,34 +462,50 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
   };
-  // Both copies of the loop run the same barriers, so the halves stay in step.
-  if (kh == 0)
-    run(std::integral_constant<int, 0>{});
-  else
-    run(std::integral_constant<int, 1>{});
-  // The key halves meet: waves 4..7 leave their partial dQ in LDS (16 KB per
-  // wave, lane-contiguous words), waves 0..3 add them in and store.
+  // Every copy of the loop runs the same barriers, so the waves stay in step.
+  if constexpr (kSplit) {
+    if (kpart == 0) run(std::integral_constant<int, 0>{});
+    else if (kpart == 1) run(std::integral_constant<int, 1>{});
+    else if (kpart == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 3>{});
+  } else {
+    if (kpart == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+  }
+  // The key parts of each query slice meet: every wave but the first of its
+  // slice leaves its partial dQ in LDS (16 KB per wave, lane-contiguous
+  // words; the tile buffers are idle now), the first adds them in order and
+  // stores.
   __syncthreads();
-  float* part = reinterpret_cast<float*>(qs < 2 ? k0s : v0s) + (qs & 1) * (64 * 64);
-  if (kh == 1) {
+  auto part = [&](int slot) __attribute__((always_inline)) -> float* {
+    bf16_bits* buf = slot < 2 ? k0s : slot < 4 ? v0s : k1s;
+    return reinterpret_cast<float*>(buf) + (slot & 1) * (64 * 64);
+  };
+  constexpr int kParts = kSplit ? 4 : 2;
+  if (kpart != 0) {
+    float* p = part(qs * (kParts - 1) + kpart - 1);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part[(u * 16 + i) * 64 + lane] = dq[u][i];
+      for (int i = 0; i < 16; ++i) p[(u * 16 + i) * 64 + lane] = dq[u][i];
   }
   __syncthreads();
-  if (kh == 0) {
+  if (kpart == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int r = 1; r < kParts; ++r) {
+      const float* p = part(qs * (kParts - 1) + r - 1);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dq[u][i] += part[(u * 16 + i) * 64 + lane];
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dq[u][i] += p[(u * 16 + i) * 64 + lane];
+    }
     if (q_inside) store_rows(dqp + hoff + (size_t)qtok * kHeadDim, dq, g.scale, gs);
   }
 }
 
 // ---------------------------------------------------------------- dK dV ---
-// One workgroup of 8 waves per (batch*head, key block); wave w owns keys
-// 32(w%4) .. +31, in one of two roles:
+// One workgroup of 8 waves per (batch*head, 128-key unit); wave w owns keys
+// 32(w%4) .. +31 of the unit, in one of two roles:
 //   w < 4  (P role):  S = Q K^T, P, dV^T += dO^T P
 //   w >= 4 (dS role): dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS
 // One wave cannot hold K, V, dK and dV (192 registers) and its working set
@@ -470,8 +515,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 // the P-role wave to the dS-role wave of the same keys as bf16 through a
 // two-slot LDS buffer per key slice, with one barrier per 32-query sub-tile
 // (it waits for LDS traffic only, never for the tile loads in flight). Q, dO
-// and the stats of a query block are double-buffered in LDS; query blocks
-// come from the set bits of the key block's mask row, in ascending order.
+// and the stats of the query rows are double-buffered in LDS; query blocks
+// come from the set bits of the key blocks' mask rows, in ascending order.
+//
+// A unit is unit `sub` of one key block of 128+ tokens, or (kPairKeys) the
+// 64-token key blocks 2u and 2u+1: keys 0..63 of the first, 64..127 of the
+// second, and the query blocks walked are the union of their mask rows.
+// Query blocks of 64 tokens (kSplit) go two at a time through the 128 query
+// rows of a step: rows 0..63 of the first set bit, 64..127 of the next one.
+// A wave whose key block a query block did not select (or the missing second
+// query block after an odd count) hands over P = 0 for those rows, so they
+// add nothing to its dK and dV.
+template <bool kPairKeys, bool kSplit>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     AttnArgs a, int nbw, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
@@ -484,15 +539,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) float st0s[2 * kBlockTokens];
   __shared__ __attribute__((aligned(1024))) float st1s[2 * kBlockTokens];
   __shared__ __attribute__((aligned(1024))) char xch[4 * 2 * 2048];  // [key slice][slot][2 KB]
-  __shared__ uint32_t mrow[kBlockTokens];
+  __shared__ uint32_t mrow[2][kBlockTokens];
   const Geom& g = a.g;
   int pair, unit;
   xcd_block(a, pair, unit);
-  // Unit `sub` (128 keys) of key block kb.
-  const int kb = unit >> a.unit_shift;
-  const int sub = unit & ((1 << a.unit_shift) - 1);
-  if (kb >= g.nbk) return;
-
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -500,6 +550,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const bool ds_role = (w >> 2) != 0;
   const int n = lane & 31;
   const int gs = lane >> 5;
+  // The unit's first key block, the wave's key block and the wave's key slot.
+  int kb0, kbw, slot;
+  if constexpr (kPairKeys) {
+    kb0 = 2 * unit;
+    kbw = kb0 + (ks >> 1);
+    slot = 32 * (ks & 1) + n;
+  } else {
+    kb0 = unit >> a.unit_shift;
+    kbw = kb0;
+    slot = (unit & ((1 << a.unit_shift) - 1)) * kBlockTokens + 32 * ks + n;
+  }
+  if (kb0 >= g.nbk) return;
+
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
   const uint32_t head_bytes = (uint32_t)g.S * (kHeadDim * 2);
   const __amdgpu_buffer_rsrc_t qrs =
@@ -512,12 +575,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const TileLanes tl = tile_lanes(g, w, lane);
 
   // P role keeps K of its keys (B operand of S), dS role keeps V (of dP). A
-  // key slot of a partial block outside the grid computes on the block's
-  // slot 0 and is not written; query slots outside the grid have zero
-  // probabilities (their stats), so they add nothing to dK or dV.
-  const bool k_inside = !g.partial || key_slot_valid(g, kb, sub * kBlockTokens + 32 * ks + n);
-  const int ktok = key_block_origin(a, kb) +
-                   (k_inside ? key_slot_offset(g, sub * kBlockTokens + 32 * ks + n) : 0);
+  // key slot outside the grid (a partial block's, or the missing second
+  // block of an odd count) computes on the unit's first slot and is not
+  // written; query slots outside the grid have zero probabilities (their
+  // stats), so they add nothing to dK or dV.
+  const bool k_inside = kbw < g.nbk && (!g.partial || key_slot_valid(g, kbw, slot));
+  const int ktok = k_inside ? key_block_origin(a, kbw) + key_slot_offset(g, slot)
+                            : key_block_origin(a, kb0);
   bf16x8 xf[8];
   {
     const bf16_bits* src = ds_role ? vp : kp;
@@ -526,36 +590,79 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       xf[s] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4*>(src + hoff + (size_t)ktok * kHeadDim + 16 * s + 8 * gs));
   }
-  if (t < nbw) mrow[t] = mask[((size_t)pair * g.nbk + kb) * nbw + t];
+  if (t < nbw) {
+    mrow[0][t] = mask[((size_t)pair * g.nbk + kb0) * nbw + t];
+    if (kPairKeys)
+      mrow[1][t] = kb0 + 1 < g.nbk ? mask[((size_t)pair * g.nbk + kb0 + 1) * nbw + t] : 0u;
+  }
   __syncthreads();
+  const int mine = kPairKeys ? (ks >> 1) : 0;  // the mask row of the wave's key block
   auto next_set = [&](int from) __attribute__((always_inline)) -> int {
     int wd = from >> 5;
     if (wd >= nbw) return g.nb;
-    uint32_t bits = __builtin_amdgcn_readfirstlane(mrow[wd]) & (0xffffffffu << (from & 31));
+    auto word = [&](int i) __attribute__((always_inline)) {
+      return __builtin_amdgcn_readfirstlane(kPairKeys ? (mrow[0][i] | mrow[1][i]) : mrow[0][i]);
+    };
+    uint32_t bits = word(wd) & (0xffffffffu << (from & 31));
     while (bits == 0u) {
       if (++wd >= nbw) return g.nb;
-      bits = __builtin_amdgcn_readfirstlane(mrow[wd]);
+      bits = word(wd);
     }
     return wd * 32 + __builtin_ctz(bits);
   };
-  auto load_stats = [&](int qb, float* dst) __attribute__((always_inline)) {
-    if (w == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)dst, 16, (uint32_t)lane * 16,
-                                               (uint32_t)qb * (2 * kBlockTokens * 4), 0, 0);
+  // Whether the wave's key block was selected by query block qb (< nb).
+  auto selected = [&](int qb) __attribute__((always_inline)) -> bool {
+    return ((__builtin_amdgcn_readfirstlane(mrow[mine][qb >> 5]) >> (qb & 31)) & 1u) != 0u;
+  };
+  // A step's query rows: block qa in rows 0..127 (128-token blocks), or qa in
+  // rows 0..63 and qb2 (nb: none) in rows 64..127 (64-token blocks).
+  struct Rows {
+    int qa, qb2;
+  };
+  auto first_rows = [&]() __attribute__((always_inline)) -> Rows {
+    const int x = next_set(0);
+    return {x, kSplit && x < g.nb ? next_set(x + 1) : g.nb};
+  };
+  auto next_rows = [&](Rows r) __attribute__((always_inline)) -> Rows {
+    const int x = next_set((kSplit && r.qb2 < g.nb ? r.qb2 : r.qa) + 1);
+    return {x, kSplit && x < g.nb ? next_set(x + 1) : g.nb};
+  };
+  auto load_rows = [&](Rows r, bf16_bits* qdst, bf16_bits* ddst, float* sdst)
+                       __attribute__((always_inline)) {
+    const int blk = (kSplit && w >= 4 && r.qb2 < g.nb) ? r.qb2 : r.qa;
+    load_tile(a, qrs, tl, w, blk, qdst);
+    load_tile(a, drs, tl, w, blk, ddst);
+    if (w == 0) {
+      // stats of a block: lse*log2(e) at floats 0.., D at floats 128... For
+      // two 64-token blocks, lanes 0..15 / 16..31 fetch the lse of the first
+      // / second block, lanes 32..47 / 48..63 their D.
+      uint32_t off;
+      if constexpr (kSplit) {
+        const int sb = ((lane & 16) && r.qb2 < g.nb) ? r.qb2 : r.qa;
+        off = (uint32_t)sb * (2 * kBlockTokens * 4) + ((lane & 32) ? kBlockTokens * 4 : 0) +
+              16 * (lane & 15);
+      } else {
+        off = (uint32_t)r.qa * (2 * kBlockTokens * 4) + 16 * lane;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)sdst, 16, off, 0, 0, 0);
+    }
   };
 
   f32x16 acc[4];  // dV (P role) or dK (dS role)
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
 
-  auto compute = [&](auto rolec, const char* qt, const char* dt, const float* sts)
-                     __attribute__((always_inline)) {
+  // keep_lo / keep_hi: whether query rows 0..63 / 64..127 of the step belong
+  // to a query block that selected the wave's key block.
+  auto compute = [&](auto rolec, const char* qt, const char* dt, const float* sts, bool keep_lo,
+                     bool keep_hi) __attribute__((always_inline)) {
     constexpr bool dsr = decltype(rolec)::value != 0;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      char* slot = xch + ks * 4096 + (tt & 1) * 2048;
+      char* xs = xch + ks * 4096 + (tt & 1) * 2048;
       bf16x8 bop[2];
       if constexpr (!dsr) {
+        const bool keep = tt < 2 ? keep_lo : keep_hi;
         f32x16 sacc = f32x16{};
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma(row_operand(qt, tt, s, tl), xf[s], sacc);
@@ -567,11 +674,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
           for (int j2 = 0; j2 < 4; ++j2) {
             const int i0 = 8 * hh + 2 * j2;
             const f32x2 l2 = *reinterpret_cast<const f32x2*>(sts + q0 + 2 * j2);
-            packed[j2] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i0], a.c_log2, -l2[0])),
-                                   __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i0 + 1], a.c_log2, -l2[1])));
+            const uint32_t pw =
+                pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i0], a.c_log2, -l2[0])),
+                          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i0 + 1], a.c_log2, -l2[1])));
+            // (With one 128+-token key block and 128-token query blocks every
+            // query block walked selected the wave's keys.)
+            packed[j2] = (kPairKeys || kSplit) && !keep ? 0u : pw;
           }
           bop[hh] = __builtin_bit_cast(bf16x8, packed);
-          *reinterpret_cast<u32x4*>(slot + hh * 1024 + lane * 16) = packed;
+          *reinterpret_cast<u32x4*>(xs + hh * 1024 + lane * 16) = packed;
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the hand-off is written
         workgroup_barrier();
@@ -584,7 +695,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int q0 = 32 * tt + 16 * hh + 8 * gs;
-          const u32x4 pb = *reinterpret_cast<const u32x4*>(slot + hh * 1024 + lane * 16);
+          const u32x4 pb = *reinterpret_cast<const u32x4*>(xs + hh * 1024 + lane * 16);
           u32x4 packed;
 #pragma unroll
           for (int j2 = 0; j2 < 4; ++j2) {
@@ -605,28 +716,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   };
 
   auto run = [&](auto rolec) __attribute__((always_inline)) {
-    int cur = next_set(0);
-    if (cur >= g.nb) return;
-    load_tile(a, qrs, tl, w, cur, q0s);
-    load_tile(a, drs, tl, w, cur, d0s);
-    load_stats(cur, st0s);
-    int nxt = next_set(cur + 1);
+    Rows cur = first_rows();
+    if (cur.qa >= g.nb) return;
+    load_rows(cur, q0s, d0s, st0s);
+    Rows nxt = next_rows(cur);
     auto step = [&](auto bc) __attribute__((always_inline)) -> bool {
       constexpr int b = decltype(bc)::value;
-      bf16_bits* qt = b == 0 ? q0s : q1s;
-      bf16_bits* dt = b == 0 ? d0s : d1s;
-      float* sts = b == 0 ? st0s : st1s;
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       workgroup_barrier();
-      if (nxt < g.nb) {
-        load_tile(a, qrs, tl, w, nxt, b == 0 ? q1s : q0s);
-        load_tile(a, drs, tl, w, nxt, b == 0 ? d1s : d0s);
-        load_stats(nxt, b == 0 ? st1s : st0s);
-      }
-      compute(rolec, reinterpret_cast<const char*>(qt), reinterpret_cast<const char*>(dt), sts);
-      if (nxt >= g.nb) return false;
+      if (nxt.qa < g.nb) load_rows(nxt, b == 0 ? q1s : q0s, b == 0 ? d1s : d0s, b == 0 ? st1s : st0s);
+      const bool keep_lo = kPairKeys ? selected(cur.qa) : true;
+      const bool keep_hi = kSplit ? (cur.qb2 < g.nb && (!kPairKeys || selected(cur.qb2))) : keep_lo;
+      compute(rolec, reinterpret_cast<const char*>(b == 0 ? q0s : q1s),
+              reinterpret_cast<const char*>(b == 0 ? d0s : d1s), b == 0 ? st0s : st1s, keep_lo,
+              keep_hi);
+      if (nxt.qa >= g.nb) return false;
       cur = nxt;
-      nxt = next_set(cur + 1);
+      nxt = next_rows(cur);
       return true;
     };
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
@@ -658,17 +764,41 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
                      stride, idx, cnt, mask);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const bool split = g.nq != kBlockTokens;
+  const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
   const dim3 grid((unsigned)((size_t)g.bh * a.nq8));
-  hipLaunchKernelGGL(bwd_dq_kernel, grid, dim3(kBwdThreads), 0, stream, a, q, k, v, dout, stats,
-                     idx, cnt, dq);
+#define BSA_LAUNCH_DQ(MODE, SPLIT)                                                                  \
+  hipLaunchKernelGGL((bwd_dq_kernel<MODE, SPLIT>), grid, dim3(kBwdThreads), 0, stream, a, q, k, v, \
+                     dout, stats, idx, cnt, dq)
+  if (split) {
+    if (mode == 0) BSA_LAUNCH_DQ(0, true);
+    else if (mode == 1) BSA_LAUNCH_DQ(1, true);
+    else BSA_LAUNCH_DQ(2, true);
+  } else {
+    if (mode == 0) BSA_LAUNCH_DQ(0, false);
+    else if (mode == 1) BSA_LAUNCH_DQ(1, false);
+    else BSA_LAUNCH_DQ(2, false);
+  }
+#undef BSA_LAUNCH_DQ
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dK/dV: one workgroup per 128-key unit of every key block.
+  // dK/dV: one workgroup per 128-key unit (a unit of a key block of 128+
+  // tokens, or two 64-token key blocks).
   AttnArgs au = a;
-  au.nq8 = ((g.nbk << a.unit_shift) + 7) / 8 * 8;
+  const int units = mode == 2 ? (g.nbk + 1) / 2 : (g.nbk << a.unit_shift);
+  au.nq8 = (units + 7) / 8 * 8;
   const dim3 grid_u((unsigned)((size_t)g.bh * au.nq8));
-  hipLaunchKernelGGL(bwd_dkdv_kernel, grid_u, dim3(kBwdThreads), 0, stream, au, nbw, q, k, v, dout,
-                     stats, mask, dk, dv);
+#define BSA_LAUNCH_DKDV(PAIR, SPLIT)                                                            \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<PAIR, SPLIT>), grid_u, dim3(kBwdThreads), 0, stream, au, \
+                     nbw, q, k, v, dout, stats, mask, dk, dv)
+  if (mode == 2) {
+    if (split) BSA_LAUNCH_DKDV(true, true);
+    else BSA_LAUNCH_DKDV(true, false);
+  } else {
+    if (split) BSA_LAUNCH_DKDV(false, true);
+    else BSA_LAUNCH_DKDV(false, false);
+  }
+#undef BSA_LAUNCH_DKDV
   return hipGetLastError();
 }
 
