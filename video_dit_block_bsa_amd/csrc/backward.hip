@@ -506,8 +506,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- dK dV ---
-// One workgroup of 8 waves per (batch*head, 128-key unit); wave w owns keys
-// 32(w%4) .. +31 of the unit, in one of two roles:
+// One workgroup of 8 waves per (batch*head, 128-key unit of a key block of
+// 128+ tokens); wave w owns keys 32(w%4) .. +31 of the unit, in one of two
+// roles:
 //   w < 4  (P role):  S = Q K^T, P, dV^T += dO^T P
 //   w >= 4 (dS role): dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS
 // One wave cannot hold K, V, dK and dV (192 registers) and its working set
@@ -518,17 +519,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 // two-slot LDS buffer per key slice, with one barrier per 32-query sub-tile
 // (it waits for LDS traffic only, never for the tile loads in flight). Q, dO
 // and the stats of the query rows are double-buffered in LDS; query blocks
-// come from the set bits of the key blocks' mask rows, in ascending order.
+// come from the set bits of the key block's mask row, in ascending order.
 //
-// A unit is unit `sub` of one key block of 128+ tokens, or (kPairKeys) the
-// 64-token key blocks 2u and 2u+1: keys 0..63 of the first, 64..127 of the
-// second, and the query blocks walked are the union of their mask rows.
-// Query blocks of 64 tokens (kSplit) go two at a time through the 128 query
-// rows of a step: rows 0..63 of the first set bit, 64..127 of the next one.
-// A wave whose key block a query block did not select (or the missing second
-// query block after an odd count) hands over P = 0 for those rows, so they
-// add nothing to its dK and dV.
-template <bool kPairKeys, bool kSplit>
+// kHalfKeys (64-token key blocks): one workgroup per key block; wave w of a
+// role owns key slice w%2 (32 keys) and query half (w/2)%2 (sub-tiles 0, 1 or
+// 2, 3 of each step), and the two query halves' partial dK and dV are added
+// once, in a fixed order, through LDS at the end.
+// kSplit (64-token query blocks): two query blocks go through the 128 query
+// rows of a step, rows 0..63 of the first set bit and 64..127 of the next one
+// (after an odd count the second half hands over P = 0, so it adds nothing).
+template <bool kHalfKeys, bool kSplit>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     AttnArgs a, int nbw, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) float st0s[2 * kBlockTokens];
   __shared__ __attribute__((aligned(1024))) float st1s[2 * kBlockTokens];
   __shared__ __attribute__((aligned(1024))) char xch[4 * 2 * 2048];  // [key slice][slot][2 KB]
-  __shared__ uint32_t mrow[2][kBlockTokens];
+  __shared__ uint32_t mrow[kBlockTokens];
   const Geom& g = a.g;
   // With condition frames the leading (condition) key blocks carry the
   // longest query lists; the contiguous per-XCD order would put them all on
@@ -552,22 +552,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int ks = w & 3;
   const bool ds_role = (w >> 2) != 0;
+  const int ks = kHalfKeys ? (w & 1) : (w & 3);  // key slice
+  const int qh = kHalfKeys ? ((w >> 1) & 1) : 0; // query half
+  const int xs_id = kHalfKeys ? (2 * ks + qh) : ks; // the P hand-off buffer of the wave pair
   const int n = lane & 31;
   const int gs = lane >> 5;
-  // The unit's first key block, the wave's key block and the wave's key slot.
-  int kb0, kbw, slot;
-  if constexpr (kPairKeys) {
-    kb0 = 2 * unit;
-    kbw = kb0 + (ks >> 1);
-    slot = 32 * (ks & 1) + n;
-  } else {
-    kb0 = unit >> a.unit_shift;
-    kbw = kb0;
-    slot = (unit & ((1 << a.unit_shift) - 1)) * kBlockTokens + 32 * ks + n;
-  }
-  if (kb0 >= g.nbk) return;
+  const int kb = unit >> a.unit_shift;
+  const int slot = (unit & ((1 << a.unit_shift) - 1)) * kBlockTokens + 32 * ks + n;
+  if (kb >= g.nbk) return;
 
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
   const uint32_t head_bytes = (uint32_t)g.S * (kHeadDim * 2);
@@ -581,13 +574,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const TileLanes tl = tile_lanes(g, w, lane);
 
   // P role keeps K of its keys (B operand of S), dS role keeps V (of dP). A
-  // key slot outside the grid (a partial block's, or the missing second
-  // block of an odd count) computes on the unit's first slot and is not
-  // written; query slots outside the grid have zero probabilities (their
-  // stats), so they add nothing to dK or dV.
-  const bool k_inside = kbw < g.nbk && (!g.partial || key_slot_valid(g, kbw, slot));
-  const int ktok = k_inside ? key_block_origin(a, kbw) + key_slot_offset(g, slot)
-                            : key_block_origin(a, kb0);
+  // key slot of a partial block outside the grid computes on the block's
+  // slot 0 and is not written; query slots outside the grid have zero
+  // probabilities (their stats), so they add nothing to dK or dV.
+  const bool k_inside = !g.partial || key_slot_valid(g, kb, slot);
+  const int ktok = key_block_origin(a, kb) + (k_inside ? key_slot_offset(g, slot) : 0);
   bf16x8 xf[8];
   {
     const bf16_bits* src = ds_role ? vp : kp;
@@ -596,29 +587,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       xf[s] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4*>(src + hoff + (size_t)ktok * kHeadDim + 16 * s + 8 * gs));
   }
-  if (t < nbw) {
-    mrow[0][t] = mask[((size_t)pair * g.nbk + kb0) * nbw + t];
-    if (kPairKeys)
-      mrow[1][t] = kb0 + 1 < g.nbk ? mask[((size_t)pair * g.nbk + kb0 + 1) * nbw + t] : 0u;
-  }
+  if (t < nbw) mrow[t] = mask[((size_t)pair * g.nbk + kb) * nbw + t];
   __syncthreads();
-  const int mine = kPairKeys ? (ks >> 1) : 0;  // the mask row of the wave's key block
   auto next_set = [&](int from) __attribute__((always_inline)) -> int {
     int wd = from >> 5;
     if (wd >= nbw) return g.nb;
-    auto word = [&](int i) __attribute__((always_inline)) {
-      return __builtin_amdgcn_readfirstlane(kPairKeys ? (mrow[0][i] | mrow[1][i]) : mrow[0][i]);
-    };
-    uint32_t bits = word(wd) & (0xffffffffu << (from & 31));
+    uint32_t bits = __builtin_amdgcn_readfirstlane(mrow[wd]) & (0xffffffffu << (from & 31));
     while (bits == 0u) {
       if (++wd >= nbw) return g.nb;
-      bits = word(wd);
+      bits = __builtin_amdgcn_readfirstlane(mrow[wd]);
     }
     return wd * 32 + __builtin_ctz(bits);
-  };
-  // Whether the wave's key block was selected by query block qb (< nb).
-  auto selected = [&](int qb) __attribute__((always_inline)) -> bool {
-    return ((__builtin_amdgcn_readfirstlane(mrow[mine][qb >> 5]) >> (qb & 31)) & 1u) != 0u;
   };
   // A step's query rows: block qa in rows 0..127 (128-token blocks), or qa in
   // rows 0..63 and qb2 (nb: none) in rows 64..127 (64-token blocks).
@@ -658,17 +637,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x16{};
 
-  // keep_lo / keep_hi: whether query rows 0..63 / 64..127 of the step belong
-  // to a query block that selected the wave's key block.
-  auto compute = [&](auto rolec, const char* qt, const char* dt, const float* sts, bool keep_lo,
+  // Sub-tiles TT0 .. TT0 + NT - 1 of a step (the query half is a template
+  // constant, so every LDS address is a per-lane offset plus an immediate).
+  // keep_hi: whether query rows 64..127 hold a query block (64-token blocks).
+  auto compute = [&](auto rolec, auto qhc, const char* qt, const char* dt, const float* sts,
                      bool keep_hi) __attribute__((always_inline)) {
     constexpr bool dsr = decltype(rolec)::value != 0;
+    constexpr int NT = kHalfKeys ? 2 : 4;
+    constexpr int TT0 = kHalfKeys ? 2 * decltype(qhc)::value : 0;
+    char* xbase = xch + xs_id * 4096;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      char* xs = xch + ks * 4096 + (tt & 1) * 2048;
+    for (int tl2 = 0; tl2 < NT; ++tl2) {
+      const int tt = TT0 + tl2;
+      char* xs = xbase + (tl2 & 1) * 2048;
       bf16x8 bop[2];
       if constexpr (!dsr) {
-        const bool keep = tt < 2 ? keep_lo : keep_hi;
         f32x16 sacc = f32x16{};
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma(row_operand(qt, tt, s, tl), xf[s], sacc);
@@ -683,9 +666,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
             const uint32_t pw =
                 pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i0], a.c_log2, -l2[0])),
                           __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i0 + 1], a.c_log2, -l2[1])));
-            // (With one 128+-token key block and 128-token query blocks every
-            // query block walked selected the wave's keys.)
-            packed[j2] = (kPairKeys || kSplit) && !keep ? 0u : pw;
+            packed[j2] = (kSplit && tt >= 2 && !keep_hi) ? 0u : pw;
           }
           bop[hh] = __builtin_bit_cast(bf16x8, packed);
           *reinterpret_cast<u32x4*>(xs + hh * 1024 + lane * 16) = packed;
@@ -721,7 +702,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     }
   };
 
-  auto run = [&](auto rolec) __attribute__((always_inline)) {
+  auto run = [&](auto rolec, auto qhc) __attribute__((always_inline)) {
     Rows cur = first_rows();
     if (cur.qa >= g.nb) return;
     load_rows(cur, q0s, d0s, st0s);
@@ -731,11 +712,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       workgroup_barrier();
       if (nxt.qa < g.nb) load_rows(nxt, b == 0 ? q1s : q0s, b == 0 ? d1s : d0s, b == 0 ? st1s : st0s);
-      const bool keep_lo = kPairKeys ? selected(cur.qa) : true;
-      const bool keep_hi = kSplit ? (cur.qb2 < g.nb && (!kPairKeys || selected(cur.qb2))) : keep_lo;
-      compute(rolec, reinterpret_cast<const char*>(b == 0 ? q0s : q1s),
-              reinterpret_cast<const char*>(b == 0 ? d0s : d1s), b == 0 ? st0s : st1s, keep_lo,
-              keep_hi);
+      compute(rolec, qhc, reinterpret_cast<const char*>(b == 0 ? q0s : q1s),
+              reinterpret_cast<const char*>(b == 0 ? d0s : d1s), b == 0 ? st0s : st1s,
+              !kSplit || cur.qb2 < g.nb);
       if (nxt.qa >= g.nb) return false;
       cur = nxt;
       nxt = next_rows(cur);
@@ -744,10 +723,35 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
     }
   };
-  if (ds_role)
-    run(std::integral_constant<int, 1>{});
-  else
-    run(std::integral_constant<int, 0>{});
+  // Every copy of the loop runs the same barriers, so the waves stay in step.
+  using std::integral_constant;
+  if (ds_role) {
+    if (qh == 0) run(integral_constant<int, 1>{}, integral_constant<int, 0>{});
+    else run(integral_constant<int, 1>{}, integral_constant<int, 1>{});
+  } else {
+    if (qh == 0) run(integral_constant<int, 0>{}, integral_constant<int, 0>{});
+    else run(integral_constant<int, 0>{}, integral_constant<int, 1>{});
+  }
+  if constexpr (kHalfKeys) {
+    // The two query halves of each (role, key slice) meet: the second half's
+    // wave leaves its partial sums in LDS (16 KB per wave, lane-contiguous
+    // words; the tile buffers are idle now), the first adds them and stores.
+    __syncthreads();
+    const int pslot = 2 * (ds_role ? 1 : 0) + ks;  // 0..3
+    float* part = reinterpret_cast<float*>(pslot < 2 ? q0s : d0s) + (pslot & 1) * (64 * 64);
+    if (qh == 1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) part[(u * 16 + i) * 64 + lane] = acc[u][i];
+    }
+    __syncthreads();
+    if (qh == 1) return;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[u][i] += part[(u * 16 + i) * 64 + lane];
+  }
   if (!k_inside) return;
   if (ds_role)
     store_rows(dkp + hoff + (size_t)ktok * kHeadDim, acc, g.scale, gs);
@@ -788,14 +792,14 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
 #undef BSA_LAUNCH_DQ
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dK/dV: one workgroup per 128-key unit (a unit of a key block of 128+
-  // tokens, or two 64-token key blocks).
+  // dK/dV: one workgroup per 128-key unit of a key block of 128+ tokens, or
+  // per 64-token key block.
   AttnArgs au = a;
-  const int units = mode == 2 ? (g.nbk + 1) / 2 : (g.nbk << a.unit_shift);
+  const int units = mode == 2 ? g.nbk : (g.nbk << a.unit_shift);
   au.nq8 = (units + 7) / 8 * 8;
   const dim3 grid_u((unsigned)((size_t)g.bh * au.nq8));
-#define BSA_LAUNCH_DKDV(PAIR, SPLIT)                                                            \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<PAIR, SPLIT>), grid_u, dim3(kBwdThreads), 0, stream, au, \
+#define BSA_LAUNCH_DKDV(HALF, SPLIT)                                                            \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<HALF, SPLIT>), grid_u, dim3(kBwdThreads), 0, stream, au, \
                      nbw, q, k, v, dout, stats, mask, dk, dv)
   if (mode == 2) {
     if (split) BSA_LAUNCH_DKDV(true, true);
