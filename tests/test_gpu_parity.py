@@ -401,6 +401,60 @@ def test_partial_blocks_dense_and_lse(chunk):
         assert np.abs(got - lse_r).max() <= 2.5e-3
 
 
+def test_longest_sequence_sampled():
+    """The longest sequence the boundary accepts (T*H*W < 2^24):
+    255 x 256 x 256 = 16,711,680 tokens, one head, so a head's K or V spans
+    4.28 GB and the tile loads' 32-bit byte offsets come within 17 MB of
+    2^32; the last row of blocks along t is partial (3 of 4 frames). Random
+    lists of 3 key blocks per query block (the last query block keeps the
+    last three key blocks, which sit at the top of the address range);
+    sampled query blocks against the oracle."""
+    import torch
+
+    from video_dit_block_bsa_amd.inputs import uniform_block_lists
+
+    T, H, W = 255, 256, 256
+    problem = Problem.make(T, H, W, 1)
+    g = PT.geometry(problem)
+    nb = g.num_blocks
+    assert nb == 64 * 64 * 32 and g.seq_len < (1 << 24)
+    _log(f"generating {T}x{H}x{W} ({g.seq_len} tokens), one head")
+    q, k, v = make_qkv(T, H, W, 1, kind="iid", seed=61)
+    idx, cnt = uniform_block_lists(nb, nb, 3, seed=62)
+    idx[nb - 1] = [nb - 3, nb - 2, nb - 1]
+    idx[0] = [0, nb // 2, nb - 1]
+    qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    out = PT.from_device(PT.run_attention(problem, qd, kd, vd, torch.from_numpy(idx).cuda(),
+                                          torch.from_numpy(cnt).cuda(), 3))
+    del qd, kd, vd
+    rng = np.random.default_rng(63)
+    sample = sorted({0, 1, nb // 2, nb - 33, nb - 2, nb - 1} |
+                    set(rng.choice(nb, size=6, replace=False).tolist()))
+    perm = O.block_token_order(g)
+    worst = 0.0
+    for i in sample:
+        blocks = [int(x) for x in idx[i]]
+        # Widen only the rows this query block touches; the oracle reads them
+        # through a block order remapped onto the widened rows.
+        need = [i] + blocks
+        sub_perm = np.full_like(perm, -1)
+        pos = 0
+        for b in dict.fromkeys(need):
+            t_b = O.block_tokens(perm, b, g.n)
+            slots = np.nonzero(perm[b * g.n:(b + 1) * g.n] >= 0)[0] + b * g.n
+            sub_perm[slots] = np.arange(pos, pos + t_b.size)
+            pos += t_b.size
+        uniq = np.concatenate([O.block_tokens(perm, b, g.n) for b in dict.fromkeys(need)])
+        qs, ks, vs = (O.bf16_bits_to_f64(a[0, 0][uniq]) for a in (q, k, v))
+        ref = O.attend_query_block(qs, ks, vs, g, i, blocks, SCALE, sub_perm, sub_perm)
+        got = O.bf16_bits_to_f64(out.reshape(q.shape)[0, 0][O.block_tokens(perm, i, g.n)])
+        err = np.abs(got - ref)
+        assert np.isfinite(got).all()
+        worst = max(worst, err.max())
+        assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS, (i, blocks)
+    _log(f"longest sequence: {len(sample)} sampled query blocks, max-abs {worst:.3e}")
+
+
 @pytest.mark.parametrize("name", ["480p", "720p", "long", "vc", "long_k64", "long_k256", "long_q64"])
 def test_full_size_workload(name):
     """Full-size workloads in the configuration the benchmark times: every

@@ -106,7 +106,7 @@ constexpr int kSlots = 5;                               // half-tile ring per wo
 // + l_b 2^(m_b-m)), m = max(m_a, m_b)). Every wave then issues half the MFMAs
 // of a unit, and the key half is a template constant inside the loop (two
 // copies), so each read still names its slot.
-template <bool kDense, bool kLse, int kKeyMode, bool kSplit>
+template <bool kDense, bool kLse, int kKeyMode, bool kSplit, bool kPartial>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const int32_t* __restrict__ idx,
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
 
   // A query slot of a partial block that lies outside the grid reads slot 0
   // (always inside) instead, and its row is never written.
-  const bool q_inside = !g.partial || block_slot_valid(g, qb, 32 * qh + n);
+  const bool q_inside = !kPartial || block_slot_valid(g, qb, 32 * qh + n);
   const int qtok = block_origin(a, qb) + (q_inside ? slot_offset(g, 32 * qh + n) : 0);
   bf16x8 qf[8];
 #pragma unroll
@@ -234,15 +234,48 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     }
   };
   // Half tile e (0: K lo, 1: K hi, 2: V lo, 3: V hi) of a unit into a slot.
+  // A row of a partial key block that lies outside the grid fetches row 0 of
+  // the block instead (inside the grid, so every address stays inside the
+  // tensor; its scores are masked, so the finite values it brings are
+  // multiplied by probability 0).
   auto load_half = [&](Cursor c, int e, bf16_bits* dst_slot) {
     const uint32_t base = unit_base(c, e & 1);
     char* dst = reinterpret_cast<char*>(dst_slot) + 16 * w * 256;
+    bool cut = false;
+    Extent ex = {0, 0, 0};
+    int jbase = 0;  // slot of row 0 of this half tile in its key block
+    if constexpr (kPartial) {
+      int kb;
+      if constexpr (kKeyMode == 2) {
+        kb = kb_at(((e & 1) && c.b < count) ? c.b : c.a);
+      } else {
+        kb = kb_at(c.a);
+        jbase = (kKeyMode == 1 ? c.b * kBlockTokens : 0) + kHalfRows * (e & 1);
+      }
+      ex = key_block_extent(a, kb);
+      cut = ex.t != g.ctk || ex.h != g.chk || ex.w != g.cwk;
+    }
+    // Bit x: row 16w + x of the half tile lies inside the grid (scalar work,
+    // only for a cut block).
+    uint32_t inside = 0xffffu;
+    if (cut) {
+      inside = 0u;
+      for (int x = 0; x < 16; ++x)
+        if (key_slot_inside(a, ex, jbase + 16 * w + x)) inside |= 1u << x;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       constexpr uint32_t sb64[4] = {0, 128, 64, 192};  // 64 * (i with its two bits swapped)
       const uint32_t row_s = (uint32_t)key_slot_offset(g, 4 * i) * (kHeadDim * 2);
+      uint32_t voff = e < 2 ? (k0 ^ sb64[i]) : (k0 ^ vx);
+      uint32_t soff = base + row_s;
+      if (cut) {
+        const bool in = ((inside >> (4 * i + (lane >> 4))) & 1u) != 0u;
+        voff = in ? voff + row_s : (uint32_t)(lane & 15) * 16u;
+        soff = base;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(e < 2 ? krs : vrs, (lds_void*)(dst + i * 1024), 16,
-                                               e < 2 ? (k0 ^ sb64[i]) : (k0 ^ vx), base + row_s, 0, 0);
+                                               voff, soff, 0, 0);
     }
   };
 
@@ -336,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
               for (int i = 0; i < 16; ++i) sacc[tt][i] = -INFINITY;
           }
         }
-        if (g.partial) {
+        if constexpr (kPartial) {
           // Keys of a partial block that lie outside the grid get -inf.
           // Half h of the unit (keys 64h .. 64h+63) holds slots base .. +63
           // of key block kb; accumulator value i of this wave's sub-tile tl
@@ -386,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
         // A wave may have seen only masked keys so far (m2 still -inf: the
         // empty half of a lone 64-token key block in split mode, or a unit
         // outside the grid): its probabilities are then exp2(-inf - 0) = 0.
-        const float msub = ((kSplit || g.partial) && m2 == -INFINITY) ? 0.f : m2;
+        const float msub = ((kSplit || kPartial) && m2 == -INFINITY) ? 0.f : m2;
 #pragma unroll
         for (int tt = 0; tt < kT; ++tt) {
 #pragma unroll
@@ -515,6 +548,9 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
   if (q_begin >= g.nb) return hipSuccess;
   dim3 grid((unsigned)((size_t)g.bh * ((g.nb - q_begin + 7) / 8 * 8)));
   const bool split = g.nq != kBlockTokens;
+  // Grids the chunks divide run kernels compiled without the partial-block
+  // code, which would otherwise cost them registers and time.
+  const bool part = g.partial != 0;
   if (dense) {
     // Dense attention walks all allowed keys in blocks of the query chunk.
     Geom gd = g;
@@ -527,23 +563,32 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
     gd.nk = g.nq;
     gd.cond_kblocks = g.cond_blocks;
     const AttnArgs a = make_attn_args(gd, 1, q_begin);
-    if (split)
-      hipLaunchKernelGGL((attn_kernel<true, false, 2, true>), grid, dim3(kThreads), 0, stream, a, q,
-                         k, v, idx, cnt, o, nullptr);
-    else
-      hipLaunchKernelGGL((attn_kernel<true, false, 0, false>), grid, dim3(kThreads), 0, stream, a, q,
-                         k, v, idx, cnt, o, nullptr);
+#define BSA_LAUNCH_DENSE(MODE, SPLIT, PART)                                                          \
+  hipLaunchKernelGGL((attn_kernel<true, false, MODE, SPLIT, PART>), grid, dim3(kThreads), 0, stream, \
+                     a, q, k, v, idx, cnt, o, nullptr)
+    if (split) {
+      if (part) BSA_LAUNCH_DENSE(2, true, true);
+      else BSA_LAUNCH_DENSE(2, true, false);
+    } else {
+      if (part) BSA_LAUNCH_DENSE(0, false, true);
+      else BSA_LAUNCH_DENSE(0, false, false);
+    }
+#undef BSA_LAUNCH_DENSE
     return hipGetLastError();
   }
   const AttnArgs a = make_attn_args(g, stride, q_begin);
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
-#define BSA_LAUNCH_ATTN(LSE, MODE, SPLIT)                                                          \
-  hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT>), grid, dim3(kThreads), 0, stream, a, q, \
-                     k, v, idx, cnt, o, lse)
-#define BSA_LAUNCH_ATTN_MODES(LSE, SPLIT)      \
-  if (mode == 0) BSA_LAUNCH_ATTN(LSE, 0, SPLIT); \
-  else if (mode == 1) BSA_LAUNCH_ATTN(LSE, 1, SPLIT); \
-  else BSA_LAUNCH_ATTN(LSE, 2, SPLIT)
+#define BSA_LAUNCH_ATTN(LSE, MODE, SPLIT)                                                      \
+  if (part)                                                                                     \
+    hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT, true>), grid, dim3(kThreads), 0,   \
+                       stream, a, q, k, v, idx, cnt, o, lse);                                   \
+  else                                                                                          \
+    hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT, false>), grid, dim3(kThreads), 0,  \
+                       stream, a, q, k, v, idx, cnt, o, lse)
+#define BSA_LAUNCH_ATTN_MODES(LSE, SPLIT)                \
+  if (mode == 0) { BSA_LAUNCH_ATTN(LSE, 0, SPLIT); }     \
+  else if (mode == 1) { BSA_LAUNCH_ATTN(LSE, 1, SPLIT); } \
+  else { BSA_LAUNCH_ATTN(LSE, 2, SPLIT); }
   if (lse) {
     if (split) { BSA_LAUNCH_ATTN_MODES(true, true); }
     else { BSA_LAUNCH_ATTN_MODES(true, false); }

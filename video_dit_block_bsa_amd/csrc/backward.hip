@@ -182,32 +182,51 @@ __device__ __forceinline__ TileLanes tile_lanes(const Geom& g, int w, int lane) 
   return t;
 }
 
-// Issues the four direct-to-LDS loads of this wave's 16 rows of the tile of
-// block `blk` (one of Q, K, V, dO through `rs`) into `tile`.
-__device__ __forceinline__ void load_tile(const AttnArgs& a, __amdgpu_buffer_rsrc_t rs,
-                                          const TileLanes& tl, int w, int blk, bf16_bits* tile) {
-  const uint32_t base = (uint32_t)block_origin(a, blk) * (kHeadDim * 2);
+// Issues the four direct-to-LDS loads of this wave's 16 rows (16w .. +15)
+// of a 128-row tile: row x holds slot jbase + (x & smask) of block `blk`
+// (a query block, or a key block with kKeys), whose slot 0 is token
+// `origin`; `lane0` is the lane's byte offset for the first load (ld or
+// ldk). A row of a partial block that lies outside the grid fetches row 0
+// of the block instead: every address stays inside the tensor, and the
+// values it brings are multiplied by probability 0 (their scores are masked
+// or their stats give P = 0).
+template <bool kKeys, bool kPartial>
+__device__ __forceinline__ void load_rows16(const AttnArgs& a, __amdgpu_buffer_rsrc_t rs,
+                                            uint32_t lane0, int w, int blk, int origin, int jbase,
+                                            int smask, bf16_bits* tile) {
+  const Geom& g = a.g;
+  const uint32_t base = (uint32_t)origin * (kHeadDim * 2);
   char* dst = reinterpret_cast<char*>(tile) + kRowsPerWave * w * 256;
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave / 4; ++i) {
-    const uint32_t row_s = (uint32_t)slot_offset(a.g, 4 * i) * (kHeadDim * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 1024), 16,
-                                             tl.ld ^ (uint32_t)(16 * i), base + row_s, 0, 0);
+  bool cut = false;
+  Extent ex = {0, 0, 0};
+  if (kPartial) {
+    ex = kKeys ? key_block_extent(a, blk) : block_extent(a, blk);
+    cut = kKeys ? (ex.t != g.ctk || ex.h != g.chk || ex.w != g.cwk)
+                : (ex.t != g.ct || ex.h != g.ch || ex.w != g.cw);
   }
-}
-
-// The same for a 128-key unit of a key block: `base_tok` is the token of the
-// unit's first slot; the rows follow the key chunk.
-__device__ __forceinline__ void load_key_tile(const AttnArgs& a, __amdgpu_buffer_rsrc_t rs,
-                                              const TileLanes& tl, int w, int base_tok,
-                                              bf16_bits* tile) {
-  const uint32_t base = (uint32_t)base_tok * (kHeadDim * 2);
-  char* dst = reinterpret_cast<char*>(tile) + kRowsPerWave * w * 256;
+  // Bit x of `inside`: row 16w + x of the tile lies inside the grid (worked
+  // out on the scalar unit; only for a cut block).
+  uint32_t inside = 0xffffu;
+  if (cut) {
+    inside = 0u;
+    for (int x = 0; x < kRowsPerWave; ++x) {
+      const int j = jbase + ((kRowsPerWave * w + x) & smask);
+      if (kKeys ? key_slot_inside(a, ex, j) : slot_inside(a, ex, j)) inside |= 1u << x;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kRowsPerWave / 4; ++i) {
-    const uint32_t row_s = (uint32_t)key_slot_offset(a.g, 4 * i) * (kHeadDim * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 1024), 16,
-                                             tl.ldk ^ (uint32_t)(16 * i), base + row_s, 0, 0);
+    const uint32_t row_s =
+        (uint32_t)(kKeys ? key_slot_offset(g, 4 * i) : slot_offset(g, 4 * i)) * (kHeadDim * 2);
+    uint32_t voff = lane0 ^ (uint32_t)(16 * i);
+    uint32_t soff = base + row_s;
+    if (cut) {
+      const int lane = threadIdx.x & 63;
+      const bool in = ((inside >> (4 * i + (lane >> 4))) & 1u) != 0u;
+      voff = in ? voff + row_s : (uint32_t)(lane & 15) * 16u;
+      soff = base;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 1024), 16, voff, soff, 0, 0);
   }
 }
 
@@ -278,7 +297,7 @@ __device__ __forceinline__ void xcd_block(const AttnArgs& a, int& pair, int& blk
 // V tiles are double-buffered in LDS (two separate objects each, the loop
 // unrolled by two so every read names its buffer at compile time and never
 // waits for the loads into the other one).
-template <int kKeyMode, bool kSplit>
+template <int kKeyMode, bool kSplit, bool kPartial>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
@@ -310,7 +329,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 
   // A query slot of a partial block outside the grid computes on slot 0 (its
   // stats make every probability 0) and is not written.
-  const bool q_inside = !g.partial || block_slot_valid(g, qb, 32 * qs + n);
+  const bool q_inside = !kPartial || block_slot_valid(g, qb, 32 * qs + n);
   const int qtok = block_origin(a, qb) + (q_inside ? slot_offset(g, 32 * qs + n) : 0);
   bf16x8 qf[8], df[8];
 #pragma unroll
@@ -354,16 +373,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
       return {next_valid(c.a + 1), 0};
     }
   };
-  // Token of the first slot that this wave's tile rows count from: waves 4..7
-  // stage rows 64..127, which in kKeyMode 2 are the upper block's (the lower
-  // one again when it is missing: those rows are never used).
-  auto wave_base = [&](Cursor c) __attribute__((always_inline)) -> int {
+  // This wave's rows of a unit's K or V tile: waves 4..7 stage rows 64..127,
+  // which in kKeyMode 2 are the upper block's (the lower one again when it is
+  // missing: those rows are never used).
+  auto load_unit = [&](Cursor c, __amdgpu_buffer_rsrc_t rs, bf16_bits* tile)
+                       __attribute__((always_inline)) {
     if constexpr (kKeyMode == 2) {
-      return key_block_origin(a, list[(w >= 4 && c.b < count) ? c.b : c.a]);
+      const int kb = list[(w >= 4 && c.b < count) ? c.b : c.a];
+      load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb, key_block_origin(a, kb), 0, kHalfTile - 1,
+                                  tile);
     } else if constexpr (kKeyMode == 1) {
-      return key_block_origin(a, list[c.a]) + key_slot_offset(g, c.b * kBlockTokens);
+      const int kb = list[c.a];
+      load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb,
+                                  key_block_origin(a, kb) + key_slot_offset(g, c.b * kBlockTokens),
+                                  c.b * kBlockTokens, kBlockTokens - 1, tile);
     } else {
-      return key_block_origin(a, list[c.a]);
+      const int kb = list[c.a];
+      load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb, key_block_origin(a, kb), 0,
+                                  kBlockTokens - 1, tile);
     }
   };
 
@@ -390,7 +417,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
         sacc[t2] = mfma(row_operand(kt, TT0 + t2, s, tl), qf[s], sacc[t2]);
         pacc[t2] = mfma(row_operand(vt, TT0 + t2, s, tl), df[s], pacc[t2]);
       }
-    if (g.partial) {
+    if constexpr (kPartial) {
       // Keys of a partial key block outside the grid: S = -inf, so P = 0.
       // Value i of sub-tile tt is key 32 tt + 16 (i/8) + 8 gs + i%8 of the
       // unit; the lane part goes through an empty asm so that nothing
@@ -438,8 +465,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   auto run = [&](auto kpc) __attribute__((always_inline)) {
     Cursor cur = first_unit();
     if (cur.a >= count) return;
-    load_key_tile(a, krs, tl, w, wave_base(cur), k0s);
-    load_key_tile(a, vrs, tl, w, wave_base(cur), v0s);
+    load_unit(cur, krs, k0s);
+    load_unit(cur, vrs, v0s);
     Cursor nxt = next_unit(cur);
     auto step = [&](auto bc) __attribute__((always_inline)) -> bool {
       constexpr int b = decltype(bc)::value;
@@ -452,8 +479,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       workgroup_barrier();
       if (nxt.a < count) {
-        load_key_tile(a, krs, tl, w, wave_base(nxt), kn);
-        load_key_tile(a, vrs, tl, w, wave_base(nxt), vn);
+        load_unit(nxt, krs, kn);
+        load_unit(nxt, vrs, vn);
       }
       compute(kpc, reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt), cur);
       if (nxt.a >= count) return false;
@@ -528,7 +555,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 // kSplit (64-token query blocks): two query blocks go through the 128 query
 // rows of a step, rows 0..63 of the first set bit and 64..127 of the next one
 // (after an odd count the second half hands over P = 0, so it adds nothing).
-template <bool kHalfKeys, bool kSplit>
+template <bool kHalfKeys, bool kSplit, bool kPartial>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     AttnArgs a, int nbw, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
@@ -577,7 +604,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   // key slot of a partial block outside the grid computes on the block's
   // slot 0 and is not written; query slots outside the grid have zero
   // probabilities (their stats), so they add nothing to dK or dV.
-  const bool k_inside = !g.partial || key_slot_valid(g, kb, slot);
+  const bool k_inside = !kPartial || key_slot_valid(g, kb, slot);
   const int ktok = key_block_origin(a, kb) + (k_inside ? key_slot_offset(g, slot) : 0);
   bf16x8 xf[8];
   {
@@ -615,8 +642,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   auto load_rows = [&](Rows r, bf16_bits* qdst, bf16_bits* ddst, float* sdst)
                        __attribute__((always_inline)) {
     const int blk = (kSplit && w >= 4 && r.qb2 < g.nb) ? r.qb2 : r.qa;
-    load_tile(a, qrs, tl, w, blk, qdst);
-    load_tile(a, drs, tl, w, blk, ddst);
+    load_rows16<false, kPartial>(a, qrs, tl.ld, w, blk, block_origin(a, blk), 0, g.nq - 1, qdst);
+    load_rows16<false, kPartial>(a, drs, tl.ld, w, blk, block_origin(a, blk), 0, g.nq - 1, ddst);
     if (w == 0) {
       // stats of a block: lse*log2(e) at floats 0.., D at floats 128... For
       // two 64-token blocks, lanes 0..15 / 16..31 fetch the lse of the first
@@ -776,19 +803,25 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
   if (e != hipSuccess) return e;
   const bool split = g.nq != kBlockTokens;
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
+  const bool part = g.partial != 0;
   const dim3 grid((unsigned)((size_t)g.bh * a.nq8));
-#define BSA_LAUNCH_DQ(MODE, SPLIT)                                                                  \
-  hipLaunchKernelGGL((bwd_dq_kernel<MODE, SPLIT>), grid, dim3(kBwdThreads), 0, stream, a, q, k, v, \
-                     dout, stats, idx, cnt, dq)
+  // Grids the chunks divide run kernels compiled without the partial-block
+  // code (the default kernels sit at the 256-VGPR limit).
+#define BSA_LAUNCH_DQ(MODE, SPLIT, PART)                                                      \
+  hipLaunchKernelGGL((bwd_dq_kernel<MODE, SPLIT, PART>), grid, dim3(kBwdThreads), 0, stream, a, \
+                     q, k, v, dout, stats, idx, cnt, dq)
+#define BSA_LAUNCH_DQ_P(MODE, SPLIT) \
+  if (part) BSA_LAUNCH_DQ(MODE, SPLIT, true); else BSA_LAUNCH_DQ(MODE, SPLIT, false)
   if (split) {
-    if (mode == 0) BSA_LAUNCH_DQ(0, true);
-    else if (mode == 1) BSA_LAUNCH_DQ(1, true);
-    else BSA_LAUNCH_DQ(2, true);
+    if (mode == 0) { BSA_LAUNCH_DQ_P(0, true); }
+    else if (mode == 1) { BSA_LAUNCH_DQ_P(1, true); }
+    else { BSA_LAUNCH_DQ_P(2, true); }
   } else {
-    if (mode == 0) BSA_LAUNCH_DQ(0, false);
-    else if (mode == 1) BSA_LAUNCH_DQ(1, false);
-    else BSA_LAUNCH_DQ(2, false);
+    if (mode == 0) { BSA_LAUNCH_DQ_P(0, false); }
+    else if (mode == 1) { BSA_LAUNCH_DQ_P(1, false); }
+    else { BSA_LAUNCH_DQ_P(2, false); }
   }
+#undef BSA_LAUNCH_DQ_P
 #undef BSA_LAUNCH_DQ
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -798,16 +831,19 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
   const int units = mode == 2 ? g.nbk : (g.nbk << a.unit_shift);
   au.nq8 = (units + 7) / 8 * 8;
   const dim3 grid_u((unsigned)((size_t)g.bh * au.nq8));
-#define BSA_LAUNCH_DKDV(HALF, SPLIT)                                                            \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<HALF, SPLIT>), grid_u, dim3(kBwdThreads), 0, stream, au, \
+#define BSA_LAUNCH_DKDV(HALF, SPLIT, PART)                                                          \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<HALF, SPLIT, PART>), grid_u, dim3(kBwdThreads), 0, stream, au, \
                      nbw, q, k, v, dout, stats, mask, dk, dv)
+#define BSA_LAUNCH_DKDV_P(HALF, SPLIT) \
+  if (part) BSA_LAUNCH_DKDV(HALF, SPLIT, true); else BSA_LAUNCH_DKDV(HALF, SPLIT, false)
   if (mode == 2) {
-    if (split) BSA_LAUNCH_DKDV(true, true);
-    else BSA_LAUNCH_DKDV(true, false);
+    if (split) { BSA_LAUNCH_DKDV_P(true, true); }
+    else { BSA_LAUNCH_DKDV_P(true, false); }
   } else {
-    if (split) BSA_LAUNCH_DKDV(false, true);
-    else BSA_LAUNCH_DKDV(false, false);
+    if (split) { BSA_LAUNCH_DKDV_P(false, true); }
+    else { BSA_LAUNCH_DKDV_P(false, false); }
   }
+#undef BSA_LAUNCH_DKDV_P
 #undef BSA_LAUNCH_DKDV
   return hipGetLastError();
 }

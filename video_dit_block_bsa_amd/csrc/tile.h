@@ -26,6 +26,7 @@ struct AttnArgs {
   uint32_t mag_nhwk;
   int unit_shift;     // log2 of the 128-key units per key block (key blocks of 256+ tokens)
   int lcwk, lchk;     // log2 of the key chunk's w and h extents
+  int lcw, lch;       // the same for the query chunk
   float c_log2;       // scale * log2(e)
 };
 
@@ -76,6 +77,20 @@ __device__ __forceinline__ Extent key_block_extent(const AttnArgs& a, int i) {
   return {min(g.ctk, g.T - bt * g.ctk), min(g.chk, g.H - bh * g.chk), min(g.cwk, g.W - bw * g.cwk)};
 }
 
+// The same for query block i (query chunk).
+__device__ __forceinline__ Extent block_extent(const AttnArgs& a, int i) {
+  const Geom& g = a.g;
+  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhw);
+  const int rem = i - bt * g.nH * g.nW;
+  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nw);
+  const int bw = rem - bh * g.nW;
+  return {min(g.ct, g.T - bt * g.ct), min(g.ch, g.H - bh * g.ch), min(g.cw, g.W - bw * g.cw)};
+}
+
+__device__ __forceinline__ bool slot_inside(const AttnArgs& a, const Extent& e, int j) {
+  return (j & (a.g.cw - 1)) < e.w && ((j >> a.lcw) & (a.g.ch - 1)) < e.h && (j >> (a.lcw + a.lch)) < e.t;
+}
+
 // Whether slot j of a key block with extents e lies inside the grid (key
 // chunk sides are powers of two).
 __device__ __forceinline__ bool key_slot_inside(const AttnArgs& a, const Extent& e, int j) {
@@ -117,6 +132,10 @@ inline AttnArgs make_attn_args(const Geom& g, int stride, int q_begin = 0) {
   for (int m = g.cwk; m > 1; m >>= 1) ++a.lcwk;
   a.lchk = 0;
   for (int m = g.chk; m > 1; m >>= 1) ++a.lchk;
+  a.lcw = 0;
+  for (int m = g.cw; m > 1; m >>= 1) ++a.lcw;
+  a.lch = 0;
+  for (int m = g.ch; m > 1; m >>= 1) ++a.lch;
   a.c_log2 = g.scale * 1.4426950408889634f;
   return a;
 }

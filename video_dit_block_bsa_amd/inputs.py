@@ -17,9 +17,9 @@ Recipes
 
 * ``make_grad``: the output gradient dL/dO of the backward workloads, i.i.d.
   N(0, 1) per element, from its own seed sequence.
-* ``random_block_lists``: key-block lists drawn uniformly without
-  replacement (for backward tests that fix the selection instead of
-  deriving it from Q and K).
+* ``random_block_lists``, ``uniform_block_lists``: key-block lists drawn
+  uniformly without replacement (for tests that fix the selection instead
+  of deriving it from Q and K).
 
 All values are rounded from float32 to bfloat16 with round-to-nearest-even.
 Each (batch, head) draws from its own child of ``SeedSequence(seed)``, so any
@@ -40,10 +40,17 @@ NOISE = 0.3
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits.
+    Works through the array in slices so that the temporaries stay small."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    flat = u.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    step = 1 << 24
+    for i in range(0, flat.size, step):
+        c = flat[i:i + step]
+        bias = np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1))
+        out[i:i + step] = (c + bias) >> np.uint32(16)
+    return out.reshape(u.shape)
 
 
 def _circulant_gauss(n: int) -> np.ndarray:
@@ -76,8 +83,14 @@ def _one_head(kind: str, seq: np.random.SeedSequence, T: int, H: int, W: int, d:
     s_f, s_q, s_k, s_v = seq.spawn(4)
     S = T * H * W
     if kind == "iid":
-        q = np.random.default_rng(s_q).standard_normal((S, d), dtype=np.float32)
-        k = np.random.default_rng(s_k).standard_normal((S, d), dtype=np.float32)
+        # Three independent streams: drawn (and rounded) in parallel threads,
+        # with the same values as drawing them one after the other.
+        def draw(stream):
+            return f32_to_bf16_bits(np.random.default_rng(stream).standard_normal((S, d), dtype=np.float32))
+
+        with ThreadPoolExecutor(max_workers=3) as ex:
+            q, k, v = ex.map(draw, (s_q, s_k, s_v))
+        return q, k, v
     elif kind == "field":
         f = _smooth_field(np.random.default_rng(s_f), T, H, W, d)
         q = np.random.default_rng(s_q).standard_normal((S, d), dtype=np.float32)
@@ -152,6 +165,20 @@ def make_grad(T: int, H: int, W: int, heads: int, head_dim: int = 128, batch: in
     with ThreadPoolExecutor(max_workers=max(1, n_threads)) as ex:
         list(ex.map(work, range(batch * heads)))
     return out
+
+
+def uniform_block_lists(rows: int, n_blocks: int, count: int, seed: int = 0):
+    """`count` distinct ids per row drawn uniformly from range(n_blocks), in
+    ascending order (for very many rows: vectorised draws, rows with a
+    repeated id drawn again). Returns (idx int32 [rows, count], cnt int32 [rows])."""
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.integers(0, n_blocks, size=(rows, count)), axis=1)
+    while True:
+        bad = np.nonzero((np.diff(idx, axis=1) == 0).any(axis=1))[0]
+        if bad.size == 0:
+            break
+        idx[bad] = np.sort(rng.integers(0, n_blocks, size=(bad.size, count)), axis=1)
+    return idx.astype(np.int32), np.full(rows, count, dtype=np.int32)
 
 
 def random_block_lists(allowed, stride: int, counts, seed: int = 0):
