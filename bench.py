@@ -37,8 +37,16 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel's source without comments and blank
+    lines, so that only a change to the code itself retires a counter
+    record."""
+    code = []
+    with open(KERNEL_SOURCE, encoding="utf-8") as f:
+        for line in f:
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def traffic_for(workload_name: str):

@@ -93,11 +93,13 @@ constexpr int kSlots = 5;                               // half-tile ring per wo
 // A unit's slot offsets are those of its first slot plus those of its slot
 // index (power-of-two chunk sides make the offset linear in the index bits).
 //
-// Partial blocks (a chunk that does not divide the grid: "3D block
-// partitioning" counts blocks with ceilings): a query slot outside the grid
+// kPartial (a chunk that does not divide the grid: "3D block partitioning"
+// counts blocks with ceilings, so the last block along a cut axis holds only
+// the tokens of its box inside the grid): a query slot outside the grid
 // computes on the block's slot 0 and is never written; the scores of key
-// slots outside the grid are set to -inf, behind a wave-uniform test per key
-// block, so blocks inside the grid cost one scalar comparison.
+// slots outside the grid are set to -inf; a tile row outside the grid fetches
+// row 0 of its block, so every load stays inside the tensor. Grids the chunks
+// divide use the instantiation without any of this.
 //
 // kSplit serves query blocks of 64 tokens: wave w takes queries 32(w%2) ..
 // +31 and key half w/2 (keys 0..63 or 64..127) of every unit, keeps its own
