@@ -188,7 +188,7 @@ size_t bsa_attention_bwd_workspace_bytes(const bsa_problem* problem);
  *   o, lse        as written by bsa_attention_lse for the same q, k, v, idx, cnt.
  *   dout          bf16 [batch, heads, S, 128]: dL/do.
  *   idx, cnt      the forward's key-block lists. The valid ids of a row must
- *                 be distinct (bsa_select's are); ids outside [0, Nb) are
+ *                 be distinct (bsa_select's are); ids outside [0, Nk) are
  *                 skipped and cnt is clamped to [0, idx_stride], as in the
  *                 forward.
  *   dq, dk, dv    bf16 [batch, heads, S, 128] out, every element written
