@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "BSA effective TFLOP/s & ms/layer at 720p-scale (~92K/215K tokens), % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "video_dit_block_bsa_amd", "csrc", "attention.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "video_dit_block_bsa_amd", "csrc", f)
+                  for f in ("attention.hip", "tile.h", "common.h")]
 
 
 def log(*a):
@@ -37,15 +38,16 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the attention kernel's source without comments and blank
-    lines, so that only a change to the code itself retires a counter
-    record."""
+    """Hash of the attention kernel's sources (the kernel file and the
+    headers it includes) without comments and blank lines, so that only a
+    change to the code itself retires a counter record."""
     code = []
-    with open(KERNEL_SOURCE, encoding="utf-8") as f:
-        for line in f:
-            line = line.split("//", 1)[0].rstrip()
-            if line:
-                code.append(line)
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                line = line.split("//", 1)[0].rstrip()
+                if line:
+                    code.append(line)
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 

@@ -226,6 +226,16 @@ def test_64_token_blocks(grid, chunk, key_chunk, k_sel, cond):
           key_chunk=key_chunk)
 
 
+@pytest.mark.parametrize("grid,chunk,key_chunk,k_sel,cond", [
+    ((8, 4, 8), (4, 4, 8), None, 2, 0),          # nH = nW = 1
+    ((9, 10, 16), (1, 8, 16), None, 3, 0),       # nW = 1, cut along h
+    ((6, 21, 32), (2, 2, 16), (1, 8, 32), 4, 2), # key grid one block wide
+])
+def test_one_block_wide_grids(grid, chunk, key_chunk, k_sel, cond):
+    """Block grids one block wide: block ids divided by 1 take their own path."""
+    _case(*grid, 2, k_sel, chunk=chunk, seed=73, cond_frames=cond, key_chunk=key_chunk)
+
+
 def test_many_blocks_one_key_block_popular():
     """One key block kept by every query block (long mask rows) and rows of
     different lengths."""

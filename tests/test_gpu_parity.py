@@ -359,6 +359,27 @@ def test_partial_blocks(grid, chunk, key_chunk, params, cond):
     _run_and_compare(problem, params, q, k, v)
 
 
+# Block grids one block wide (or one block per frame): the kernels divide
+# block ids by nW and nH*nW, and a divisor of 1 takes its own path.
+@pytest.mark.parametrize("grid,chunk,key_chunk,params,cond", [
+    ((8, 4, 8), (4, 4, 8), None, SelectParams.topk(2), 0),            # nH = nW = 1
+    ((9, 10, 16), (1, 8, 16), None, SelectParams.cdf(0.7, 2, 6), 0),  # nW = 1, cut along h
+    ((6, 21, 32), (2, 2, 16), (1, 8, 32), SelectParams.topk(6), 2),   # key grid one block wide
+    ((12, 5, 7), (4, 4, 8), (2, 4, 8), SelectParams.topk(3), 4),      # cut to one block per frame
+])
+def test_one_block_wide_grids(grid, chunk, key_chunk, params, cond):
+    T, H, W = grid
+    q, k, v = make_qkv(T, H, W, 2, kind="iid", seed=71)
+    problem = Problem.make(T, H, W, 2, chunk=chunk, cond_frames=cond, key_chunk=key_chunk)
+    _run_and_compare(problem, params, q, k, v)
+    dense = PT.from_device(PT.run_dense(problem, *(PT.to_device(a) for a in (q, k, v))))
+    g = PT.geometry(problem)
+    for h in range(2):
+        ref = O.dense_head(*(O.bf16_bits_to_f64(a[0, h]) for a in (q, k, v)), g, SCALE)
+        err = np.abs(O.bf16_bits_to_f64(dense.reshape(q.shape)[0, h]) - ref)
+        assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS
+
+
 @pytest.mark.parametrize("chunk", [(4, 4, 8), (2, 4, 8)])
 def test_partial_blocks_dense_and_lse(chunk):
     """Partial grid with condition frames: dense attention against the

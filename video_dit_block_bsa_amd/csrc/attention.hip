@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   // A query slot of a partial block that lies outside the grid reads slot 0
   // (always inside) instead, and its row is never written.
   const bool q_inside = !kPartial || block_slot_valid(g, qb, 32 * qh + n);
-  const int qtok = block_origin(a, qb) + (q_inside ? slot_offset(g, 32 * qh + n) : 0);
+  const int qtok = block_origin<kPartial>(a, qb) + (q_inside ? slot_offset(g, 32 * qh + n) : 0);
   bf16x8 qf[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
@@ -227,12 +227,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   auto unit_base = [&](Cursor c, int h) -> uint32_t {
     if constexpr (kKeyMode == 2) {
       const int p = (h != 0 && c.b < count) ? c.b : c.a;
-      return (uint32_t)key_block_origin(a, kb_at(p)) * (kHeadDim * 2);
+      return (uint32_t)key_block_origin<kPartial>(a, kb_at(p)) * (kHeadDim * 2);
     } else if constexpr (kKeyMode == 1) {
-      return (uint32_t)(key_block_origin(a, kb_at(c.a)) + key_slot_offset(g, c.b * kBlockTokens)) *
-                 (kHeadDim * 2) + h * half_off;
+      return (uint32_t)(key_block_origin<kPartial>(a, kb_at(c.a)) +
+                        key_slot_offset(g, c.b * kBlockTokens)) * (kHeadDim * 2) +
+             h * half_off;
     } else {
-      return (uint32_t)key_block_origin(a, kb_at(c.a)) * (kHeadDim * 2) + h * half_off;
+      return (uint32_t)key_block_origin<kPartial>(a, kb_at(c.a)) * (kHeadDim * 2) + h * half_off;
     }
   };
   // Half tile e (0: K lo, 1: K hi, 2: V lo, 3: V hi) of a unit into a slot.
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
         kb = kb_at(c.a);
         jbase = (kKeyMode == 1 ? c.b * kBlockTokens : 0) + kHalfRows * (e & 1);
       }
-      ex = key_block_extent(a, kb);
+      ex = key_block_extent<kPartial>(a, kb);
       cut = ex.t != g.ctk || ex.h != g.chk || ex.w != g.cwk;
     }
     // Bit x: row 16w + x of the half tile lies inside the grid (scalar work,
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
           // of key block kb; accumulator value i of this wave's sub-tile tl
           // of that half is key 32 tl + 16 (i/8) + 8 gs + i%8 of the half.
           auto mask_half = [&](int h, int kb, int base) {
-            const Extent e = key_block_extent(a, kb);
+            const Extent e = key_block_extent<kPartial>(a, kb);
             if (e.t == g.ctk && e.h == g.chk && e.w == g.cwk) return;
             // The lane's offset passes through an empty asm so that nothing
             // derived from it is hoisted out of the loop (64 live registers).
@@ -550,9 +551,10 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
   if (q_begin >= g.nb) return hipSuccess;
   dim3 grid((unsigned)((size_t)g.bh * ((g.nb - q_begin + 7) / 8 * 8)));
   const bool split = g.nq != kBlockTokens;
-  // Grids the chunks divide run kernels compiled without the partial-block
-  // code, which would otherwise cost them registers and time.
-  const bool part = g.partial != 0;
+  // Grids the chunks divide (with more than one block along w and within a
+  // frame) run kernels compiled without the general code, which would
+  // otherwise cost them registers and time.
+  bool part = needs_general(g);
   if (dense) {
     // Dense attention walks all allowed keys in blocks of the query chunk.
     Geom gd = g;
@@ -565,6 +567,7 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
     gd.nk = g.nq;
     gd.cond_kblocks = g.cond_blocks;
     const AttnArgs a = make_attn_args(gd, 1, q_begin);
+    part = needs_general(gd);
 #define BSA_LAUNCH_DENSE(MODE, SPLIT, PART)                                                          \
   hipLaunchKernelGGL((attn_kernel<true, false, MODE, SPLIT, PART>), grid, dim3(kThreads), 0, stream, \
                      a, q, k, v, idx, cnt, o, nullptr)

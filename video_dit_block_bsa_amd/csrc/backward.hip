@@ -200,7 +200,7 @@ __device__ __forceinline__ void load_rows16(const AttnArgs& a, __amdgpu_buffer_r
   bool cut = false;
   Extent ex = {0, 0, 0};
   if (kPartial) {
-    ex = kKeys ? key_block_extent(a, blk) : block_extent(a, blk);
+    ex = kKeys ? key_block_extent<kPartial>(a, blk) : block_extent<kPartial>(a, blk);
     cut = kKeys ? (ex.t != g.ctk || ex.h != g.chk || ex.w != g.cwk)
                 : (ex.t != g.ct || ex.h != g.ch || ex.w != g.cw);
   }
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   // A query slot of a partial block outside the grid computes on slot 0 (its
   // stats make every probability 0) and is not written.
   const bool q_inside = !kPartial || block_slot_valid(g, qb, 32 * qs + n);
-  const int qtok = block_origin(a, qb) + (q_inside ? slot_offset(g, 32 * qs + n) : 0);
+  const int qtok = block_origin<kPartial>(a, qb) + (q_inside ? slot_offset(g, 32 * qs + n) : 0);
   bf16x8 qf[8], df[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -380,16 +380,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
                        __attribute__((always_inline)) {
     if constexpr (kKeyMode == 2) {
       const int kb = list[(w >= 4 && c.b < count) ? c.b : c.a];
-      load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb, key_block_origin(a, kb), 0, kHalfTile - 1,
-                                  tile);
+      load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb, key_block_origin<kPartial>(a, kb), 0,
+                                  kHalfTile - 1, tile);
     } else if constexpr (kKeyMode == 1) {
       const int kb = list[c.a];
       load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb,
-                                  key_block_origin(a, kb) + key_slot_offset(g, c.b * kBlockTokens),
+                                  key_block_origin<kPartial>(a, kb) +
+                                      key_slot_offset(g, c.b * kBlockTokens),
                                   c.b * kBlockTokens, kBlockTokens - 1, tile);
     } else {
       const int kb = list[c.a];
-      load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb, key_block_origin(a, kb), 0,
+      load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb, key_block_origin<kPartial>(a, kb), 0,
                                   kBlockTokens - 1, tile);
     }
   };
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
       // Value i of sub-tile tt is key 32 tt + 16 (i/8) + 8 gs + i%8 of the
       // unit; the lane part goes through an empty asm so that nothing
       // derived from it is hoisted out of the loop.
-      const Extent e = key_block_extent(a, list[kUpper ? un.b : un.a]);
+      const Extent e = key_block_extent<kPartial>(a, list[kUpper ? un.b : un.a]);
       if (e.t != g.ctk || e.h != g.chk || e.w != g.cwk) {
         int lb = (kKeyMode == 1 ? un.b * kBlockTokens : 0) - (kUpper ? kHalfTile : 0) + 8 * gs;
         asm volatile("" : "+v"(lb));
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   // slot 0 and is not written; query slots outside the grid have zero
   // probabilities (their stats), so they add nothing to dK or dV.
   const bool k_inside = !kPartial || key_slot_valid(g, kb, slot);
-  const int ktok = key_block_origin(a, kb) + (k_inside ? key_slot_offset(g, slot) : 0);
+  const int ktok = key_block_origin<kPartial>(a, kb) + (k_inside ? key_slot_offset(g, slot) : 0);
   bf16x8 xf[8];
   {
     const bf16_bits* src = ds_role ? vp : kp;
@@ -642,8 +643,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   auto load_rows = [&](Rows r, bf16_bits* qdst, bf16_bits* ddst, float* sdst)
                        __attribute__((always_inline)) {
     const int blk = (kSplit && w >= 4 && r.qb2 < g.nb) ? r.qb2 : r.qa;
-    load_rows16<false, kPartial>(a, qrs, tl.ld, w, blk, block_origin(a, blk), 0, g.nq - 1, qdst);
-    load_rows16<false, kPartial>(a, drs, tl.ld, w, blk, block_origin(a, blk), 0, g.nq - 1, ddst);
+    const int origin = block_origin<kPartial>(a, blk);
+    load_rows16<false, kPartial>(a, qrs, tl.ld, w, blk, origin, 0, g.nq - 1, qdst);
+    load_rows16<false, kPartial>(a, drs, tl.ld, w, blk, origin, 0, g.nq - 1, ddst);
     if (w == 0) {
       // stats of a block: lse*log2(e) at floats 0.., D at floats 128... For
       // two 64-token blocks, lanes 0..15 / 16..31 fetch the lse of the first
@@ -803,10 +805,11 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
   if (e != hipSuccess) return e;
   const bool split = g.nq != kBlockTokens;
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
-  const bool part = g.partial != 0;
+  const bool part = needs_general(g);
   const dim3 grid((unsigned)((size_t)g.bh * a.nq8));
-  // Grids the chunks divide run kernels compiled without the partial-block
-  // code (the default kernels sit at the 256-VGPR limit).
+  // Grids the chunks divide (with more than one block along w and within a
+  // frame) run kernels compiled without the general code (the default
+  // kernels sit at the 256-VGPR limit).
 #define BSA_LAUNCH_DQ(MODE, SPLIT, PART)                                                      \
   hipLaunchKernelGGL((bwd_dq_kernel<MODE, SPLIT, PART>), grid, dim3(kBwdThreads), 0, stream, a, \
                      q, k, v, dout, stats, idx, cnt, dq)

@@ -90,6 +90,13 @@ __device__ __forceinline__ bool key_slot_valid(const Geom& g, int i, int j) {
          bw * g.cwk + j % g.cwk < g.W;
 }
 
+// Whether a problem needs the general kernel instantiations: partial
+// blocks, or a block count of 1 along w or within a frame (the fast ones
+// divide block ids by magic numbers that need a divisor of 2 or more).
+inline bool needs_general(const Geom& g) {
+  return g.partial || g.nW == 1 || g.nH * g.nW == 1 || g.nWk == 1 || g.nHk * g.nWk == 1;
+}
+
 // Number of leading key blocks query block i may select (block-causal:
 // condition query blocks see the condition key blocks only).
 __device__ __forceinline__ int allowed_key_blocks(const Geom& g, int i) {

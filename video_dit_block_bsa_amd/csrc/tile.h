@@ -20,8 +20,8 @@ struct AttnArgs {
   int stride;
   int q_begin;        // first query block of the launch (the others are skipped)
   int nq8;            // query blocks of the launch per head, rounded up to a multiple of 8
-  uint32_t mag_nw;    // floor(2^32 / nW) + 1
-  uint32_t mag_nhw;   // floor(2^32 / (nH*nW)) + 1
+  uint32_t mag_nw;    // floor(2^32 / nW) + 1, or 0 when nW = 1 (see div_magic)
+  uint32_t mag_nhw;   // floor(2^32 / (nH*nW)) + 1, or 0 when nH*nW = 1
   uint32_t mag_nwk;   // the same for the key-block grid
   uint32_t mag_nhwk;
   int unit_shift;     // log2 of the 128-key units per key block (key blocks of 256+ tokens)
@@ -30,12 +30,28 @@ struct AttnArgs {
   float c_log2;       // scale * log2(e)
 };
 
+// x / d with m = magic(d): the high half of x * m, exact for the ranges the
+// host checks. A divisor of 1 (whose magic would not fit in 32 bits) is
+// encoded as m = 0 and handled only when kGeneral is set: the host launches
+// the general kernels (the kPartial instantiations) for any grid with a
+// block count of 1 along w or in a frame.
+template <bool kGeneral>
+__device__ __forceinline__ int div_magic(int x, uint32_t m) {
+  if constexpr (kGeneral) return m ? (int)__umulhi((uint32_t)x, m) : x;
+  return (int)__umulhi((uint32_t)x, m);
+}
+
+inline uint32_t magic(int d) {
+  return d == 1 ? 0u : (uint32_t)(0x100000000ull / (uint64_t)d + 1);
+}
+
 // Latent-order token of the first slot of block i.
+template <bool kGeneral = false>
 __device__ __forceinline__ int block_origin(const AttnArgs& a, int i) {
   const Geom& g = a.g;
-  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhw);
+  const int bt = div_magic<kGeneral>(i, a.mag_nhw);
   const int rem = i - bt * g.nH * g.nW;
-  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nw);
+  const int bh = div_magic<kGeneral>(rem, a.mag_nw);
   const int bw = rem - bh * g.nW;
   return ((bt * g.ct) * g.H + bh * g.ch) * g.W + bw * g.cw;
 }
@@ -48,11 +64,12 @@ __device__ __forceinline__ int slot_offset(const Geom& g, int j) {
 }
 
 // The same two for key blocks (key chunk and key-block grid).
+template <bool kGeneral = false>
 __device__ __forceinline__ int key_block_origin(const AttnArgs& a, int i) {
   const Geom& g = a.g;
-  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhwk);
+  const int bt = div_magic<kGeneral>(i, a.mag_nhwk);
   const int rem = i - bt * g.nHk * g.nWk;
-  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nwk);
+  const int bh = div_magic<kGeneral>(rem, a.mag_nwk);
   const int bw = rem - bh * g.nWk;
   return ((bt * g.ctk) * g.H + bh * g.chk) * g.W + bw * g.cwk;
 }
@@ -68,21 +85,23 @@ __device__ __forceinline__ int key_slot_offset(const Geom& g, int j) {
 struct Extent {
   int t, h, w;
 };
+template <bool kGeneral = false>
 __device__ __forceinline__ Extent key_block_extent(const AttnArgs& a, int i) {
   const Geom& g = a.g;
-  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhwk);
+  const int bt = div_magic<kGeneral>(i, a.mag_nhwk);
   const int rem = i - bt * g.nHk * g.nWk;
-  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nwk);
+  const int bh = div_magic<kGeneral>(rem, a.mag_nwk);
   const int bw = rem - bh * g.nWk;
   return {min(g.ctk, g.T - bt * g.ctk), min(g.chk, g.H - bh * g.chk), min(g.cwk, g.W - bw * g.cwk)};
 }
 
 // The same for query block i (query chunk).
+template <bool kGeneral = false>
 __device__ __forceinline__ Extent block_extent(const AttnArgs& a, int i) {
   const Geom& g = a.g;
-  const int bt = (int)__umulhi((uint32_t)i, a.mag_nhw);
+  const int bt = div_magic<kGeneral>(i, a.mag_nhw);
   const int rem = i - bt * g.nH * g.nW;
-  const int bh = (int)__umulhi((uint32_t)rem, a.mag_nw);
+  const int bh = div_magic<kGeneral>(rem, a.mag_nw);
   const int bw = rem - bh * g.nW;
   return {min(g.ct, g.T - bt * g.ct), min(g.ch, g.H - bh * g.ch), min(g.cw, g.W - bw * g.cw)};
 }
@@ -122,10 +141,10 @@ inline AttnArgs make_attn_args(const Geom& g, int stride, int q_begin = 0) {
   a.stride = stride;
   a.q_begin = q_begin;
   a.nq8 = (g.nb - q_begin + 7) / 8 * 8;
-  a.mag_nw = (uint32_t)(0x100000000ull / (uint64_t)g.nW + 1);
-  a.mag_nhw = (uint32_t)(0x100000000ull / (uint64_t)(g.nH * g.nW) + 1);
-  a.mag_nwk = (uint32_t)(0x100000000ull / (uint64_t)g.nWk + 1);
-  a.mag_nhwk = (uint32_t)(0x100000000ull / (uint64_t)(g.nHk * g.nWk) + 1);
+  a.mag_nw = magic(g.nW);
+  a.mag_nhw = magic(g.nH * g.nW);
+  a.mag_nwk = magic(g.nWk);
+  a.mag_nhwk = magic(g.nHk * g.nWk);
   a.unit_shift = 0;
   for (int m = g.nk / 128; m > 1; m >>= 1) ++a.unit_shift;
   a.lcwk = 0;
