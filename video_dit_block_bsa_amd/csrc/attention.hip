@@ -108,7 +108,20 @@ constexpr int kSlots = 5;                               // half-tile ring per wo
 // + l_b 2^(m_b-m)), m = max(m_a, m_b)). Every wave then issues half the MFMAs
 // of a unit, and the key half is a template constant inside the loop (two
 // copies), so each read still names its slot.
-template <bool kDense, bool kLse, int kKeyMode, bool kSplit, bool kPartial>
+//
+// kUnion also serves query blocks of 64 tokens (128-token key blocks, grids
+// the chunks divide, an even number of block rows along t): one workgroup
+// takes the two blocks at t-rows 2m and 2m+1 of the same (h, w) column, whose
+// 128 slots form one box of twice the chunk's depth (slot j >= 64 is slot
+// j - 64 of the second block, by the linearity of the slot offsets). It
+// walks the union of the two key lists, merged by a two-cursor walk, and
+// stages each key block once; waves 0, 1 (first block) and 2, 3 (second
+// block) skip the products of a unit their block did not select. Neighbouring
+// blocks select mostly the same keys, so the tiles gathered per query drop
+// by a quarter on smooth inputs while the MFMA work stays that of the blocks'
+// own lists. The walk visits every list entry once whatever the lists'
+// order; ascending lists make it share the most.
+template <bool kDense, bool kLse, int kKeyMode, bool kSplit, bool kPartial, bool kUnion = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const int32_t* __restrict__ idx,
@@ -134,8 +147,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const int pair = x / a.nq8;
   const int r = x - pair * a.nq8;
   const int chunk = a.nq8 >> 3;
-  const int qb = a.q_begin + (r & 7) * chunk + (r >> 3);
-  if (qb >= g.nb) return;
+  const int nhw = g.nH * g.nW;  // query blocks per t-row
+  // kUnion: x indexes pairs; pair p holds block p + (p / nhw) * nhw (t-row
+  // 2 (p / nhw)) and the block one t-row after it.
+  const int qi = (kUnion ? a.q_begin / 2 : a.q_begin) + (r & 7) * chunk + (r >> 3);
+  if (qi >= (kUnion ? g.nb / 2 : g.nb)) return;
+  const int qb = kUnion ? qi + div_magic<false>(qi, a.mag_nhw) * nhw : qi;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -182,44 +199,65 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const uint32_t vx = 80u * (uint32_t)r_lane;  // ((L%16) ^ 4r) ^ ((L%16) ^ r), in bytes
   const uint32_t half_off = (uint32_t)key_slot_offset(g, kHalfRows) * (kHeadDim * 2);
 
-  int count;
+  int count, count_b = 0;
   const int32_t* list = nullptr;
+  const int32_t* list_b = nullptr;  // kUnion: the second block's list
   if (kDense) {
     count = allowed_blocks(g, qb);
   } else {
     list = idx + ((size_t)pair * g.nb + qb) * a.stride;
     count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
+    if constexpr (kUnion) {
+      list_b = list + (size_t)nhw * a.stride;
+      count_b = min(max(cntp[(size_t)pair * g.nb + qb + nhw], 0), a.stride);
+    }
   }
-  // Next usable list position at or after `from` (ids outside [0, Nk) are skipped).
-  auto next_valid = [&](int from) {
+  // Next usable position of list l (c entries) at or after `from` (ids
+  // outside [0, Nk) are skipped).
+  auto next_valid_in = [&](const int32_t* l, int c, int from) {
     if (kDense) return from;
-    while (from < count) {
-      const int kb = list[from];
+    while (from < c) {
+      const int kb = l[from];
       if (kb >= 0 && kb < g.nbk) break;
       ++from;
     }
     return from;
   };
+  auto next_valid = [&](int from) { return next_valid_in(list, count, from); };
   auto kb_at = [&](int pos) { return kDense ? pos : list[pos]; };
   // Unit cursor: (position, unit within the key block) for kKeyMode 0 and 1,
   // (position of the lower block, position of the upper block) for kKeyMode 2.
-  // The unit exists while .a < count.
+  // The unit exists while .a < count. kUnion: (position in the first list,
+  // position in the second, the unit's key block = the smaller of the two
+  // entries, bit 0 / bit 1 set when it is the first / second list's entry);
+  // the unit exists while either position is inside its list.
   struct Cursor {
-    int a, b;
+    int a, b, kb, m;
   };
+  auto union_unit = [&](int pa, int pb) -> Cursor {
+    const int ka = pa < count ? list[pa] : 0x7fffffff;
+    const int kb = pb < count_b ? list_b[pb] : 0x7fffffff;
+    const int k = min(ka, kb);
+    return {pa, pb, k, (ka == k ? 1 : 0) | (kb == k ? 2 : 0)};
+  };
+  auto live = [&](const Cursor& c) { return kUnion ? (c.a < count || c.b < count_b) : c.a < count; };
   auto first_unit = [&]() -> Cursor {
+    if constexpr (kUnion) return union_unit(next_valid(0), next_valid_in(list_b, count_b, 0));
     const int p = next_valid(0);
-    return {p, kKeyMode == 2 ? next_valid(p + 1) : 0};
+    return {p, kKeyMode == 2 ? next_valid(p + 1) : 0, 0, 0};
   };
   auto next_unit = [&](Cursor c) -> Cursor {
-    if constexpr (kKeyMode == 1) {
-      if (c.b + 1 < (1 << a.unit_shift)) return {c.a, c.b + 1};
-      return {next_valid(c.a + 1), 0};
+    if constexpr (kUnion) {
+      return union_unit((c.m & 1) ? next_valid(c.a + 1) : c.a,
+                        (c.m & 2) ? next_valid_in(list_b, count_b, c.b + 1) : c.b);
+    } else if constexpr (kKeyMode == 1) {
+      if (c.b + 1 < (1 << a.unit_shift)) return {c.a, c.b + 1, 0, 0};
+      return {next_valid(c.a + 1), 0, 0, 0};
     } else if constexpr (kKeyMode == 2) {
       const int p = next_valid(c.b + 1);
-      return {p, next_valid(p + 1)};
+      return {p, next_valid(p + 1), 0, 0};
     } else {
-      return {next_valid(c.a + 1), 0};
+      return {next_valid(c.a + 1), 0, 0, 0};
     }
   };
   // Byte offset of the first slot of half h (0: keys 0..63, 1: keys 64..127)
@@ -233,7 +271,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
                         key_slot_offset(g, c.b * kBlockTokens)) * (kHeadDim * 2) +
              h * half_off;
     } else {
-      return (uint32_t)key_block_origin<kPartial>(a, kb_at(c.a)) * (kHeadDim * 2) + h * half_off;
+      return (uint32_t)key_block_origin<kPartial>(a, kUnion ? c.kb : kb_at(c.a)) * (kHeadDim * 2) +
+             h * half_off;
     }
   };
   // Half tile e (0: K lo, 1: K hi, 2: V lo, 3: V hi) of a unit into a slot.
@@ -307,12 +346,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   }
 
   // Units: cur (the unit of the current phase) and nxt (the one after it,
-  // with nxt.a == count past the last). KH is the key half in split mode.
+  // not live past the last). KH is the key half in split mode.
   auto run = [&](auto khc) {
   constexpr int KH = decltype(khc)::value;
   constexpr int kT = kSplit ? 2 : 4;  // 32-key sub-tiles of S per wave
   Cursor cur = first_unit();
-  if (cur.a < count) {
+  if (live(cur)) {
     Cursor nxt = next_unit(cur);
     // Half tiles 0, 1, 2 (K_0 lo, K_0 hi, V_0 lo) into slots 0, 1, 2.
     load_half(cur, 0, slot0);
@@ -336,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
       // Refill the slots of the previous phase with half tiles 2p+3, 2p+4:
       // V_j hi and K_{j+1} lo in an S phase, K_{j+1} hi and V_{j+1} lo in a
       // P V phase.
-      const Cursor un = nxt.a < count ? nxt : cur;
+      const Cursor un = live(nxt) ? nxt : cur;
       if constexpr (is_s) {
         load_half(cur, 3, slot_ptr(std::integral_constant<int, sc>{}));
         load_half(un, 0, slot_ptr(std::integral_constant<int, sd>{}));
@@ -346,7 +385,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
       }
       const char* lo = reinterpret_cast<const char*>(slot_ptr(std::integral_constant<int, sa>{}));
       const char* hi = reinterpret_cast<const char*>(slot_ptr(std::integral_constant<int, sb>{}));
+      // kUnion: whether this wave's block selected the unit's key block.
+      const bool own = !kUnion || ((cur.m >> (w >> 1)) & 1) != 0;
       if constexpr (is_s) {
+        if (!own) return true;
         // S^T = K Q^T for this wave's 32 queries and all 128 keys, channel
         // steps outermost (four independent accumulators between dependent
         // MFMAs).
@@ -463,11 +505,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
         };
         if constexpr (kSplit) {
           pv_half(KH ? hi : lo, 0);
-        } else {
+        } else if (own) {
           pv_half(lo, 0);
           pv_half(hi, 4);
         }
-        if (nxt.a >= count) return false;
+        if (!live(nxt)) return false;
         cur = nxt;
         nxt = next_unit(cur);
         return true;
@@ -581,8 +623,22 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
 #undef BSA_LAUNCH_DENSE
     return hipGetLastError();
   }
-  const AttnArgs a = make_attn_args(g, stride, q_begin);
+  AttnArgs a = make_attn_args(g, stride, q_begin);
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
+  // 64-token query blocks with 128-token key blocks take them in t-adjacent
+  // pairs (kUnion) when the launch covers whole pairs of t-rows.
+  const int nhw = g.nH * g.nW;
+  if (split && mode == 0 && !part && (g.nb / nhw) % 2 == 0 && q_begin % (2 * nhw) == 0) {
+    a.nq8 = ((g.nb - q_begin) / 2 + 7) / 8 * 8;
+    const dim3 grid_u((unsigned)((size_t)g.bh * a.nq8));
+    if (lse)
+      hipLaunchKernelGGL((attn_kernel<false, true, 0, false, false, true>), grid_u, dim3(kThreads), 0,
+                         stream, a, q, k, v, idx, cnt, o, lse);
+    else
+      hipLaunchKernelGGL((attn_kernel<false, false, 0, false, false, true>), grid_u, dim3(kThreads), 0,
+                         stream, a, q, k, v, idx, cnt, o, lse);
+    return hipGetLastError();
+  }
 #define BSA_LAUNCH_ATTN(LSE, MODE, SPLIT)                                                      \
   if (part)                                                                                     \
     hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT, true>), grid, dim3(kThreads), 0,   \
