@@ -21,7 +21,7 @@ import parity as PT
 from oracle import bsa_oracle as O
 from test_gpu_parity import _run_and_compare
 from video_dit_block_bsa_amd.binding import Problem, SelectParams
-from video_dit_block_bsa_amd.inputs import make_qkv
+from video_dit_block_bsa_amd.inputs import make_grad, make_qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +147,39 @@ def test_pairs_lse():
         err = np.abs(lse[0, h].cpu().numpy() - lse_r).max()
         _log(f"lse head {h}: max-abs {err:.3e}")
         assert err <= 2.5e-3
+
+
+# Backward: dQ takes the same pairs (dK/dV is unchanged); every gradient
+# element against the oracle, on the oracle's selection and on shuffled
+# random lists with invalid ids and empty rows.
+@pytest.mark.parametrize("grid,chunk,key_chunk,k_sel,cond", [
+    ((8, 16, 32), (2, 4, 8), (4, 4, 8), 5, 4),    # paired, condition rows
+    ((8, 8, 32), (1, 8, 8), (2, 8, 8), 3, 0),     # paired, another chunk
+    ((6, 16, 32), (2, 4, 8), (2, 8, 8), 3, 0),    # odd t-rows: unpaired
+])
+def test_pairs_backward_selection(grid, chunk, key_chunk, k_sel, cond):
+    from test_gpu_backward import _case
+
+    _case(*grid, 2, k_sel, chunk=chunk, kind="field", seed=87, cond_frames=cond,
+          key_chunk=key_chunk)
+
+
+def test_pairs_backward_shuffled_lists():
+    from test_gpu_backward import compare_all
+
+    T, H, W, heads = 8, 16, 32, 2
+    q, k, v = make_qkv(T, H, W, heads, kind="field", seed=88)
+    do = make_grad(T, H, W, heads, seed=88)
+    problem = Problem.make(T, H, W, heads, chunk=(2, 4, 8), key_chunk=(4, 4, 8))
+    g = PT.geometry(problem)
+    nbk = O.key_geometry(g).num_blocks
+    rows, stride = heads * g.num_blocks, 10
+    rng = np.random.default_rng(789)
+    idx = np.full((rows, stride), -1, dtype=np.int32)
+    cnt = rng.integers(0, stride + 1, size=rows).astype(np.int32)
+    for r in range(rows):
+        ids = rng.choice(nbk, size=stride, replace=False).astype(np.int32)
+        bad = rng.random(stride) < 0.15
+        ids[bad] = rng.choice([-2, nbk, nbk + 9], size=int(bad.sum()))
+        idx[r] = ids
+    compare_all(problem, q, k, v, do, idx, cnt, stride)

@@ -297,7 +297,16 @@ __device__ __forceinline__ void xcd_block(const AttnArgs& a, int& pair, int& blk
 // V tiles are double-buffered in LDS (two separate objects each, the loop
 // unrolled by two so every read names its buffer at compile time and never
 // waits for the loads into the other one).
-template <int kKeyMode, bool kSplit, bool kPartial>
+//
+// kUnion (64-token query blocks, 128-token key blocks, grids the chunks
+// divide, an even number of block rows along t), as in the forward: one
+// workgroup takes the blocks at t-rows 2m and 2m+1 of a column as the 128
+// query slots of one box and walks the union of their key lists, each key
+// tile gathered once. Waves 0..3 serve the first block and 4..7 the second
+// (wave w: query slice w%2 of its block, key part (w/2)%2), so each SIMD,
+// holding waves w and w+4, keeps one wave busy when only one block selected
+// a unit; the other block's waves skip its products.
+template <int kKeyMode, bool kSplit, bool kPartial, bool kUnion = false>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
     const bf16_bits* __restrict__ vp, const bf16_bits* __restrict__ dop,
@@ -308,15 +317,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) bf16_bits k1s[kBlockTokens * kHeadDim];
   __shared__ __attribute__((aligned(1024))) bf16_bits v1s[kBlockTokens * kHeadDim];
   const Geom& g = a.g;
-  int pair, qb;
-  xcd_block(a, pair, qb);
-  if (qb >= g.nb) return;
+  int pair, qi;
+  xcd_block(a, pair, qi);
+  const int nhw = g.nH * g.nW;  // query blocks per t-row
+  // kUnion: qi indexes pairs; pair p holds block p + (p / nhw) * nhw and the
+  // block one t-row after it.
+  if (qi >= (kUnion ? g.nb / 2 : g.nb)) return;
+  const int qb = kUnion ? qi + div_magic<false>(qi, a.mag_nhw) * nhw : qi;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int qs = kSplit ? (w & 1) : (w & 3);  // query slice
-  const int kpart = kSplit ? (w >> 1) : (w >> 2);
+  // Query slice (32 queries of the block, or of the pair's box) and key part.
+  const int qs = kUnion ? 2 * (w >> 2) + (w & 1) : kSplit ? (w & 1) : (w & 3);
+  const int kpart = kUnion ? ((w >> 1) & 1) : kSplit ? (w >> 1) : (w >> 2);
   const int n = lane & 31;
   const int gs = lane >> 5;
   const size_t hoff = (size_t)pair * g.S * kHeadDim;
@@ -338,39 +352,63 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + off));
     df[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dop + off));
   }
-  const float* st = stats + ((size_t)pair * g.nb + qb) * (2 * kBlockTokens);
-  const float lse2 = st[32 * qs + n];
-  const float dd = st[kBlockTokens + 32 * qs + n];
+  // Stats of the wave's queries (kUnion: of its own block of the pair).
+  const int sblk = kUnion ? qb + (qs >> 1) * nhw : qb;
+  const int sslot = 32 * (kUnion ? (qs & 1) : qs) + n;
+  const float* st = stats + ((size_t)pair * g.nb + sblk) * (2 * kBlockTokens);
+  const float lse2 = st[sslot];
+  const float dd = st[kBlockTokens + sslot];
 
   const int32_t* list = idx + ((size_t)pair * g.nb + qb) * a.stride;
   const int count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
-  auto next_valid = [&](int from) __attribute__((always_inline)) {
-    while (from < count) {
-      const int kb = list[from];
+  const int32_t* list_b = list + (size_t)nhw * a.stride;  // kUnion: the second block's list
+  const int count_b = kUnion ? min(max(cntp[(size_t)pair * g.nb + qb + nhw], 0), a.stride) : 0;
+  auto next_valid_in = [&](const int32_t* l, int c, int from) __attribute__((always_inline)) {
+    while (from < c) {
+      const int kb = l[from];
       if (kb >= 0 && kb < g.nbk) break;
       ++from;
     }
     return from;
   };
+  auto next_valid = [&](int from) __attribute__((always_inline)) {
+    return next_valid_in(list, count, from);
+  };
   // Unit cursor, as in the forward: (position, unit within the key block)
   // for kKeyMode 0 and 1, (position of the lower block, position of the upper
-  // block) for kKeyMode 2. The unit exists while .a < count.
+  // block) for kKeyMode 2; the unit exists while .a < count. kUnion:
+  // (positions in the two lists, the unit's key block = the smaller entry,
+  // bit 0 / 1 set when it is the first / second list's); the unit exists
+  // while either position is inside its list.
   struct Cursor {
-    int a, b;
+    int a, b, kb, m;
+  };
+  auto union_unit = [&](int pa, int pb) __attribute__((always_inline)) -> Cursor {
+    const int ka = pa < count ? list[pa] : 0x7fffffff;
+    const int kb = pb < count_b ? list_b[pb] : 0x7fffffff;
+    const int k = min(ka, kb);
+    return {pa, pb, k, (ka == k ? 1 : 0) | (kb == k ? 2 : 0)};
+  };
+  auto live = [&](const Cursor& c) __attribute__((always_inline)) {
+    return kUnion ? (c.a < count || c.b < count_b) : c.a < count;
   };
   auto first_unit = [&]() __attribute__((always_inline)) -> Cursor {
+    if constexpr (kUnion) return union_unit(next_valid(0), next_valid_in(list_b, count_b, 0));
     const int p = next_valid(0);
-    return {p, kKeyMode == 2 ? next_valid(p + 1) : 0};
+    return {p, kKeyMode == 2 ? next_valid(p + 1) : 0, 0, 0};
   };
   auto next_unit = [&](Cursor c) __attribute__((always_inline)) -> Cursor {
-    if constexpr (kKeyMode == 1) {
-      if (c.b + 1 < (1 << a.unit_shift)) return {c.a, c.b + 1};
-      return {next_valid(c.a + 1), 0};
+    if constexpr (kUnion) {
+      return union_unit((c.m & 1) ? next_valid(c.a + 1) : c.a,
+                        (c.m & 2) ? next_valid_in(list_b, count_b, c.b + 1) : c.b);
+    } else if constexpr (kKeyMode == 1) {
+      if (c.b + 1 < (1 << a.unit_shift)) return {c.a, c.b + 1, 0, 0};
+      return {next_valid(c.a + 1), 0, 0, 0};
     } else if constexpr (kKeyMode == 2) {
       const int p = next_valid(c.b + 1);
-      return {p, next_valid(p + 1)};
+      return {p, next_valid(p + 1), 0, 0};
     } else {
-      return {next_valid(c.a + 1), 0};
+      return {next_valid(c.a + 1), 0, 0, 0};
     }
   };
   // This wave's rows of a unit's K or V tile: waves 4..7 stage rows 64..127,
@@ -389,7 +427,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
                                       key_slot_offset(g, c.b * kBlockTokens),
                                   c.b * kBlockTokens, kBlockTokens - 1, tile);
     } else {
-      const int kb = list[c.a];
+      const int kb = kUnion ? c.kb : list[c.a];
       load_rows16<true, kPartial>(a, rs, tl.ldk, w, kb, key_block_origin<kPartial>(a, kb), 0,
                                   kBlockTokens - 1, tile);
     }
@@ -407,6 +445,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     constexpr bool kUpper = kKeyMode == 2 && TT0 >= 2;          // rows of the upper block
     if constexpr (kUpper) {
       if (un.b >= count) return;  // a lone last 64-token block: no upper half
+    }
+    if constexpr (kUnion) {
+      if (((un.m >> (w >> 2)) & 1) == 0) return;  // not selected by this wave's block
     }
     f32x16 sacc[NS], pacc[NS];
 #pragma unroll
@@ -465,7 +506,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 
   auto run = [&](auto kpc) __attribute__((always_inline)) {
     Cursor cur = first_unit();
-    if (cur.a >= count) return;
+    if (!live(cur)) return;
     load_unit(cur, krs, k0s);
     load_unit(cur, vrs, v0s);
     Cursor nxt = next_unit(cur);
@@ -479,12 +520,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
       // everyone's are, and everyone has finished reading the other buffer.
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       workgroup_barrier();
-      if (nxt.a < count) {
+      if (live(nxt)) {
         load_unit(nxt, krs, kn);
         load_unit(nxt, vrs, vn);
       }
       compute(kpc, reinterpret_cast<const char*>(kt), reinterpret_cast<const char*>(vt), cur);
-      if (nxt.a >= count) return false;
+      if (!live(nxt)) return false;
       cur = nxt;
       nxt = next_unit(cur);
       return true;
@@ -807,9 +848,17 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
   const bool part = needs_general(g);
   const dim3 grid((unsigned)((size_t)g.bh * a.nq8));
+  const int nhw = g.nH * g.nW;
   // Grids the chunks divide (with more than one block along w and within a
   // frame) run kernels compiled without the general code (the default
-  // kernels sit at the 256-VGPR limit).
+  // kernels sit at the 256-VGPR limit). 64-token query blocks with 128-token
+  // key blocks go in t-adjacent pairs when the t-rows pair up.
+  if (split && mode == 0 && !part && (g.nb / nhw) % 2 == 0) {
+    AttnArgs au = a;
+    au.nq8 = (g.nb / 2 + 7) / 8 * 8;
+    hipLaunchKernelGGL((bwd_dq_kernel<0, false, false, true>), dim3((unsigned)((size_t)g.bh * au.nq8)),
+                       dim3(kBwdThreads), 0, stream, au, q, k, v, dout, stats, idx, cnt, dq);
+  } else {
 #define BSA_LAUNCH_DQ(MODE, SPLIT, PART)                                                      \
   hipLaunchKernelGGL((bwd_dq_kernel<MODE, SPLIT, PART>), grid, dim3(kBwdThreads), 0, stream, a, \
                      q, k, v, dout, stats, idx, cnt, dq)
@@ -826,6 +875,7 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
   }
 #undef BSA_LAUNCH_DQ_P
 #undef BSA_LAUNCH_DQ
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dK/dV: one workgroup per 128-key unit of a key block of 128+ tokens, or
