@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 
   const int32_t* list = idx + ((size_t)pair * g.nb + qb) * a.stride;
   const int count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
-  const int32_t* list_b = list + (size_t)nhw * a.stride;  // kUnion: the second block's list
+  const int32_t* list_b = kUnion ? list + (size_t)nhw * a.stride : nullptr;  // the second block's list
   const int count_b = kUnion ? min(max(cntp[(size_t)pair * g.nb + qb + nhw], 0), a.stride) : 0;
   auto next_valid_in = [&](const int32_t* l, int c, int from) __attribute__((always_inline)) {
     while (from < c) {
