@@ -45,22 +45,26 @@ def _step_tensors(T, H, W, heads, cond_frames, seed0, seed1):
     return a, tuple(step1)
 
 
-@pytest.mark.parametrize("grid,chunk,key_chunk,params", [
-    ((16, 16, 32), (4, 4, 8), None, SelectParams.topk(6)),
-    ((16, 16, 32), (4, 4, 8), None, SelectParams.cdf(0.8, 2, 10)),
-    ((16, 16, 32), (4, 4, 8), (2, 4, 8), SelectParams.topk(9)),
-    ((16, 16, 32), (4, 4, 8), (4, 8, 8), SelectParams.topk(3)),
-    ((16, 16, 32), (2, 4, 8), (4, 4, 8), SelectParams.topk(5)),
+@pytest.mark.parametrize("grid,chunk,key_chunk,params,cond", [
+    ((16, 16, 32), (4, 4, 8), None, SelectParams.topk(6), 4),
+    ((16, 16, 32), (4, 4, 8), None, SelectParams.cdf(0.8, 2, 10), 4),
+    ((16, 16, 32), (4, 4, 8), (2, 4, 8), SelectParams.topk(9), 4),
+    ((16, 16, 32), (4, 4, 8), (4, 8, 8), SelectParams.topk(3), 4),
+    # 64-token query blocks: the noisy rows start on an even t-row (paired
+    # blocks) or on an odd one (one block per workgroup)
+    ((16, 16, 32), (2, 4, 8), (4, 4, 8), SelectParams.topk(5), 4),
+    ((16, 16, 32), (2, 4, 8), (2, 8, 8), SelectParams.topk(5), 4),
+    ((16, 16, 32), (2, 4, 8), (2, 8, 8), SelectParams.cdf(0.8, 2, 8), 2),
     # partial blocks along t, h and w
-    ((14, 18, 36), (4, 4, 8), None, SelectParams.topk(6)),
-    ((14, 18, 36), (4, 4, 8), (4, 8, 8), SelectParams.cdf(0.8, 1, 8)),
+    ((14, 18, 36), (4, 4, 8), None, SelectParams.topk(6), 4),
+    ((14, 18, 36), (4, 4, 8), (4, 8, 8), SelectParams.cdf(0.8, 1, 8), 4),
 ])
-def test_noisy_rows_match_full_path(grid, chunk, key_chunk, params):
+def test_noisy_rows_match_full_path(grid, chunk, key_chunk, params, cond):
     import torch
 
     from video_dit_block_bsa_amd import binding as B
 
-    (T, H, W), heads, cond = grid, 2, 4
+    (T, H, W), heads = grid, 2
     problem = Problem.make(T, H, W, heads, chunk=chunk, cond_frames=cond, key_chunk=key_chunk)
     g = PT.geometry(problem)
     nb, cq = g.num_blocks, g.cond_blocks

@@ -1,13 +1,13 @@
 """64-token query blocks taken in t-adjacent pairs (GPU against the oracle).
 
-With 128-token key blocks and an even number of block rows along t, the
-sparse kernel runs one workgroup per pair of query blocks at t-rows 2m and
-2m+1 and walks the union of their two key lists. These cases check that
-each block still attends exactly to its own list: selections from the
+With 128-token key blocks, the sparse kernel and dQ run one workgroup per
+pair of query blocks at t-rows 2m and 2m+1 (after an odd number of rows the
+last one alone) and walk the union of the two key lists. These cases check
+that each block still attends exactly to its own list: selections from the
 select kernel, hand-made lists (unordered, ids outside [0, Nk), a list
 that one block of a pair has and the other lacks, empty lists), random
-shuffled lists, the log-normaliser output, and a grid with an odd number
-of t-rows (the unpaired kernel) beside it.
+shuffled lists, the log-normaliser output, and grids with an odd number of
+t-rows.
 """
 
 from __future__ import annotations
@@ -36,7 +36,7 @@ def _log(*a):
     ((12, 16, 32), (2, 4, 8), (4, 4, 8), SelectParams.cdf(0.8, 2, 9), 4),   # paired, condition rows
     ((8, 8, 32), (1, 8, 8), (2, 8, 8), SelectParams.topk(3), 0),            # paired, another chunk
     ((4, 32, 64), (2, 4, 8), (2, 8, 8), SelectParams.topk(7), 0),           # one pair of t-rows
-    ((6, 16, 32), (2, 4, 8), (2, 8, 8), SelectParams.topk(3), 0),           # odd t-rows: unpaired
+    ((6, 16, 32), (2, 4, 8), (2, 8, 8), SelectParams.topk(3), 0),           # odd t-rows: last alone
 ])
 def test_pairs_select_and_attend(grid, chunk, key_chunk, params, cond):
     T, H, W = grid
@@ -73,6 +73,20 @@ def _attend_lists(problem, q, k, v, idx, cnt, stride):
     for p, i in empty:
         b, h = divmod(p, q.shape[1])
         assert np.all(out[b, h][O.block_tokens(perm, i, g.n)] == 0)
+
+
+def test_pairs_lone_last_row_lists():
+    """Grid 6x8x16, query chunk (2,4,8): three t-rows of 4 blocks, pairs
+    (0,4), (1,5), (2,6), (3,7) and blocks 8..11 alone; shuffled lists."""
+    T, H, W = 6, 8, 16
+    q, k, v = make_qkv(T, H, W, 1, kind="iid", seed=91)
+    problem = Problem.make(T, H, W, 1, chunk=(2, 4, 8), key_chunk=(2, 8, 8))
+    nbk = 3 * 1 * 2
+    rng = np.random.default_rng(792)
+    idx = np.stack([rng.permutation(nbk)[:4] for _ in range(12)]).astype(np.int32)
+    cnt = rng.integers(0, 5, size=12).astype(np.int32)
+    cnt[8] = 4
+    _attend_lists(problem, q, k, v, idx, cnt, 4)
 
 
 def test_pairs_hand_lists():
@@ -155,7 +169,7 @@ def test_pairs_lse():
 @pytest.mark.parametrize("grid,chunk,key_chunk,k_sel,cond", [
     ((8, 16, 32), (2, 4, 8), (4, 4, 8), 5, 4),    # paired, condition rows
     ((8, 8, 32), (1, 8, 8), (2, 8, 8), 3, 0),     # paired, another chunk
-    ((6, 16, 32), (2, 4, 8), (2, 8, 8), 3, 0),    # odd t-rows: unpaired
+    ((6, 16, 32), (2, 4, 8), (2, 8, 8), 3, 0),    # odd t-rows: last alone
 ])
 def test_pairs_backward_selection(grid, chunk, key_chunk, k_sel, cond):
     from test_gpu_backward import _case

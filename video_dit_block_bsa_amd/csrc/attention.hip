@@ -110,17 +110,21 @@ constexpr int kSlots = 5;                               // half-tile ring per wo
 // copies), so each read still names its slot.
 //
 // kUnion also serves query blocks of 64 tokens (128-token key blocks, grids
-// the chunks divide, an even number of block rows along t): one workgroup
-// takes the two blocks at t-rows 2m and 2m+1 of the same (h, w) column, whose
-// 128 slots form one box of twice the chunk's depth (slot j >= 64 is slot
-// j - 64 of the second block, by the linearity of the slot offsets). It
+// the chunks divide): one workgroup takes the two blocks at t-rows r0 + 2m
+// and r0 + 2m + 1 of the same (h, w) column (r0: the launch's first row),
+// whose 128 slots form one box of twice the chunk's depth (slot j >= 64 is
+// slot j - 64 of the second block, by the linearity of the slot offsets);
+// after an odd number of rows the last one has no partner, and waves 2, 3
+// then read the first block's slot 0, own no unit and write nothing. It
 // walks the union of the two key lists, merged by a two-cursor walk, and
 // stages each key block once; waves 0, 1 (first block) and 2, 3 (second
 // block) skip the products of a unit their block did not select. Neighbouring
 // blocks select mostly the same keys, so the tiles gathered per query drop
 // by a quarter on smooth inputs while the MFMA work stays that of the blocks'
 // own lists. The walk visits every list entry once whatever the lists'
-// order; ascending lists make it share the most.
+// order; ascending lists make it share the most. A wave's arithmetic depends
+// only on its own block's list, walked in that list's order, so a block gets
+// the same bits whichever block it is paired with.
 template <bool kDense, bool kLse, int kKeyMode, bool kSplit, bool kPartial, bool kUnion = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     AttnArgs a, const bf16_bits* __restrict__ qp, const bf16_bits* __restrict__ kp,
@@ -148,11 +152,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const int r = x - pair * a.nq8;
   const int chunk = a.nq8 >> 3;
   const int nhw = g.nH * g.nW;  // query blocks per t-row
-  // kUnion: x indexes pairs; pair p holds block p + (p / nhw) * nhw (t-row
-  // 2 (p / nhw)) and the block one t-row after it.
-  const int qi = (kUnion ? a.q_begin / 2 : a.q_begin) + (r & 7) * chunk + (r >> 3);
-  if (qi >= (kUnion ? g.nb / 2 : g.nb)) return;
-  const int qb = kUnion ? qi + div_magic<false>(qi, a.mag_nhw) * nhw : qi;
+  // kUnion: x indexes pairs; pair p = m nhw + c holds block q_begin + 2m nhw
+  // + c and, if it exists, the block one t-row after it.
+  const int qi = (kUnion ? 0 : a.q_begin) + (r & 7) * chunk + (r >> 3);
+  const int qb = kUnion ? a.q_begin + qi + div_magic<false>(qi, a.mag_nhw) * nhw : qi;
+  if (qb >= g.nb) return;
+  const bool has_b = kUnion && qb + nhw < g.nb;  // the pair's second block exists
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -172,7 +177,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
 
   // A query slot of a partial block that lies outside the grid reads slot 0
   // (always inside) instead, and its row is never written.
-  const bool q_inside = !kPartial || block_slot_valid(g, qb, 32 * qh + n);
+  const bool q_inside =
+      kUnion ? (w < 2 || has_b) : !kPartial || block_slot_valid(g, qb, 32 * qh + n);
   const int qtok = block_origin<kPartial>(a, qb) + (q_inside ? slot_offset(g, 32 * qh + n) : 0);
   bf16x8 qf[8];
 #pragma unroll
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   } else {
     list = idx + ((size_t)pair * g.nb + qb) * a.stride;
     count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
-    if constexpr (kUnion) {
+    if (kUnion && has_b) {
       list_b = list + (size_t)nhw * a.stride;
       count_b = min(max(cntp[(size_t)pair * g.nb + qb + nhw], 0), a.stride);
     }
@@ -625,11 +631,12 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
   }
   AttnArgs a = make_attn_args(g, stride, q_begin);
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
-  // 64-token query blocks with 128-token key blocks take them in t-adjacent
-  // pairs (kUnion) when the launch covers whole pairs of t-rows.
+  // 64-token query blocks with 128-token key blocks go in t-adjacent pairs
+  // (kUnion), counted from the launch's first t-row.
   const int nhw = g.nH * g.nW;
-  if (split && mode == 0 && !part && (g.nb / nhw) % 2 == 0 && q_begin % (2 * nhw) == 0) {
-    a.nq8 = ((g.nb - q_begin) / 2 + 7) / 8 * 8;
+  if (split && mode == 0 && !part && q_begin % nhw == 0) {
+    const int pairs = ((g.nb - q_begin) / nhw + 1) / 2 * nhw;
+    a.nq8 = (pairs + 7) / 8 * 8;
     const dim3 grid_u((unsigned)((size_t)g.bh * a.nq8));
     if (lse)
       hipLaunchKernelGGL((attn_kernel<false, true, 0, false, false, true>), grid_u, dim3(kThreads), 0,

@@ -299,9 +299,9 @@ __device__ __forceinline__ void xcd_block(const AttnArgs& a, int& pair, int& blk
 // waits for the loads into the other one).
 //
 // kUnion (64-token query blocks, 128-token key blocks, grids the chunks
-// divide, an even number of block rows along t), as in the forward: one
-// workgroup takes the blocks at t-rows 2m and 2m+1 of a column as the 128
-// query slots of one box and walks the union of their key lists, each key
+// divide), as in the forward: one workgroup takes the blocks at t-rows 2m and
+// 2m+1 of a column as the 128 query slots of one box (after an odd number of
+// rows the last one alone) and walks the union of their key lists, each key
 // tile gathered once. Waves 0..3 serve the first block and 4..7 the second
 // (wave w: query slice w%2 of its block, key part (w/2)%2), so each SIMD,
 // holding waves w and w+4, keeps one wave busy when only one block selected
@@ -320,10 +320,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   int pair, qi;
   xcd_block(a, pair, qi);
   const int nhw = g.nH * g.nW;  // query blocks per t-row
-  // kUnion: qi indexes pairs; pair p holds block p + (p / nhw) * nhw and the
-  // block one t-row after it.
-  if (qi >= (kUnion ? g.nb / 2 : g.nb)) return;
+  // kUnion: qi indexes pairs; pair p holds block p + (p / nhw) * nhw and, if
+  // it exists, the block one t-row after it.
   const int qb = kUnion ? qi + div_magic<false>(qi, a.mag_nhw) * nhw : qi;
+  if (qb >= g.nb) return;
+  const bool has_b = kUnion && qb + nhw < g.nb;  // the pair's second block exists
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -343,7 +344,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 
   // A query slot of a partial block outside the grid computes on slot 0 (its
   // stats make every probability 0) and is not written.
-  const bool q_inside = !kPartial || block_slot_valid(g, qb, 32 * qs + n);
+  // kUnion: the slices of a missing second block compute on slot 0 of the
+  // first (they own no unit) and are not written.
+  const bool q_inside =
+      kUnion ? (qs < 2 || has_b) : !kPartial || block_slot_valid(g, qb, 32 * qs + n);
   const int qtok = block_origin<kPartial>(a, qb) + (q_inside ? slot_offset(g, 32 * qs + n) : 0);
   bf16x8 qf[8], df[8];
 #pragma unroll
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     df[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dop + off));
   }
   // Stats of the wave's queries (kUnion: of its own block of the pair).
-  const int sblk = kUnion ? qb + (qs >> 1) * nhw : qb;
+  const int sblk = (kUnion && qs >= 2 && has_b) ? qb + nhw : qb;
   const int sslot = 32 * (kUnion ? (qs & 1) : qs) + n;
   const float* st = stats + ((size_t)pair * g.nb + sblk) * (2 * kBlockTokens);
   const float lse2 = st[sslot];
@@ -361,8 +365,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 
   const int32_t* list = idx + ((size_t)pair * g.nb + qb) * a.stride;
   const int count = min(max(cntp[(size_t)pair * g.nb + qb], 0), a.stride);
-  const int32_t* list_b = kUnion ? list + (size_t)nhw * a.stride : nullptr;  // the second block's list
-  const int count_b = kUnion ? min(max(cntp[(size_t)pair * g.nb + qb + nhw], 0), a.stride) : 0;
+  const int32_t* list_b = has_b ? list + (size_t)nhw * a.stride : nullptr;  // the second block's list
+  const int count_b = has_b ? min(max(cntp[(size_t)pair * g.nb + qb + nhw], 0), a.stride) : 0;
   auto next_valid_in = [&](const int32_t* l, int c, int from) __attribute__((always_inline)) {
     while (from < c) {
       const int kb = l[from];
@@ -852,10 +856,10 @@ hipError_t launch_attention_bwd(const Geom& g, const bf16_bits* q, const bf16_bi
   // Grids the chunks divide (with more than one block along w and within a
   // frame) run kernels compiled without the general code (the default
   // kernels sit at the 256-VGPR limit). 64-token query blocks with 128-token
-  // key blocks go in t-adjacent pairs when the t-rows pair up.
-  if (split && mode == 0 && !part && (g.nb / nhw) % 2 == 0) {
+  // key blocks go in t-adjacent pairs.
+  if (split && mode == 0 && !part) {
     AttnArgs au = a;
-    au.nq8 = (g.nb / 2 + 7) / 8 * 8;
+    au.nq8 = ((g.nb / nhw + 1) / 2 * nhw + 7) / 8 * 8;
     hipLaunchKernelGGL((bwd_dq_kernel<0, false, false, true>), dim3((unsigned)((size_t)g.bh * au.nq8)),
                        dim3(kBwdThreads), 0, stream, au, q, k, v, dout, stats, idx, cnt, dq);
   } else {
