@@ -175,8 +175,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(vp + hoff), (short)0, head_bytes, kBufferWord3);
 
-  // A query slot of a partial block that lies outside the grid reads slot 0
-  // (always inside) instead, and its row is never written.
+  // A query slot of a partial block that lies outside the grid, or one of
+  // the missing second block of a lone last row (kUnion), reads slot 0 of the
+  // (first) block instead, and its row is never written.
   const bool q_inside =
       kUnion ? (w < 2 || has_b) : !kPartial || block_slot_valid(g, qb, 32 * qh + n);
   const int qtok = block_origin<kPartial>(a, qb) + (q_inside ? slot_offset(g, 32 * qh + n) : 0);
