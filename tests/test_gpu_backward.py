@@ -307,23 +307,24 @@ def test_deterministic():
 
 
 @pytest.mark.timeout(600)
-def test_full_size_long_sampled():
-    """215,040 tokens, 32 heads, top-k 105 (the configuration the benchmark
-    times): the backward runs on every head; the oracle checks dq of sampled
+@pytest.mark.parametrize("name", ["long", "long_q64", "long_k64"])
+def test_full_size_sampled(name):
+    """215,040 tokens, 32 heads (the configurations the benchmark times: 128-
+    token blocks, 64-token query blocks taken in pairs by dQ, 64-token key
+    blocks): the backward runs on every head; the oracle checks dq of sampled
     query blocks and dk, dv of sampled key blocks (visiting every query block
     that kept them) on two heads. The selection is the oracle's own."""
     import torch
 
-    from video_dit_block_bsa_amd import binding as B
-
-    w = WORKLOADS["long"]
-    _log(f"generating long: {w.T}x{w.H}x{w.W}, {w.heads} heads")
+    w = WORKLOADS[name]
+    _log(f"generating {name}: {w.T}x{w.H}x{w.W}, {w.heads} heads")
     q, k, v = make_qkv(w.T, w.H, w.W, w.heads, kind=w.kind, seed=w.seed)
     do = make_grad(w.T, w.H, w.W, w.heads, seed=w.seed)
     problem = Problem.from_workload(w)
     params = SelectParams.from_workload(w)
     g = PT.geometry(problem)
-    nb = g.num_blocks
+    kg = O.key_geometry(g)
+    nb, nbk = g.num_blocks, kg.num_blocks
     heads = [0, 19]
     sp = PT.oracle_params(params)
     stride = O.index_stride(sp)
@@ -346,11 +347,12 @@ def test_full_size_long_sampled():
     o, o_plain, lse, dq, dk, dv = run_backward(problem, q, k, v, do, idx, cnt, stride)
     assert np.array_equal(o, o_plain)
     perm = O.block_token_order(g)
+    kperm = O.block_token_order(kg)
     rng = np.random.default_rng(7)
     for h in heads:
         oi, oc = rows[h]
         qbs = sorted(set(rng.choice(nb, size=2, replace=False).tolist()) | {0, nb - 1})
-        kbs = sorted(rng.choice(nb, size=2, replace=False).tolist())
+        kbs = sorted(rng.choice(nbk, size=2, replace=False).tolist())
         keepers = sorted({i for i in range(nb) for kb in kbs if kb in set(oi[i, :oc[i]].tolist())})
         _log(f"head {h}: query blocks {qbs}, key blocks {kbs} kept by {len(keepers)} query blocks")
         qf, kf, vf, dof = (O.bf16_bits_to_f64(a[0, h]) for a in (q, k, v, do))
@@ -358,11 +360,11 @@ def test_full_size_long_sampled():
         dq_r, dk_r, dv_r = O.backward_head(qf, kf, vf, dof, g, oi, oc, SCALE,
                                            query_blocks=sorted(set(qbs) | set(keepers)))
         for i in qbs:
-            tok = perm[i * 128:(i + 1) * 128]
+            tok = O.block_tokens(perm, i, g.n)
             assert np.abs(lse[0, h][tok] - lse_r[tok]).max() <= LSE_ABS
             check_close(f"dq head {h} block {i}", dq[0, h][tok], dq_r[tok])
         for kb in kbs:
-            tok = perm[kb * 128:(kb + 1) * 128]
+            tok = O.block_tokens(kperm, kb, kg.n)
             if not any(kb in set(oi[i, :oc[i]].tolist()) for i in range(nb)):
                 assert np.all(dk[0, h][tok] == 0) and np.all(dv[0, h][tok] == 0)
                 continue
