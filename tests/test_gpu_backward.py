@@ -307,13 +307,15 @@ def test_deterministic():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["long", "long_q64", "long_k64"])
+@pytest.mark.parametrize("name", ["long", "long_q64", "long_k64", "long_k256", "vc"])
 def test_full_size_sampled(name):
-    """215,040 tokens, 32 heads (the configurations the benchmark times: 128-
-    token blocks, 64-token query blocks taken in pairs by dQ, 64-token key
-    blocks): the backward runs on every head; the oracle checks dq of sampled
-    query blocks and dk, dv of sampled key blocks (visiting every query block
-    that kept them) on two heads. The selection is the oracle's own."""
+    """Full-size workloads, 32 heads (the configurations the benchmark times:
+    215,040 tokens with 128-token blocks, 64-token query blocks taken in pairs
+    by dQ, 64- and 256-token key blocks; 61,440 tokens with condition frames
+    and CDF selection). The backward runs on every head; the oracle checks dq
+    of sampled query blocks and dk, dv of sampled key blocks (visiting every
+    query block that kept them) on two heads. The selection is the oracle's
+    own."""
     import torch
 
     w = WORKLOADS[name]
