@@ -264,17 +264,20 @@ def test_key_chunks(grid, chunk, key_chunk, params, cond):
     _run_and_compare(problem, params, q, k, v)
 
 
-def test_query_chunk_64_dense_and_lse():
+@pytest.mark.parametrize("cond", [4, 2])
+def test_query_chunk_64_dense_and_lse(cond):
     """64-token query blocks: dense attention against the oracle's dense
     (block-causal) attention, and bsa_attention_lse: the same o as
-    bsa_attention and lse against the oracle's."""
+    bsa_attention and lse against the oracle's. With an even number of
+    condition t-rows the dense kernel runs on boxes of twice the chunk's
+    depth; with an odd one (cond 2) on the chunk itself."""
     import torch
 
     from video_dit_block_bsa_amd import binding as B
 
     T, H, W = 8, 16, 32
     q, k, v = make_qkv(T, H, W, 2, kind="field", seed=29)
-    problem = Problem.make(T, H, W, 2, chunk=(2, 4, 8), cond_frames=4)
+    problem = Problem.make(T, H, W, 2, chunk=(2, 4, 8), cond_frames=cond)
     g = PT.geometry(problem)
     qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
     o = O.bf16_bits_to_f64(PT.from_device(PT.run_dense(problem, qd, kd, vd)).reshape(q.shape))

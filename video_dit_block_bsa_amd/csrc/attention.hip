@@ -606,21 +606,34 @@ hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* 
   bool part = needs_general(g);
   if (dense) {
     // Dense attention walks all allowed keys in blocks of the query chunk.
+    // Its result does not depend on the block shape, so 64-token chunks run
+    // as boxes of twice their depth when those tile the grid and the
+    // condition frames (half the key traffic per query).
     Geom gd = g;
-    gd.ctk = g.ct;
-    gd.chk = g.ch;
-    gd.cwk = g.cw;
-    gd.nHk = g.nH;
-    gd.nWk = g.nW;
-    gd.nbk = g.nb;
-    gd.nk = g.nq;
-    gd.cond_kblocks = g.cond_blocks;
+    const int rows = g.nb / (g.nH * g.nW);
+    if (split && !g.partial && q_begin == 0 && rows % 2 == 0 &&
+        (g.cond_blocks / (g.nH * g.nW)) % 2 == 0) {
+      gd.ct = 2 * g.ct;
+      gd.nq = kBlockTokens;
+      gd.nb = g.nb / 2;
+      gd.cond_blocks = g.cond_blocks / 2;
+      grid = dim3((unsigned)((size_t)g.bh * ((gd.nb + 7) / 8 * 8)));
+    }
+    const bool split_d = gd.nq != kBlockTokens;
+    gd.ctk = gd.ct;
+    gd.chk = gd.ch;
+    gd.cwk = gd.cw;
+    gd.nHk = gd.nH;
+    gd.nWk = gd.nW;
+    gd.nbk = gd.nb;
+    gd.nk = gd.nq;
+    gd.cond_kblocks = gd.cond_blocks;
     const AttnArgs a = make_attn_args(gd, 1, q_begin);
     part = needs_general(gd);
 #define BSA_LAUNCH_DENSE(MODE, SPLIT, PART)                                                          \
   hipLaunchKernelGGL((attn_kernel<true, false, MODE, SPLIT, PART>), grid, dim3(kThreads), 0, stream, \
                      a, q, k, v, idx, cnt, o, nullptr)
-    if (split) {
+    if (split_d) {
       if (part) BSA_LAUNCH_DENSE(2, true, true);
       else BSA_LAUNCH_DENSE(2, true, false);
     } else {
