@@ -7,7 +7,8 @@ that each block still attends exactly to its own list: selections from the
 select kernel, hand-made lists (unordered, ids outside [0, Nk), a list
 that one block of a pair has and the other lacks, empty lists), random
 shuffled lists, the log-normaliser output, and grids with an odd number of
-t-rows.
+t-rows. The dense baseline runs 64-token chunks on boxes of twice their
+depth where those tile the grid; its cases come last.
 """
 
 from __future__ import annotations
@@ -197,3 +198,26 @@ def test_pairs_backward_shuffled_lists():
         ids[bad] = rng.choice([-2, nbk, nbk + 9], size=int(bad.sum()))
         idx[r] = ids
     compare_all(problem, q, k, v, do, idx, cnt, stride)
+
+
+# Dense baseline with 64-token query chunks: boxes of twice the chunk's depth
+# when they tile the grid and the condition rows, the chunk itself otherwise.
+@pytest.mark.parametrize("grid,chunk,cond,batch,heads", [
+    ((8, 16, 32), (2, 4, 8), 0, 1, 2),     # doubled boxes
+    ((8, 8, 32), (1, 8, 8), 2, 2, 3),      # doubled boxes, condition rows, batch 2
+    ((12, 16, 16), (4, 2, 8), 4, 1, 2),    # three t-rows: the chunk itself
+    ((8, 16, 32), (2, 4, 8), 2, 1, 2),     # one condition row: the chunk itself
+])
+def test_dense_64_token_chunks(grid, chunk, cond, batch, heads):
+    T, H, W = grid
+    q, k, v = make_qkv(T, H, W, heads, batch=batch, kind="field", seed=92)
+    problem = Problem.make(T, H, W, heads, batch=batch, chunk=chunk, cond_frames=cond)
+    g = PT.geometry(problem)
+    out = PT.from_device(PT.run_dense(problem, *(PT.to_device(a) for a in (q, k, v))))
+    out = out.reshape(q.shape)
+    for b in range(batch):
+        for h in range(heads):
+            ref = O.dense_head(*(O.bf16_bits_to_f64(a[b, h]) for a in (q, k, v)), g, SCALE)
+            err = np.abs(O.bf16_bits_to_f64(out[b, h]) - ref)
+            _log(f"dense ({b},{h}): max-abs {err.max():.3e}, mean-abs {err.mean():.3e}")
+            assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS

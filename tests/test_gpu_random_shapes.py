@@ -3,9 +3,10 @@
 Each case draws a latent grid (often one that the chunks do not divide), a
 query chunk of 64 or 128 tokens, a key chunk of 64 to 1024 tokens or none,
 condition frames, batch and heads, and a top-k or CDF rule. The forward is
-checked on every index row and every output (the rules of the parity tests);
-the backward, on the oracle's own selection, on every gradient element (the
-tolerances of the backward tests). Inputs are i.i.d. N(0, 1).
+checked on every index row and every output (the rules of the parity tests),
+and the dense baseline on every output; the backward, on the oracle's own
+selection, on every gradient element (the tolerances of the backward tests).
+Inputs are i.i.d. N(0, 1).
 """
 
 from __future__ import annotations
@@ -15,6 +16,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle.bsa_oracle as O
 import parity as PT
 from test_gpu_backward import compare_all, oracle_selection
 from test_gpu_parity import _run_and_compare
@@ -22,6 +24,8 @@ from video_dit_block_bsa_amd.binding import Problem, SelectParams
 from video_dit_block_bsa_amd.inputs import make_grad, make_qkv
 
 pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(128)
 
 QUERY_CHUNKS = [(4, 4, 8), (2, 4, 8), (4, 2, 8), (2, 8, 8), (8, 4, 4), (1, 8, 16), (4, 8, 4), (2, 2, 16)]
 KEY_CHUNKS = [None, None, (2, 4, 8), (4, 4, 8), (4, 8, 8), (2, 8, 16), (8, 8, 16), (1, 8, 32)]
@@ -60,6 +64,14 @@ def test_forward_random_shape(seed):
     q, k, v = make_qkv(problem.T, problem.H, problem.W, problem.heads, batch=problem.batch,
                        kind="iid", seed=2000 + seed)
     _run_and_compare(problem, params, q, k, v)
+    dense = PT.from_device(PT.run_dense(problem, *(PT.to_device(a) for a in (q, k, v))))
+    dense = dense.reshape(q.shape)
+    g = PT.geometry(problem)
+    for b in range(problem.batch):
+        for h in range(problem.heads):
+            ref = O.dense_head(*(O.bf16_bits_to_f64(a[b, h]) for a in (q, k, v)), g, SCALE)
+            err = np.abs(O.bf16_bits_to_f64(dense[b, h]) - ref)
+            assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS, (b, h, err.max())
 
 
 @pytest.mark.parametrize("seed", range(12))
