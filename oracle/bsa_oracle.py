@@ -61,9 +61,10 @@ with its reason in the design notes of the repository):
 
 Backward pass (the gradients of the attention step for fixed selections):
 [DeepDive] "Implementation details and design trade-offs" states that the
-operator has both a forward and a backward pass, and [Blog-CN] section 7
-("实现 cross-reference") lists separate dQ and dK/dV backward kernels and a
-forward-to-backward transpose of the block index lists. The pages print no
+operator has both a forward and a backward pass, and [Notes] section 7
+("实现 cross-reference", on the same zhaifeiyue notes page) lists separate
+dQ and dK/dV backward kernels and a forward-to-backward transpose of the
+block index lists. The pages print no
 backward formulas; ``backward_head`` differentiates the forward above
 (softmax over the gathered keys) by the chain rule, and treats the block
 selection as a constant (it is a discrete choice with no gradient).
@@ -231,7 +232,11 @@ def index_stride(params: SelectParams) -> int:
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
-    """Exact widening of bfloat16 bit patterns (uint16) to float64."""
+    """Exact widening of bfloat16 bit patterns (uint16) to float64.
+
+    bfloat16 is the upper half of an IEEE-754 binary32, so the pattern moved
+    into the high 16 bits of a 32-bit word is that float32 exactly (the pages
+    fix no input precision; the inputs here are bf16 tensors)."""
     u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u32.view(np.float32).astype(np.float64)
 

@@ -9,6 +9,7 @@ mistakes in the oracle and checks that some pin catches each one.
 from __future__ import annotations
 
 import json
+import math
 import os
 from fractions import Fraction
 
@@ -729,7 +730,57 @@ def pin_partial_backward_autograd():
             assert np.abs(mine - ref.numpy()).max() < 1e-10
 
 
+# ------------------------------------------------------ bf16 widening ---
+def _bf16_by_format(bits: int) -> float:
+    """Value of a bfloat16 bit pattern from the format's definition: 1 sign
+    bit, 8 exponent bits with bias 127 and 7 fraction bits (the upper half of
+    an IEEE-754 binary32). Written from the field layout, not by shifting into
+    a float32."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * float("inf") if f == 0 else float("nan")
+    if e == 0:  # subnormal: 2^-126 * f/128
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+def pin_bf16_widening():
+    """bf16_bits_to_f64 against values the bfloat16 format fixes: hand-worked
+    patterns, then all 65,536 patterns against the field-by-field definition
+    (NaN patterns must widen to NaN, -0 must keep its sign)."""
+    known = {
+        0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0xC000: -2.0, 0x3F00: 0.5,
+        0xC049: -3.140625,            # -(1 + 73/128) * 2
+        0x0001: 2.0 ** -133,          # smallest subnormal
+        0x807F: -(127 / 128) * 2.0 ** -126,  # largest negative subnormal
+        0x0080: 2.0 ** -126,          # smallest normal
+        0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,  # largest finite
+        0x7F80: math.inf, 0xFF80: -math.inf,
+    }
+    got = O.bf16_bits_to_f64(np.array(list(known), dtype=np.uint16))
+    for (bits, want), val in zip(known.items(), got):
+        assert val == want, f"0x{bits:04X}: {val!r} != {want!r}"
+    nz = O.bf16_bits_to_f64(np.array([0x8000, 0x0000], dtype=np.uint16))
+    assert nz[0] == 0.0 and math.copysign(1.0, nz[0]) == -1.0, "0x8000 must widen to -0.0"
+    assert math.copysign(1.0, nz[1]) == 1.0, "0x0000 must widen to +0.0"
+    for bits in (0x7FC0, 0xFFC1, 0x7F81):
+        assert math.isnan(O.bf16_bits_to_f64(np.array([bits], dtype=np.uint16))[0])
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    wide = O.bf16_bits_to_f64(allbits)
+    assert wide.dtype == np.float64 and wide.shape == (1 << 16,)
+    ref = np.array([_bf16_by_format(int(b)) for b in allbits], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(wide), nan)
+    assert np.array_equal(wide[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(wide[~nan]), np.signbit(ref[~nan]))
+    # A 2-D array keeps its shape (the oracle widens [S, d] tensors).
+    assert O.bf16_bits_to_f64(np.full((3, 5), 0x3F80, dtype=np.uint16)).shape == (3, 5)
+
+
 ALL_PINS = [
+    pin_bf16_widening,
     pin_block_order_geometry,
     pin_handworked_golden,
     pin_dense_equals_textbook,

@@ -17,9 +17,11 @@ softmax is peaked (dP - D is small next to D), and dQ = s dS K inherits the
 absolute error s P dD K, which is a larger fraction of a smaller dQ. On the
 smooth-field inputs this doubles to triples the relative error (measured up
 to 0.6% mean, 2.2% max), and more where blocks are small and the softmax
-sharper: on the 6 x 6 x 12 grid (partial blocks of 16 to 64 tokens) a numpy
-model of exactly these roundings (bf16 P, dS, O and dQ, fp64 otherwise)
-gives 1.04-1.08% mean and 2.7% max against the float64 oracle. dQ takes
+sharper: on the 6 x 6 x 12 grid (partial blocks of 16 to 64 tokens) the
+numpy model of exactly these roundings in tests/bf16_error_model.py (bf16 P,
+dS, O and dQ, fp64 otherwise) gives 1.04-1.08% mean and 2.7% max against the
+float64 oracle; tests/test_tolerance_model.py derives the bound below from
+it on the CPU. dQ takes
   max <= 4e-2 * max |oracle|,  mean <= 1.5e-2 * mean |oracle|.
 lse: |gpu - oracle| <= 2.5e-3. The forward sums bf16-rounded probabilities,
 each within a relative 2^-9, so the sum and its log are off by at most

@@ -13,6 +13,24 @@ _orig_order = O.block_token_order
 _orig_pool = O.pool_blocks
 _orig_cdf = O.select_cdf
 _orig_lse = O.forward_lse_head
+_orig_bf16 = O.bf16_bits_to_f64
+
+
+def _bf16_shift15(bits):
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def _bf16_as_float16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _bf16_sign_dropped(bits):
+    return np.abs(_orig_bf16(bits))
+
+
+def _bf16_low_half(bits):
+    return np.asarray(bits, dtype=np.uint16).astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def _attend_no_scale(q, k, v, g, i, key_blocks, scale, perm=None, kperm=None):
@@ -163,6 +181,10 @@ def _lse_without_max(q, k, v, g, idx, cnt, scale, query_blocks=None):
 
 
 MUTANTS = {
+    "bf16 widened with a 15-bit shift": ("bf16_bits_to_f64", _bf16_shift15),
+    "bf16 read as float16": ("bf16_bits_to_f64", _bf16_as_float16),
+    "bf16 sign dropped": ("bf16_bits_to_f64", _bf16_sign_dropped),
+    "bf16 placed in the low half of a float32": ("bf16_bits_to_f64", _bf16_low_half),
     "attention scale dropped": ("attend_query_block", _attend_no_scale),
     "keys used as values": ("attend_query_block", _attend_keys_as_values),
     "intra-block order h/w swapped": ("block_token_order", _order_hw_swapped),
