@@ -204,7 +204,7 @@ def cond_cache_bench(w, problem, params, qd, kd, vd, stride, full_ms, steps):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    cond_blocks = (w.cond_frames // w.chunk[0]) * (w.H // w.chunk[1]) * (w.W // w.chunk[2])
+    cond_blocks = w.cond_blocks
     log(f"[bench] condition-KV cache step: {ms:.3f} ms (full step {full_ms:.3f} ms)")
     del idx, cnt, o, ws, cache
     return {
@@ -264,7 +264,7 @@ def main():
     qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
     problem = B.Problem.from_workload(w)
     params = B.SelectParams.from_workload(w)
-    stride = B.index_stride(params)
+    stride = B.index_stride(problem, params)
     rows = w.batch * w.heads * w.num_blocks
     idx = torch.empty((rows, stride), dtype=torch.int32, device="cuda")
     cnt = torch.empty((rows,), dtype=torch.int32, device="cuda")

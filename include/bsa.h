@@ -101,8 +101,17 @@ typedef struct bsa_select_params {
 } bsa_select_params;
 
 /* Row length of the idx array written by bsa_select: k (top-k) or k_max
- * (CDF). Returns -1 on invalid parameters. */
-int32_t bsa_index_stride(const bsa_select_params* params);
+ * (CDF), the most key blocks one query block can keep under the rule
+ * ("Top-r" and "CDF-p" modes, deep dive "Implementation details and design
+ * trade-offs"). `problem` may be NULL; when given it is validated too.
+ * Returns -1 on an invalid problem or parameters. */
+int32_t bsa_index_stride(const bsa_problem* problem, const bsa_select_params* params);
+
+/* Bytes of device workspace one BSA step needs when bsa_select and
+ * bsa_attention share a single buffer (the larger of the two sizes below;
+ * the calls are ordered on one stream, so the buffer can be reused).
+ * Returns 0 on invalid arguments. */
+size_t bsa_workspace_bytes(const bsa_problem* problem, const bsa_select_params* params);
 
 /* Bytes of device workspace bsa_select needs: pooled Q (512 bytes per query
  * block), pooled K (512 bytes per key block) and the Nb x Nk pooled score
@@ -149,8 +158,13 @@ bsa_status bsa_attention(const bsa_problem* problem, const void* q, const void* 
 
 /* Dense softmax attention over every key the query may see (all keys, or
  * condition keys only for condition queries when cond_frames > 0): the
- * baseline that BSA is measured against, using the same tile engine. The key
- * chunk plays no part. Arguments as for bsa_attention. */
+ * baseline that BSA is measured against. The pages' baseline is dense
+ * FlashAttention-3 on one H800 (the charles2530 write-up, section "高效推理：
+ * C2F 与 BSA", speed table; deep dive, "Block Sparse Attention": BSA keeps
+ * under 10 % of the dense attention compute). Here it runs on the same tile
+ * engine as bsa_attention, with every allowed key block taken in order, so
+ * the speedup measures the sparsity, not a different kernel. The key chunk
+ * plays no part. Arguments as for bsa_attention. */
 bsa_status dense_attention(const bsa_problem* problem, const void* q, const void* k,
                            const void* v, void* o, void* workspace,
                            size_t workspace_bytes, void* stream);

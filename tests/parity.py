@@ -43,7 +43,7 @@ def run_select(problem, params, q_d, k_d):
 
     from video_dit_block_bsa_amd import binding as B
 
-    stride = B.index_stride(params)
+    stride = B.index_stride(problem, params)
     rows = problem.batch * problem.heads * problem.num_blocks
     idx = torch.full((max(rows, 1), stride), -7, dtype=torch.int32, device="cuda")
     cnt = torch.full((max(rows, 1),), -7, dtype=torch.int32, device="cuda")

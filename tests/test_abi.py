@@ -61,9 +61,33 @@ def test_workspace_sizes():
 
 
 def test_index_stride():
-    assert B.index_stride(B.SelectParams.topk(45)) == 45
-    assert B.index_stride(B.SelectParams.cdf(0.9, 4, 64)) == 64
-    assert B.index_stride(B.SelectParams.topk(0)) == -1
+    p = _problem()
+    assert B.index_stride(p, B.SelectParams.topk(45)) == 45
+    assert B.index_stride(p, B.SelectParams.cdf(0.9, 4, 64)) == 64
+    assert B.index_stride(None, B.SelectParams.cdf(0.9, 4, 64)) == 64
+    assert B.index_stride(p, B.SelectParams.topk(0)) == -1
+    assert B.index_stride(_problem(head_dim=64), B.SelectParams.topk(4)) == -1
+
+
+def test_boundary_names_of_the_contract():
+    """The hot-path contract's entry points and helpers, by name: bsa_select,
+    bsa_attention, dense_attention, bsa_workspace_bytes(problem, params),
+    bsa_index_stride(problem, params) and bsa_status_string. The split
+    workspace helpers come on top."""
+    names = declared_functions()
+    for must in ("bsa_select", "bsa_attention", "dense_attention", "bsa_workspace_bytes",
+                 "bsa_index_stride", "bsa_status_string", "bsa_select_workspace_bytes",
+                 "bsa_attention_workspace_bytes"):
+        assert must in names, must
+    text = open(HEADER).read()
+    assert re.search(r"int32_t bsa_index_stride\(const bsa_problem\* problem,\s*"
+                     r"const bsa_select_params\* params\)", text)
+    assert re.search(r"size_t bsa_workspace_bytes\(const bsa_problem\* problem,\s*"
+                     r"const bsa_select_params\* params\)", text)
+    p, sp = _problem(), B.SelectParams.topk(105)
+    assert B.workspace_bytes(p, sp) == max(B.select_workspace_bytes(p, sp),
+                                           B.attention_workspace_bytes(p))
+    assert B.workspace_bytes(_problem(head_dim=64), sp) == 0
 
 
 def _select(problem, params, q=FAKE, k=FAKE, idx=FAKE, cnt=FAKE, ws=FAKE, ws_bytes=1 << 40):
@@ -303,3 +327,39 @@ def test_partial_grids():
     assert q.num_key_blocks == 14 * 12 * 2
     assert B.select_workspace_bytes(q, sp) > 0
     assert B.attention_bwd_workspace_bytes(p) == B.attention_bwd_workspace_bytes(_problem(T=60))
+
+
+def test_binding_checks_tensors_before_the_library():
+    """The binding rejects a wrong dtype, a non-contiguous view, too few
+    elements and a host tensor before any pointer reaches the library (which
+    cannot see sizes or strides). Runs on the CPU: every call fails in the
+    binding's own checks."""
+    import torch
+
+    p = B.Problem.make(8, 8, 16, 2)  # 1024 tokens, 8 blocks, 2 heads
+    n = 2 * 1024 * 128
+    good = torch.empty(n, dtype=torch.bfloat16)
+    sp = B.SelectParams.topk(2)
+    idx = torch.empty(16 * 2, dtype=torch.int32)
+    cnt = torch.empty(16, dtype=torch.int32)
+    cases = [
+        ("q must be torch.bfloat16", dict(q=torch.empty(n, dtype=torch.float16))),
+        ("q must be contiguous", dict(q=torch.empty(2 * n, dtype=torch.bfloat16)[::2])),
+        ("needs at least", dict(q=torch.empty(n - 1, dtype=torch.bfloat16))),
+        ("must be on a GPU", dict(q=good)),
+    ]
+    for msg, kw in cases:
+        args = dict(q=good, k=good, v=good, o=good)
+        args.update(kw)
+        with pytest.raises(B.BSAError, match=msg):
+            B.bsa_attention(p, args["q"], args["k"], args["v"], idx, cnt, 2, args["o"],
+                            (0, 0), stream=0)
+    with pytest.raises(B.BSAError, match="idx must be torch.int32"):
+        B.bsa_select(p, sp, FAKE, FAKE, idx.to(torch.int64), cnt, (0, 0), stream=0)
+    with pytest.raises(B.BSAError, match="idx holds 31 elements"):
+        B.bsa_select(p, sp, FAKE, FAKE, idx[:31], cnt, (0, 0), stream=0)
+    with pytest.raises(B.BSAError, match="cnt holds"):
+        B.bsa_attention(p, FAKE, FAKE, FAKE, FAKE, cnt[:15], 2, FAKE, (0, 0), stream=0)
+    with pytest.raises(B.BSAError, match="lse must be torch.float32"):
+        B.bsa_attention_lse(p, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE,
+                            torch.empty(2048, dtype=torch.float64), (0, 0), stream=0)

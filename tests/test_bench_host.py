@@ -46,3 +46,29 @@ def test_traffic_record_matches_kernel_source():
     assert rec["kernel_source_sha"] == bench.kernel_source_hash()
     for name in ("long", "720p", "480p", "vc"):
         assert bench.traffic_for(name) > 0
+
+
+@pytest.mark.parametrize("grid,chunk,key_chunk", [
+    ((6, 6, 12), (4, 4, 8), ()),
+    ((10, 20, 36), (4, 4, 8), (4, 8, 8)),
+    ((93, 45, 80), (4, 4, 8), (2, 4, 8)),
+    ((56, 48, 80), (4, 4, 8), ()),
+])
+def test_workload_block_counts_match_the_library(grid, chunk, key_chunk):
+    """bench.py sizes idx and cnt from Workload.num_blocks: on a grid the
+    chunk does not divide it must count partial blocks as the library does
+    (ceilings), or bsa_select would write past the end of idx."""
+    from video_dit_block_bsa_amd import binding as B
+    from video_dit_block_bsa_amd.workloads import Workload
+
+    w = Workload("t", *grid, heads=2, chunk=chunk, key_chunk=key_chunk)
+    p = B.Problem.from_workload(w)
+    assert w.num_blocks == p.num_blocks
+    assert w.num_key_blocks == p.num_key_blocks
+    # The library's own counts, read back from its workspace size (the layout
+    # documented in bsa.h: pooled Q, pooled K and the pooled scores, fp32,
+    # each part rounded up to 256 bytes).
+    nb, nk = w.num_blocks, w.num_key_blocks
+    a = lambda x: -(-x // 256) * 256
+    want = a(2 * nb * 512) + a(2 * nk * 512) + a(2 * nb * nk * 4)
+    assert B.select_workspace_bytes(p, B.SelectParams.topk(3)) == want

@@ -68,7 +68,7 @@ def test_noisy_rows_match_full_path(grid, chunk, key_chunk, params, cond):
     problem = Problem.make(T, H, W, heads, chunk=chunk, cond_frames=cond, key_chunk=key_chunk)
     g = PT.geometry(problem)
     nb, cq = g.num_blocks, g.cond_blocks
-    stride = B.index_stride(params)
+    stride = B.index_stride(problem, params)
     steps = _step_tensors(T, H, W, heads, cond, 51, 52)
     cache = torch.full((max(B.cond_cache_bytes(problem), 16) // 4,), float("nan"), dtype=torch.float32,
                        device="cuda")
@@ -121,7 +121,7 @@ def test_vc_workload_full_size():
     w = WORKLOADS["vc"]
     problem = Problem.from_workload(w)
     params = SelectParams.from_workload(w)
-    stride = B.index_stride(params)
+    stride = B.index_stride(problem, params)
     g = PT.geometry(problem)
     nb, cq = g.num_blocks, g.cond_blocks
     q, k, v = make_qkv(w.T, w.H, w.W, w.heads, kind=w.kind, seed=w.seed)

@@ -287,7 +287,7 @@ def test_query_chunk_64_dense_and_lse(cond):
         _log(f"dense q64 head {h}: max-abs {err.max():.3e}, mean-abs {err.mean():.3e}")
         assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS
     params = SelectParams.topk(5)
-    stride = B.index_stride(params)
+    stride = B.index_stride(problem, params)
     idx_d, cnt_d = PT.run_select(problem, params, qd, kd)
     o1 = PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, stride)
     o2 = torch.full_like(qd, float("nan"))
@@ -405,7 +405,7 @@ def test_partial_blocks_dense_and_lse(chunk):
         _log(f"dense partial {chunk} head {h}: max-abs {err.max():.3e}, mean-abs {err.mean():.3e}")
         assert err.max() <= PT.MAX_ABS and err.mean() <= PT.MEAN_ABS
     params = SelectParams.topk(6)
-    stride = B.index_stride(params)
+    stride = B.index_stride(problem, params)
     idx_d, cnt_d = PT.run_select(problem, params, qd, kd)
     o1 = PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, stride)
     o2 = torch.full_like(qd, float("nan"))

@@ -144,7 +144,7 @@ def test_pairs_lse():
     g = PT.geometry(problem)
     qd, kd, vd = PT.to_device(q), PT.to_device(k), PT.to_device(v)
     params = SelectParams.topk(5)
-    stride = B.index_stride(params)
+    stride = B.index_stride(problem, params)
     idx_d, cnt_d = PT.run_select(problem, params, qd, kd)
     o1 = PT.run_attention(problem, qd, kd, vd, idx_d, cnt_d, stride)
     o2 = torch.full_like(qd, float("nan"))

@@ -2,7 +2,9 @@
 
 Argument marshalling only: every function here turns Python objects into
 the pointers and sizes of the C entry point of the same name and raises
-``BSAError`` on a non-OK status. Device buffers may be torch tensors (their
+``BSAError`` on a non-OK status. Torch tensors are checked first (dtype,
+contiguous layout, GPU device, enough elements for the problem), because
+the library receives bare pointers and cannot see sizes or strides. Device buffers may be torch tensors (their
 ``data_ptr()`` is passed) or raw integer device addresses. ``stream`` is a
 ``torch.cuda.Stream``, a raw hipStream_t integer, or None for torch's current
 stream. The library must have been built (``python -m
@@ -122,8 +124,10 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         P, SP = ctypes.POINTER(Problem), ctypes.POINTER(SelectParams)
         vp, i32p = ctypes.c_void_p, ctypes.c_void_p
-        L.bsa_index_stride.argtypes = [SP]
+        L.bsa_index_stride.argtypes = [P, SP]
         L.bsa_index_stride.restype = ctypes.c_int32
+        L.bsa_workspace_bytes.argtypes = [P, SP]
+        L.bsa_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_select_workspace_bytes.argtypes = [P, SP]
         L.bsa_select_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_attention_workspace_bytes.argtypes = [P]
@@ -169,6 +173,43 @@ def _ptr(x):
     return x.data_ptr()
 
 
+def _require(x, name, dtype, numel):
+    """Checks a torch tensor argument before its pointer reaches the library,
+    which cannot see sizes or strides: the dtype, a contiguous layout, a GPU
+    device and at least `numel` elements. Raw integer addresses and None are
+    passed through unchecked (the library rejects NULL itself)."""
+    if x is None or isinstance(x, int):
+        return
+    import torch
+
+    if dtype is not None and x.dtype != getattr(torch, dtype):
+        raise BSAError(-1, f"{name} must be torch.{dtype} (got {x.dtype})")
+    if not x.is_contiguous():
+        raise BSAError(-1, f"{name} must be contiguous")
+    if x.numel() < numel:
+        raise BSAError(-1, f"{name} holds {x.numel()} elements, needs at least {numel}")
+    if x.device.type != "cuda":
+        raise BSAError(-1, f"{name} must be on a GPU (got {x.device})")
+
+
+def _check_qkv(problem, **tensors):
+    n = problem.batch * problem.heads * problem.seq_len * problem.head_dim
+    for name, t in tensors.items():
+        _require(t, name, "bfloat16", n)
+
+
+def _check_lists(problem, idx, cnt, stride):
+    rows = problem.batch * problem.heads * problem.num_blocks
+    _require(idx, "idx", "int32", rows * max(int(stride), 0))
+    _require(cnt, "cnt", "int32", rows)
+
+
+def _check_workspace(ws):
+    if isinstance(ws, tuple) or ws is None:
+        return
+    _require(ws, "workspace", None, 0)
+
+
 def _nbytes(x):
     if x is None:
         return 0
@@ -194,8 +235,15 @@ def _check(status):
         raise BSAError(status, msg)
 
 
-def index_stride(params: SelectParams) -> int:
-    return lib().bsa_index_stride(ctypes.byref(params))
+def index_stride(problem, params: SelectParams) -> int:
+    """bsa_index_stride; ``problem`` may be None."""
+    return lib().bsa_index_stride(None if problem is None else ctypes.byref(problem),
+                                  ctypes.byref(params))
+
+
+def workspace_bytes(problem: Problem, params: SelectParams) -> int:
+    """bsa_workspace_bytes: one buffer for bsa_select followed by bsa_attention."""
+    return lib().bsa_workspace_bytes(ctypes.byref(problem), ctypes.byref(params))
 
 
 def select_workspace_bytes(problem: Problem, params: SelectParams) -> int:
@@ -209,6 +257,9 @@ def attention_workspace_bytes(problem: Problem) -> int:
 def bsa_select(problem, params, q, k, idx, cnt, workspace, stream=None):
     """bsa_select: pooled scores and key-block selection -> idx, cnt.
     ``workspace`` is a tensor or a (pointer, nbytes) tuple."""
+    _check_qkv(problem, q=q, k=k)
+    _check_lists(problem, idx, cnt, index_stride(problem, params))
+    _check_workspace(workspace)
     ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
     _check(lib().bsa_select(ctypes.byref(problem), ctypes.byref(params), _ptr(q), _ptr(k),
                             _ptr(idx), _ptr(cnt), ws_ptr, _nbytes(workspace), _stream(stream)))
@@ -216,6 +267,9 @@ def bsa_select(problem, params, q, k, idx, cnt, workspace, stream=None):
 
 def bsa_attention(problem, q, k, v, idx, cnt, idx_stride, o, workspace, stream=None):
     """bsa_attention: attention restricted to the listed key blocks -> o."""
+    _check_qkv(problem, q=q, k=k, v=v, o=o)
+    _check_lists(problem, idx, cnt, idx_stride)
+    _check_workspace(workspace)
     ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
     _check(lib().bsa_attention(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                _ptr(cnt), int(idx_stride), _ptr(o), ws_ptr, _nbytes(workspace),
@@ -224,6 +278,8 @@ def bsa_attention(problem, q, k, v, idx, cnt, idx_stride, o, workspace, stream=N
 
 def dense_attention(problem, q, k, v, o, workspace, stream=None):
     """dense_attention: softmax attention over every allowed key -> o."""
+    _check_qkv(problem, q=q, k=k, v=v, o=o)
+    _check_workspace(workspace)
     ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
     _check(lib().dense_attention(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                  ws_ptr, _nbytes(workspace), _stream(stream)))
@@ -236,6 +292,10 @@ def attention_bwd_workspace_bytes(problem: Problem) -> int:
 def bsa_attention_lse(problem, q, k, v, idx, cnt, idx_stride, o, lse, workspace, stream=None):
     """bsa_attention_lse: bsa_attention that also writes the per-query
     log-normaliser -> o, lse."""
+    _check_qkv(problem, q=q, k=k, v=v, o=o)
+    _check_lists(problem, idx, cnt, idx_stride)
+    _require(lse, "lse", "float32", problem.batch * problem.heads * problem.seq_len)
+    _check_workspace(workspace)
     ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
     _check(lib().bsa_attention_lse(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                    _ptr(cnt), int(idx_stride), _ptr(o), _ptr(lse), ws_ptr,
@@ -246,6 +306,10 @@ def bsa_attention_bwd(problem, q, k, v, o, dout, lse, idx, cnt, idx_stride, dq, 
                       workspace, stream=None):
     """bsa_attention_bwd: gradients of sum(dout * o) for fixed selections
     -> dq, dk, dv."""
+    _check_qkv(problem, q=q, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv)
+    _check_lists(problem, idx, cnt, idx_stride)
+    _require(lse, "lse", "float32", problem.batch * problem.heads * problem.seq_len)
+    _check_workspace(workspace)
     ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
     _check(lib().bsa_attention_bwd(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                    _ptr(dout), _ptr(lse), _ptr(idx), _ptr(cnt), int(idx_stride),
@@ -259,6 +323,9 @@ def cond_cache_bytes(problem: Problem) -> int:
 
 def bsa_pool_cond_keys(problem, k, cache, stream=None):
     """bsa_pool_cond_keys: pooled condition keys -> cache (tensor or (ptr, nbytes))."""
+    _check_qkv(problem, k=k)
+    if not isinstance(cache, tuple):
+        _require(cache, "cache", "float32", cond_cache_bytes(problem) // 4)
     cache_ptr = cache[0] if isinstance(cache, tuple) else _ptr(cache)
     _check(lib().bsa_pool_cond_keys(ctypes.byref(problem), _ptr(k), cache_ptr, _nbytes(cache),
                                     _stream(stream)))
@@ -267,6 +334,11 @@ def bsa_pool_cond_keys(problem, k, cache, stream=None):
 def bsa_select_noisy(problem, params, q, k, cache, idx, cnt, workspace, stream=None):
     """bsa_select_noisy: selection for the noisy query blocks, condition
     pooled keys from the cache."""
+    _check_qkv(problem, q=q, k=k)
+    _check_lists(problem, idx, cnt, index_stride(problem, params))
+    if not isinstance(cache, tuple):
+        _require(cache, "cache", "float32", cond_cache_bytes(problem) // 4)
+    _check_workspace(workspace)
     ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
     cache_ptr = cache[0] if isinstance(cache, tuple) else _ptr(cache)
     _check(lib().bsa_select_noisy(ctypes.byref(problem), ctypes.byref(params), _ptr(q), _ptr(k),
@@ -276,6 +348,9 @@ def bsa_select_noisy(problem, params, q, k, cache, idx, cnt, workspace, stream=N
 
 def bsa_attention_noisy(problem, q, k, v, idx, cnt, idx_stride, o, workspace, stream=None):
     """bsa_attention_noisy: attention for the noisy query blocks -> o."""
+    _check_qkv(problem, q=q, k=k, v=v, o=o)
+    _check_lists(problem, idx, cnt, idx_stride)
+    _check_workspace(workspace)
     ws_ptr = workspace[0] if isinstance(workspace, tuple) else _ptr(workspace)
     _check(lib().bsa_attention_noisy(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                      _ptr(cnt), int(idx_stride), _ptr(o), ws_ptr,

@@ -44,10 +44,12 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, save_asm: str | None = None) -> str:
-    """Compile every source and link libbsa.so; returns the library path."""
-    objs = []
+    """Compile every source (in parallel, one hipcc per file) and link
+    libbsa.so; returns the library path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     with tempfile.TemporaryDirectory(prefix="bsa_build_") as tmp:
-        for src in SOURCES:
+        def compile_one(src):
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
             if save_asm:
@@ -63,7 +65,11 @@ def build(verbose: bool = False, save_asm: str | None = None) -> str:
                 raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
             if errs.strip() and verbose:
                 print(errs, file=sys.stderr)
-            objs.append(obj)
+            return obj
+
+        jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            objs = list(pool.map(compile_one, SOURCES))
         tmp_lib = LIB + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         res = subprocess.run(cmd, capture_output=True, text=True)

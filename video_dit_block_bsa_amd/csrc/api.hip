@@ -287,9 +287,21 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 extern "C" {
 
-int32_t bsa_index_stride(const bsa_select_params* params) {
+int32_t bsa_index_stride(const bsa_problem* problem, const bsa_select_params* params) {
+  if (problem) {
+    Checked c;
+    if (check_problem(problem, &c) != BSA_OK) return -1;
+  }
   if (check_params(params) != BSA_OK) return -1;
   return params->mode == BSA_TOPK ? params->k : params->k_max;
+}
+
+size_t bsa_workspace_bytes(const bsa_problem* problem, const bsa_select_params* params) {
+  Checked c;
+  if (check_problem(problem, &c) != BSA_OK || check_params(params) != BSA_OK) return 0;
+  const size_t sel = select_layout(c.g).total;
+  const size_t att = attention_ws(c.g);
+  return sel > att ? sel : att;
 }
 
 size_t bsa_select_workspace_bytes(const bsa_problem* problem, const bsa_select_params* params) {

@@ -12,6 +12,10 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 
 
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
@@ -39,8 +43,16 @@ class Workload:
 
     @property
     def num_blocks(self) -> int:
+        """Query blocks per (batch, head). Counts are ceilings: a chunk that
+        does not divide the grid leaves a partial block at the far edge."""
         ct, ch, cw = self.chunk
-        return (self.T // ct) * (self.H // ch) * (self.W // cw)
+        return _cdiv(self.T, ct) * _cdiv(self.H, ch) * _cdiv(self.W, cw)
+
+    @property
+    def cond_blocks(self) -> int:
+        """Leading condition query blocks (cond_frames is a multiple of ct)."""
+        ct, ch, cw = self.chunk
+        return (self.cond_frames // ct) * _cdiv(self.H, ch) * _cdiv(self.W, cw)
 
     @property
     def block_tokens(self) -> int:
@@ -59,7 +71,7 @@ class Workload:
     @property
     def num_key_blocks(self) -> int:
         a, b, c = self.kchunk
-        return (self.T // a) * (self.H // b) * (self.W // c)
+        return _cdiv(self.T, a) * _cdiv(self.H, b) * _cdiv(self.W, c)
 
     @property
     def stride(self) -> int:
