@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
 METRIC = "BSA effective TFLOP/s & ms/layer at 720p-scale (~92K/215K tokens), % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "video_dit_block_bsa_amd", "csrc", f)
@@ -35,6 +36,54 @@ KERNEL_SOURCES = [os.path.join(ROOT, "video_dit_block_bsa_amd", "csrc", f)
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def device_info() -> dict:
+    """Compute-unit count and maximum engine clock of the GPU agent as
+    rocminfo reports them (the peak figures assume 256 CUs at 2.4 GHz)."""
+    import subprocess
+
+    info = {"source": "rocminfo"}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        out = ""
+    agent = None
+    for block in out.split("*******"):
+        if "gfx950" in block and "Compute Unit:" in block:
+            agent = block
+            break
+    if agent:
+        for line in agent.splitlines():
+            key, _, val = line.strip().partition(":")
+            val = val.strip().split()[0] if val.strip() else ""
+            if key == "Marketing Name":
+                info["name"] = line.split(":", 1)[1].strip()
+            elif key == "Compute Unit" and val.isdigit():
+                info["compute_units"] = int(val)
+            elif key == "Max Clock Freq. (MHz)" and val.isdigit():
+                info["max_clock_mhz"] = int(val)
+    if "compute_units" not in info or not info.get("name"):
+        import torch
+
+        props = torch.cuda.get_device_properties(0)
+        if "compute_units" not in info:
+            info.update(source="torch", compute_units=props.multi_processor_count)
+        info["name"] = info.get("name") or props.name
+    return info
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 def kernel_source_hash() -> str:
@@ -65,6 +114,36 @@ def traffic_for(workload_name: str):
     if not w:
         return None
     return w.get("hbm_bytes_per_launch")
+
+
+def roofline_record(flops: float, avg_ms: float, traffic) -> dict:
+    """Roofline of the attention kernel (the step's dominant kernel, one
+    launch per bsa_attention call) against both roofs: effective flops over
+    the bf16 MFMA peak, and HBM-side bytes counted by rocprofv3 (FETCH_SIZE
+    and WRITE_SIZE, or None without a current record) over the HBM peak. The
+    binding roof is the one the kernel comes closer to; `achieved`, `peak`,
+    `unit` and `frac` describe that roof."""
+    sec = avg_ms * 1e-3
+    tflops = flops / sec / 1e12
+    frac_mfma = tflops / PEAK_BF16_TFLOPS
+    gbps = None if traffic is None else traffic / sec / 1e9
+    frac_hbm = None if gbps is None else gbps / PEAK_HBM_GBPS
+    hbm = frac_hbm is not None and frac_hbm > frac_mfma
+    return {
+        "bound": "hbm" if hbm else "mfma",
+        "kernel": "bsa_attention (block-sparse flash attention, attn_kernel<false, false, KeyMode>)",
+        "achieved": round(gbps if hbm else tflops, 2),
+        "peak": PEAK_HBM_GBPS if hbm else PEAK_BF16_TFLOPS,
+        "unit": "GB/s" if hbm else "TFLOP/s",
+        "frac": round(frac_hbm if hbm else frac_mfma, 4),
+        "frac_mfma": round(frac_mfma, 4),
+        "frac_hbm": None if frac_hbm is None else round(frac_hbm, 4),
+        "achieved_tflops": round(tflops, 2),
+        "achieved_hbm_gbps": None if gbps is None else round(gbps, 1),
+        "traffic": traffic,
+        "flops_per_launch": flops,
+        "avg_launch_ms": round(avg_ms, 4),
+    }
 
 
 def cpu_baseline(w, q, k, v, blocks: int, seconds: float):
@@ -105,15 +184,18 @@ def cpu_baseline(w, q, k, v, blocks: int, seconds: float):
     blocks = done
     t = t_att + t_sel * blocks / g.num_blocks
     flops = 4.0 * g.n * g.nk * w.head_dim * float(cnt[:blocks].sum())
+    rate = flops / t
     return {
-        "value": round(flops / t / 1e12, 6),
+        "value": round(rate / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"head 0 of {w.name}: selection of all {g.num_blocks} query blocks "
                    f"({t_sel:.2f} s, prorated) + float64 attention of the first {blocks} "
                    f"query blocks ({t_att:.2f} s)"),
         "seconds": round(t_sel + t_att, 2),
+        "rate_flop_per_s": rate,
     }
 
 
@@ -306,6 +388,7 @@ def main():
     wall = time.perf_counter() - t0
     sel_ms = [e[0].elapsed_time(e[1]) for e in events]
     att_ms = [e[1].elapsed_time(e[2]) for e in events]
+    step_ms = [e[0].elapsed_time(e[2]) for e in events]
     ms_per_step = wall * 1e3 / args.steps
     value = eff / (ms_per_step * 1e-3) / 1e12
     att_avg = float(np.mean(att_ms))
@@ -338,27 +421,18 @@ def main():
         bwd = backward_bench(w, problem, qd, kd, vd, idx, cnt, stride, ws_att, stream, eff,
                              args.backward_steps)
 
-    att_tflops = eff / (att_avg * 1e-3) / 1e12
-    traffic = traffic_for(w.name)
-    roofline = {
-        "bound": "mfma",
-        "kernel": "bsa_attention (block-sparse flash attention, attn_kernel<false, false, KeyMode>)",
-        "achieved": round(att_tflops, 2),
-        "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
-        "traffic": traffic,
-        "flops_per_launch": eff,
-        "avg_launch_ms": round(att_avg, 4),
-    }
+    roofline = roofline_record(eff, att_avg, traffic_for(w.name))
     cpu = None
     if args.cpu_blocks > 0:
         del qd, kd, vd
         torch.cuda.empty_cache()
         log("[bench] timing the CPU oracle sample ...")
         cpu = cpu_baseline(w, q, k, v, args.cpu_blocks, args.cpu_seconds)
+        # The oracle's time for the whole layer (every head and query block)
+        # at the sampled rate.
+        cpu["ms_per_layer"] = round(eff / cpu.pop("rate_flop_per_s") * 1e3, 1)
         log(f"[bench] CPU oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads "
-            f"({cpu['seconds']} s)")
+            f"({cpu['seconds']} s; {cpu['ms_per_layer'] / 1e3:.0f} s per layer)")
 
     ct, ch, cw = w.chunk
     sel_desc = (f"top-k {w.k}" if w.mode == "topk"
@@ -390,6 +464,9 @@ def main():
             "effective_tflop_per_step": round(eff / 1e12, 4),
         },
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_min": round(float(np.min(step_ms)), 4),
+        "device": device_info(),
         "select_ms": round(float(np.mean(sel_ms)), 4),
         "attention_ms": round(att_avg, 4),
         "dense_ms": None if dense_ms is None else round(dense_ms, 3),

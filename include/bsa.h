@@ -114,8 +114,8 @@ int32_t bsa_index_stride(const bsa_problem* problem, const bsa_select_params* pa
 size_t bsa_workspace_bytes(const bsa_problem* problem, const bsa_select_params* params);
 
 /* Bytes of device workspace bsa_select needs: pooled Q (512 bytes per query
- * block), pooled K (512 bytes per key block) and the Nb x Nk pooled score
- * matrix (fp32), per (batch, head), each part rounded up to 256 bytes.
+ * block) and pooled K (512 bytes per key block), fp32, per (batch, head),
+ * each part rounded up to 256 bytes. The pooled scores never leave the chip.
  * Returns 0 on invalid arguments. */
 size_t bsa_select_workspace_bytes(const bsa_problem* problem,
                                   const bsa_select_params* params);
@@ -135,7 +135,7 @@ size_t bsa_attention_workspace_bytes(const bsa_problem* problem);
  *   cnt      int32 [batch, heads, Nb] out: number of kept key blocks.
  *   Ties between equal pooled scores keep the lower key-block id. A
  *   condition query block only considers condition key blocks.
- * Limits: Nk <= 4096 key blocks per (batch, head) (BSA_ERR_UNSUPPORTED). */
+ * Limits: Nk <= 32768 key blocks per (batch, head) (BSA_ERR_UNSUPPORTED). */
 bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* params,
                       const void* q, const void* k, int32_t* idx, int32_t* cnt,
                       void* workspace, size_t workspace_bytes, void* stream);

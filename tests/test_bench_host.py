@@ -66,9 +66,25 @@ def test_workload_block_counts_match_the_library(grid, chunk, key_chunk):
     assert w.num_blocks == p.num_blocks
     assert w.num_key_blocks == p.num_key_blocks
     # The library's own counts, read back from its workspace size (the layout
-    # documented in bsa.h: pooled Q, pooled K and the pooled scores, fp32,
-    # each part rounded up to 256 bytes).
+    # documented in bsa.h: pooled Q and pooled K, fp32, each part rounded up
+    # to 256 bytes).
     nb, nk = w.num_blocks, w.num_key_blocks
     a = lambda x: -(-x // 256) * 256
-    want = a(2 * nb * 512) + a(2 * nk * 512) + a(2 * nb * nk * 4)
+    want = a(2 * nb * 512) + a(2 * nk * 512)
     assert B.select_workspace_bytes(p, B.SelectParams.topk(3)) == want
+
+
+def test_roofline_names_the_closer_roof():
+    """The record reports both fractions and binds to the larger one."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    r = bench.roofline_record(47.352e12, 46.37, 328.2e9)  # 215K tokens, round-one figures
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["frac_mfma"] - 47.352e12 / 46.37e-3 / 2.5e15) < 1e-4
+    assert abs(r["frac_hbm"] - 328.2e9 / 46.37e-3 / 8e12) < 1e-4
+    assert r["frac"] == r["frac_hbm"]
+    r = bench.roofline_record(47.352e12, 46.37, 100e9)
+    assert r["bound"] == "mfma" and r["frac"] == r["frac_mfma"]
+    r = bench.roofline_record(47.352e12, 46.37, None)
+    assert r["bound"] == "mfma" and r["frac_hbm"] is None

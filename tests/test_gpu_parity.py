@@ -493,6 +493,25 @@ def test_full_size_workload(name):
         assert cnt.min() >= w.k_min and cnt.max() <= w.k_max
 
 
+@pytest.mark.parametrize("params,cond", [(SelectParams.topk(352), 0),
+                                          (SelectParams.cdf(0.9, 4, 64), 4)])
+def test_more_than_4096_key_blocks(params, cond):
+    """The pages' 720p x 93-frame token count (93 x 45 x 80 = 334,800 tokens;
+    deep dive, "VAE, Text Encoder, and Token Spaces") cut into 128-token query blocks and
+    64-token key blocks: 2,880 query blocks, 5,640 key blocks (the last t- and
+    h-rows partial), more than a row's scores fit in registers, so the
+    selection searches them in LDS. Top-k at the pages' ratio r = N_k/16, and
+    CDF with condition frames. Every index row against the oracle, outputs
+    on a sample."""
+    T, H, W = 93, 45, 80
+    problem = Problem.make(T, H, W, 2, key_chunk=(2, 4, 8), cond_frames=cond)
+    assert problem.num_key_blocks == 5640 and problem.num_blocks == 2880
+    q, k, v = make_qkv(T, H, W, 2, kind="field", seed=91)
+    _, cnt, _, _ = _run_and_compare(problem, params, q, k, v, all_outputs=False, sample=(2, 6),
+                                    seed=92)
+    _log(f"counts: min {cnt.min()}, mean {cnt.mean():.2f}, max {cnt.max()}")
+
+
 def test_dense_720p_sampled():
     """Dense baseline at 720p x 93f on sampled query blocks."""
     w = WORKLOADS["720p"]

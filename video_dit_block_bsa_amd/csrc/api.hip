@@ -7,7 +7,7 @@
 #include <string.h>
 
 #include "bsa.h"
-#include "common.h"
+#include "launch.h"
 
 namespace {
 
@@ -22,7 +22,10 @@ bsa_status fail(bsa_status st, const char* fmt, ...) {
   return st;
 }
 
-constexpr int kMaxBlocks = 4096;  // select keeps a row's scores in registers
+// Selection keeps a tile's score rows in 128 KB of LDS (one row at least).
+constexpr int kMaxSelectKeyBlocks = 32768;
+// The backward's transposed selection and per-row masks.
+constexpr int kMaxBlocks = 4096;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -136,20 +139,27 @@ bsa_status check_params(const bsa_select_params* sp) {
   return BSA_OK;
 }
 
+// Selection workspace: pooled Q then pooled K (fp32); the pooled scores stay
+// in LDS.
 struct SelectLayout {
-  size_t qp, kp, s, total;
+  size_t qp, kp, total;
 };
 
 SelectLayout select_layout(const bsa::Geom& g) {
   SelectLayout L;
   L.qp = 0;
   L.kp = align_up((size_t)g.bh * g.nb * bsa::kHeadDim * sizeof(float));
-  L.s = L.kp + align_up((size_t)g.bh * g.nbk * bsa::kHeadDim * sizeof(float));
-  L.total = L.s + align_up((size_t)g.bh * g.nb * g.nbk * sizeof(float));
+  L.total = L.kp + align_up((size_t)g.bh * g.nbk * bsa::kHeadDim * sizeof(float));
   return L;
 }
 
 size_t attention_ws(const bsa::Geom&) { return 0; }
+
+// Launch status is read with hipGetLastError, which reports the last error
+// of any HIP call on the thread. An error some earlier call left pending (the
+// caller's own, or one a runtime fallback recorded without failing) is not
+// this library's to report, so it is cleared before the library launches.
+void clear_pending_error() { (void)hipGetLastError(); }
 
 bsa_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess)
@@ -184,6 +194,7 @@ bsa_status attention_common(const bsa_problem* problem, const void* q, const voi
                 workspace_bytes);
   (void)workspace;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  clear_pending_error();
   return launched(bsa::launch_attention(c.g, static_cast<const bsa::bf16_bits*>(q),
                                         static_cast<const bsa::bf16_bits*>(k),
                                         static_cast<const bsa::bf16_bits*>(v), idx, cnt,
@@ -209,9 +220,9 @@ bsa_status select_common(const bsa_problem* problem, const bsa_select_params* pa
   st = check_params(params);
   if (st != BSA_OK) return st;
   if (c.empty) return BSA_OK;
-  if (c.g.nbk > kMaxBlocks)
+  if (c.g.nbk > kMaxSelectKeyBlocks)
     return fail(BSA_ERR_UNSUPPORTED, "%d key blocks per head: selection supports at most %d",
-                c.g.nbk, kMaxBlocks);
+                c.g.nbk, kMaxSelectKeyBlocks);
   if (!q || !k || !idx || !cnt)
     return fail(BSA_ERR_INVALID_ARG, "q, k, idx and cnt must be non-NULL");
   if (!aligned16(q) || !aligned16(k)) return fail(BSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
@@ -234,9 +245,9 @@ bsa_status select_common(const bsa_problem* problem, const bsa_select_params* pa
   char* ws = static_cast<char*>(workspace);
   float* qp = reinterpret_cast<float*>(ws + L.qp);
   float* kp = reinterpret_cast<float*>(ws + L.kp);
-  float* sc = reinterpret_cast<float*>(ws + L.s);
   const bsa::bf16_bits* qb = static_cast<const bsa::bf16_bits*>(q);
   const bsa::bf16_bits* kb = static_cast<const bsa::bf16_bits*>(k);
+  clear_pending_error();
   if (c.g.nq == bsa::kBlockTokens && c.g.nk == bsa::kBlockTokens && c.g.ctk == c.g.ct &&
       c.g.chk == c.g.ch && !c.g.partial) {
     st = launched(bsa::launch_pool(c.g, qb, kb, qp, kp, row0, s), "pool");
@@ -254,9 +265,7 @@ bsa_status select_common(const bsa_problem* problem, const bsa_select_params* pa
     if (e != hipSuccess)
       return fail(BSA_ERR_LAUNCH, "condition cache copy failed: %s", hipGetErrorString(e));
   }
-  st = launched(bsa::launch_scores(c.g, qp, kp, sc, row0, s), "scores");
-  if (st != BSA_OK) return st;
-  return launched(bsa::launch_select(c.g, sc, params->mode, params->k, params->cdf_p,
+  return launched(bsa::launch_select(c.g, qp, kp, params->mode, params->k, params->cdf_p,
                                      params->k_min, params->k_max, stride, idx, cnt, row0, s),
                   "select");
 }
@@ -341,6 +350,7 @@ bsa_status bsa_pool_cond_keys(const bsa_problem* problem, const void* k, float* 
   if (cache_bytes < cond_cache_bytes(c.g))
     return fail(BSA_ERR_WORKSPACE, "the condition cache needs %zu bytes (got %zu)",
                 cond_cache_bytes(c.g), cache_bytes);
+  clear_pending_error();
   return launched(bsa::launch_pool_keys(c.g, static_cast<const bsa::bf16_bits*>(k), cache, 0,
                                         c.g.cond_kblocks, c.g.cond_kblocks,
                                         reinterpret_cast<hipStream_t>(stream)),
@@ -432,6 +442,7 @@ bsa_status bsa_attention_bwd(const bsa_problem* problem, const void* q, const vo
   if (!aligned16(workspace)) return fail(BSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   char* ws = static_cast<char*>(workspace);
   using bsa::bf16_bits;
+  clear_pending_error();
   return launched(
       bsa::launch_attention_bwd(
           c.g, static_cast<const bf16_bits*>(q), static_cast<const bf16_bits*>(k),

@@ -40,6 +40,7 @@
 // 256 MB Infinity Cache).
 #include <type_traits>
 
+#include "launch.h"
 #include "tile.h"
 
 namespace bsa {

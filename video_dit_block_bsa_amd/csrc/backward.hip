@@ -40,6 +40,7 @@
 // conflicts with this one swizzle.
 #include <type_traits>
 
+#include "launch.h"
 #include "tile.h"
 
 namespace bsa {

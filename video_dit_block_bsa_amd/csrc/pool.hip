@@ -11,7 +11,7 @@
 // through LDS and are added in a fixed order, so the result is deterministic
 // (and the same as summing the 8 tokens, then the 16 groups, in order).
 // HBM-bound: 2 x 32 KB read and 2 x 512 B written per workgroup.
-#include "common.h"
+#include "launch.h"
 
 namespace bsa {
 

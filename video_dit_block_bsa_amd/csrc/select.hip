@@ -1,87 +1,32 @@
-// Pooled block scores and key-block selection ("Block selection via pooled
-// attention scores" and the Top-r / CDF-p modes of "Implementation details
-// and design trade-offs", LongCat-Video deep dive, section "Block Sparse
-// Attention"; combined top-k/CDF clamps from the zhaifeiyue notes, section 3).
+// Pooled block scores and key-block selection in one kernel ("Block selection
+// via pooled attention scores" and the Top-r / CDF-p modes of "Implementation
+// details and design trade-offs", LongCat-Video deep dive, section "Block
+// Sparse Attention"; combined top-k/CDF clamps from the zhaifeiyue notes,
+// section 3). The pages score blocks from pooled vectors "without computing
+// the full QK^T"; here the pooled score matrix does not leave the chip either.
 //
-// scores_kernel: S = (Q_pool K_pool^T) * scale per (batch, head), fp32,
-//   Nb query blocks x Nk key blocks. A
-//   64 x 64 output tile per workgroup, both operand tiles staged in LDS, fp32
-//   MFMA 32x32x2 with a fixed summation order over the 128 channels.
-// select_kernel: one wave64 per query-block row. The row's scores live in
-//   registers (lane l holds key blocks l, l+64, ...). Scores are mapped to
-//   order-preserving 32-bit keys; the k-th largest key is found by a 32-step
-//   bitwise search whose counts are wave ballots. Ties at the threshold go to
-//   the lower key-block id. CDF mode first finds the smallest top set whose
-//   softmax mass reaches p with the same bitwise search on mass, then clamps
-//   the count and selects that many blocks. Everything is wave-uniform and
-//   summed in fixed orders, so results are deterministic.
-#include "common.h"
+// One workgroup owns a tile of query-block rows of one (batch, head):
+//   scores  S[r][j] = (Q_pool[r] . K_pool[j]) * scale for every key block j,
+//           with fp32 MFMA 16x16x4 (exact fp32 products, fp32 sums in a fixed
+//           order), written into LDS. Each wave streams its own 16-column
+//           slices of K_pool straight from global memory (L2-resident: 512
+//           bytes per key block per head), so K_pool is read once per
+//           workgroup and never staged.
+//   select  one wave per row. Scores are mapped to order-preserving 32-bit
+//           keys; the k-th largest key is found by a 32-step bitwise search
+//           whose counts are wave ballots, and ties at the threshold go to
+//           the lower key-block id. CDF mode first finds the smallest top set
+//           whose softmax mass reaches p with the same bitwise search on
+//           mass, then clamps the count and selects that many blocks. The
+//           row's scores sit in registers (lane l holds key blocks l, l+64,
+//           ...) when there are at most 4096 key blocks, and are re-read from
+//           LDS at every step of the search beyond that.
+// Everything is wave-uniform and summed in fixed orders, so results are
+// deterministic, and a row's result does not depend on the rows it shares a
+// workgroup with.
+#include "launch.h"
 
 namespace bsa {
-
-constexpr int kScoreTile = 64;
-constexpr int kScoreRow = kHeadDim + 4;  // padded LDS row (floats)
-
-// One 64 x 64 tile of S per workgroup; wave w computes the 32 x 32 sub-tile
-// (w / 2, w % 2) with fp32 MFMA 32x32x2 (exact fp32 products, fp32 sums).
-// Step kk of the 64 MFMAs contracts channels kk (lanes 0..31) and 64 + kk
-// (lanes 32..63): any pairing of channels works as long as both operands use
-// the same one, and this one lets a lane read four steps of its row with one
-// 16-byte LDS load. Row stride 132 floats keeps those loads conflict-free.
-__global__ __launch_bounds__(kThreads) void scores_kernel(Geom g, int row0, const float* __restrict__ qp,
-                                                          const float* __restrict__ kp,
-                                                          float* __restrict__ s) {
-  __shared__ __attribute__((aligned(16))) float qs[kScoreTile][kScoreRow];
-  __shared__ __attribute__((aligned(16))) float ks[kScoreTile][kScoreRow];
-  const int bh = blockIdx.z;
-  const int i0 = row0 + blockIdx.y * kScoreTile;
-  const int j0 = blockIdx.x * kScoreTile;
-  const int t = threadIdx.x;
-  const float* qb = qp + (size_t)bh * g.nb * kHeadDim;
-  const float* kb = kp + (size_t)bh * g.nbk * kHeadDim;
-
-  // Stage both 64 x 128 operand tiles row-major; rows past nb are zero.
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int c = t + kThreads * r;
-    const int row = c >> 5;
-    const int d4 = c & 31;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (i0 + row < g.nb) a = *reinterpret_cast<const float4*>(qb + (size_t)(i0 + row) * kHeadDim + d4 * 4);
-    if (j0 + row < g.nbk) b = *reinterpret_cast<const float4*>(kb + (size_t)(j0 + row) * kHeadDim + d4 * 4);
-    *reinterpret_cast<float4*>(&qs[row][d4 * 4]) = a;
-    *reinterpret_cast<float4*>(&ks[row][d4 * 4]) = b;
-  }
-  __syncthreads();
-
-  const int lane = t & 63;
-  const int w = t >> 6;
-  const int wr = w >> 1, wc = w & 1;
-  const int m = lane & 31;
-  const int h = lane >> 5;
-  const float* arow = &qs[32 * wr + m][64 * h];
-  const float* brow = &ks[32 * wc + m][64 * h];
-  f32x16 acc = {};
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const float4 a = *reinterpret_cast<const float4*>(arow + 4 * c);
-    const float4 b = *reinterpret_cast<const float4*>(brow + 4 * c);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
-  }
-  // Accumulator value v holds row 8(v/4) + 4h + v%4, column m of the sub-tile.
-  const int j = j0 + 32 * wc + m;
-  if (j < g.nbk) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int i = i0 + 32 * wr + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (i < g.nb) s[((size_t)bh * g.nb + i) * g.nbk + j] = acc[v] * g.scale;
-    }
-  }
-}
 
 // Order-preserving map from fp32 to uint32 (larger float -> larger key);
 // -0 and +0 map to the same key. Key 0 marks "not a candidate".
@@ -102,32 +47,90 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// Rows row0 .. nb-1 of every (batch, head).
-template <int R>
-__global__ __launch_bounds__(kThreads) void select_kernel(Geom g, int row0, const float* __restrict__ s,
-                                                          int mode, int k, float p, int k_min,
-                                                          int k_max, int stride,
-                                                          int32_t* __restrict__ idx,
-                                                          int32_t* __restrict__ cnt) {
+// Scores of rows i0 .. i0+15 against every key block into LDS rows of `lds`
+// floats (rows past the tile's `rows` are computed on row i0 and not kept).
+// Step s of a 16x16x4 MFMA contracts channels s, 32+s, 64+s and 96+s: lane
+// group kk = lane/16 supplies channel 32kk+s of its row (A) or column (B), so
+// each lane reads its 32 channels as 8 consecutive 16-byte loads.
+__device__ __forceinline__ void score_rows(const Geom& g, const float* __restrict__ qrow0,
+                                           const float* __restrict__ kb, int rows, int lds,
+                                           float* srows, int wave, int nwaves) {
   const int lane = threadIdx.x & 63;
-  const int rows_per_head = g.nb - row0;
-  const int local = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (local >= g.bh * rows_per_head) return;  // whole wave leaves together
-  const int i = row0 + local % rows_per_head;
-  const int row = (local / rows_per_head) * g.nb + i;
-  const int na = allowed_key_blocks(g, i);
-  const float* srow = s + (size_t)row * g.nbk;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  uint32_t key[R];
-  float val[R];
+  const int m = lane & 15;
+  const int kk = lane >> 4;
+  float qa[32];
+  {
+    const float* src = qrow0 + (size_t)(m < rows ? m : 0) * kHeadDim + 32 * kk;
 #pragma unroll
-  for (int c = 0; c < R; ++c) {
-    const int j = c * 64 + lane;
-    const bool ok = j < na;
-    val[c] = ok ? srow[j] : -INFINITY;
-    key[c] = ok ? order_key(val[c]) : 0u;
+    for (int s = 0; s < 8; ++s) {
+      const float4 x = *reinterpret_cast<const float4*>(src + 4 * s);
+      qa[4 * s] = x.x;
+      qa[4 * s + 1] = x.y;
+      qa[4 * s + 2] = x.z;
+      qa[4 * s + 3] = x.w;
+    }
   }
+  const int ntiles = (g.nbk + 15) >> 4;
+  for (int ct = wave; ct < ntiles; ct += nwaves) {
+    const int col = ct * 16 + m;
+    const float* src = kb + (size_t)(col < g.nbk ? col : 0) * kHeadDim + 32 * kk;
+    float kf[32];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float4 x = *reinterpret_cast<const float4*>(src + 4 * s);
+      kf[4 * s] = x.x;
+      kf[4 * s + 1] = x.y;
+      kf[4 * s + 2] = x.z;
+      kf[4 * s + 3] = x.w;
+    }
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s], kf[s], acc, 0, 0, 0);
+    // Accumulator value v is row 4*kk + v, column m of the tile.
+    if (col < g.nbk) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 4 * kk + v;
+        if (r < rows) srows[r * lds + col] = acc[v] * g.scale;
+      }
+    }
+  }
+}
+
+// Selection of one row whose n_allowed scores are row[0 .. na-1] (LDS).
+// kR > 0: the row is copied into registers (kR chunks of 64 per lane,
+// na <= 64 kR); kR == 0: every step re-reads it from LDS.
+template <int kR>
+__device__ __forceinline__ void select_row(const float* row, int na, int mode, int k, float p,
+                                           int k_min, int k_max, int stride,
+                                           int32_t* __restrict__ out, int32_t* __restrict__ cnt_out) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int nch = kR > 0 ? kR : (na + 63) >> 6;
+  constexpr int kRegs = kR > 0 ? kR : 1;  // also the unroll count of the chunk loops
+  uint32_t key_r[kRegs];
+  float val_r[kRegs];
+  if constexpr (kR > 0) {
+#pragma unroll kRegs
+    for (int c = 0; c < kR; ++c) {
+      const int j = c * 64 + lane;
+      const bool ok = j < na;
+      val_r[c] = ok ? row[j] : -INFINITY;
+      key_r[c] = ok ? order_key(val_r[c]) : 0u;
+    }
+  }
+  // Score and key of chunk c for this lane.
+  auto score = [&](int c) -> float {
+    if constexpr (kR > 0) return val_r[c];
+    const int j = c * 64 + lane;
+    return j < na ? row[j] : -INFINITY;
+  };
+  auto key_of = [&](int c) -> uint32_t {
+    if constexpr (kR > 0) return key_r[c];
+    const int j = c * 64 + lane;
+    return j < na ? order_key(row[j]) : 0u;
+  };
 
   int keep;
   if (mode == 0) {
@@ -135,26 +138,35 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Geom g, int row0, cons
   } else {
     // Softmax over the allowed blocks (fp32, max-subtracted).
     float m = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < R; ++c) m = fmaxf(m, val[c]);
+#pragma unroll kRegs
+    for (int c = 0; c < nch; ++c) m = fmaxf(m, score(c));
     m = wave_max(m);
     float z = 0.f;
-#pragma unroll
-    for (int c = 0; c < R; ++c) {
-      val[c] = (key[c] != 0u) ? expf(val[c] - m) : 0.f;
-      z += val[c];
+#pragma unroll kRegs
+    for (int c = 0; c < nch; ++c) {
+      const float e = (key_of(c) != 0u) ? expf(score(c) - m) : 0.f;
+      if constexpr (kR > 0) val_r[c] = e;
+      z += e;
     }
     z = wave_sum(z);
     const float inv_z = 1.0f / z;
-#pragma unroll
-    for (int c = 0; c < R; ++c) val[c] *= inv_z;
+    // Probability of chunk c for this lane (the same expression, evaluated
+    // the same way, whether kept in registers or recomputed).
+    auto prob = [&](int c) -> float {
+      if constexpr (kR > 0) return val_r[c];
+      return (key_of(c) != 0u) ? expf(score(c) - m) * inv_z : 0.f;
+    };
+    if constexpr (kR > 0) {
+#pragma unroll kRegs
+      for (int c = 0; c < kR; ++c) val_r[c] *= inv_z;
+    }
     // Largest key threshold whose top set still holds mass >= p.
     uint32_t tau = 0u;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = tau | (1u << bit);
       float part = 0.f;
-#pragma unroll
-      for (int c = 0; c < R; ++c) part += (key[c] >= cand) ? val[c] : 0.f;
+#pragma unroll kRegs
+      for (int c = 0; c < nch; ++c) part += (key_of(c) >= cand) ? prob(c) : 0.f;
       if (wave_sum(part) >= p) tau = cand;
     }
     int raw;
@@ -163,21 +175,23 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Geom g, int row0, cons
     } else {
       int gt = 0;
       float part = 0.f;
-#pragma unroll
-      for (int c = 0; c < R; ++c) {
-        gt += __popcll(__ballot(key[c] > tau));
-        part += (key[c] > tau) ? val[c] : 0.f;
+#pragma unroll kRegs
+      for (int c = 0; c < nch; ++c) {
+        const uint32_t kc = key_of(c);
+        gt += __popcll(__ballot(kc > tau));
+        part += (kc > tau) ? prob(c) : 0.f;
       }
       float run = wave_sum(part);
       int add = 0;
       // Blocks tied at the threshold join in ascending id order until the
       // mass reaches p.
-#pragma unroll
-      for (int c = 0; c < R; ++c) {
-        uint64_t eq = __ballot(key[c] == tau);
+#pragma unroll kRegs
+      for (int c = 0; c < nch; ++c) {
+        uint64_t eq = __ballot(key_of(c) == tau);
+        const float pc = prob(c);
         while (eq != 0ull && run < p) {
           const int src = __ffsll((long long)eq) - 1;
-          run += __shfl(val[c], src);
+          run += __shfl(pc, src);
           ++add;
           eq &= eq - 1ull;
         }
@@ -193,22 +207,22 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Geom g, int row0, cons
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int c_ge = 0;
-#pragma unroll
-    for (int c = 0; c < R; ++c) c_ge += __popcll(__ballot(key[c] >= cand));
+#pragma unroll kRegs
+    for (int c = 0; c < nch; ++c) c_ge += __popcll(__ballot(key_of(c) >= cand));
     if (c_ge >= keep) tau = cand;
   }
   int gt = 0;
-#pragma unroll
-  for (int c = 0; c < R; ++c) gt += __popcll(__ballot(key[c] > tau));
+#pragma unroll kRegs
+  for (int c = 0; c < nch; ++c) gt += __popcll(__ballot(key_of(c) > tau));
   const int need_eq = keep - gt;
 
-  int32_t* out = idx + (size_t)row * stride;
   int pos = 0;
   int eq_seen = 0;
-#pragma unroll
-  for (int c = 0; c < R; ++c) {
-    const bool is_gt = key[c] > tau;
-    const bool is_eq = key[c] == tau;
+#pragma unroll kRegs
+  for (int c = 0; c < nch; ++c) {
+    const uint32_t kc = key_of(c);
+    const bool is_gt = kc > tau;
+    const bool is_eq = kc == tau;
     const uint64_t eqb = __ballot(is_eq);
     const int eq_rank = eq_seen + __popcll(eqb & below);
     const bool sel = is_gt || (is_eq && eq_rank < need_eq);
@@ -218,45 +232,84 @@ __global__ __launch_bounds__(kThreads) void select_kernel(Geom g, int row0, cons
     eq_seen += __popcll(eqb);
   }
   for (int q = keep + lane; q < stride; q += 64) out[q] = -1;
-  if (lane == 0) cnt[row] = keep;
+  if (lane == 0) *cnt_out = keep;
 }
 
-hipError_t launch_scores(const Geom& g, const float* qp, const float* kp, float* s, int row0,
+struct SelectArgs {
+  Geom g;
+  int row0;       // first query block of every (batch, head) to select for
+  int tiles;      // row tiles per (batch, head)
+  int rows;       // rows per tile
+  int lds;        // LDS row stride (floats)
+  int mode, k, k_min, k_max, stride;
+  float p;
+};
+
+// kR: register chunks per lane (1..64) or 0 (rows re-read from LDS);
+// kWaves: waves per workgroup; kLdsFloats: LDS for the tile's score rows.
+template <int kR, int kWaves, int kLdsFloats>
+__global__ __launch_bounds__(64 * kWaves) void fused_select_kernel(SelectArgs a, const float* __restrict__ qp,
+                                                                  const float* __restrict__ kp,
+                                                                  int32_t* __restrict__ idx,
+                                                                  int32_t* __restrict__ cnt) {
+  __shared__ __attribute__((aligned(16))) float srows[kLdsFloats];
+  const Geom& g = a.g;
+  const int bh = blockIdx.x / a.tiles;
+  const int tile = blockIdx.x - bh * a.tiles;
+  const int i0 = a.row0 + tile * a.rows;
+  const int rows = min(a.rows, g.nb - i0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  score_rows(g, qp + ((size_t)bh * g.nb + i0) * kHeadDim, kp + (size_t)bh * g.nbk * kHeadDim, rows,
+             a.lds, srows, wave, kWaves);
+  __syncthreads();
+  for (int r = wave; r < rows; r += kWaves) {
+    const int i = i0 + r;
+    const size_t row = (size_t)bh * g.nb + i;
+    select_row<kR>(srows + r * a.lds, allowed_key_blocks(g, i), a.mode, a.k, a.p, a.k_min, a.k_max,
+                   a.stride, idx + row * a.stride, cnt + row);
+  }
+}
+
+constexpr int kSelectLds = 32768;  // floats (128 KB) of score rows per workgroup
+
+hipError_t launch_select(const Geom& g, const float* qp, const float* kp, int mode, int k, float p,
+                         int k_min, int k_max, int stride, int32_t* idx, int32_t* cnt, int row0,
                          hipStream_t stream) {
   if (row0 >= g.nb) return hipSuccess;
-  dim3 grid((g.nbk + kScoreTile - 1) / kScoreTile, (g.nb - row0 + kScoreTile - 1) / kScoreTile,
-            g.bh);
-  hipLaunchKernelGGL(scores_kernel, grid, dim3(kThreads), 0, stream, g, row0, qp, kp, s);
-  return hipGetLastError();
-}
-
-template <int R>
-static hipError_t launch_select_r(const Geom& g, const float* s, int mode, int k, float p,
-                                  int k_min, int k_max, int stride, int32_t* idx, int32_t* cnt,
-                                  int row0, hipStream_t stream) {
-  const long rows = (long)g.bh * (g.nb - row0);
-  if (rows <= 0) return hipSuccess;
-  const int rows_per_wg = kThreads / 64;
-  dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
-  hipLaunchKernelGGL(select_kernel<R>, grid, dim3(kThreads), 0, stream, g, row0, s, mode, k, p,
-                     k_min, k_max, stride, idx, cnt);
-  return hipGetLastError();
-}
-
-hipError_t launch_select(const Geom& g, const float* s, int mode, int k, float p, int k_min,
-                         int k_max, int stride, int32_t* idx, int32_t* cnt, int row0,
-                         hipStream_t stream) {
+  SelectArgs a;
+  a.g = g;
+  a.row0 = row0;
+  a.mode = mode;
+  a.k = k;
+  a.p = p;
+  a.k_min = k_min;
+  a.k_max = k_max;
+  a.stride = stride;
+  a.lds = (g.nbk + 3) & ~3;
   const int chunks = (g.nbk + 63) / 64;
-#define BSA_SELECT_R(R) \
-  return launch_select_r<R>(g, s, mode, k, p, k_min, k_max, stride, idx, cnt, row0, stream)
-  if (chunks <= 1) BSA_SELECT_R(1);
-  if (chunks <= 2) BSA_SELECT_R(2);
-  if (chunks <= 4) BSA_SELECT_R(4);
-  if (chunks <= 8) BSA_SELECT_R(8);
-  if (chunks <= 16) BSA_SELECT_R(16);
-  if (chunks <= 32) BSA_SELECT_R(32);
-  BSA_SELECT_R(64);
-#undef BSA_SELECT_R
+  // Rows per tile: 16 while the rows' scores fit in registers with four
+  // waves per SIMD (<= 2048 key blocks), 8 up to 4096 key blocks (two waves
+  // per SIMD, 64 register chunks), then as many as 128 KB of LDS holds.
+  int rows;
+  if (chunks <= 32) rows = 16;
+  else if (chunks <= 64) rows = 8;
+  else rows = a.lds <= kSelectLds / 4 ? 4 : a.lds <= kSelectLds / 2 ? 2 : 1;
+  a.rows = rows;
+  a.tiles = (g.nb - row0 + rows - 1) / rows;
+  const dim3 grid((unsigned)((size_t)a.tiles * g.bh));
+#define BSA_FUSED(R, WAVES, LDS)                                                             \
+  hipLaunchKernelGGL((fused_select_kernel<R, WAVES, LDS>), grid, dim3(64 * (WAVES)), 0, stream, a, \
+                     qp, kp, idx, cnt)
+  if (chunks <= 1) BSA_FUSED(1, 16, 16 * 64);
+  else if (chunks <= 2) BSA_FUSED(2, 16, 16 * 128);
+  else if (chunks <= 4) BSA_FUSED(4, 16, 16 * 256);
+  else if (chunks <= 8) BSA_FUSED(8, 16, 16 * 512);
+  else if (chunks <= 16) BSA_FUSED(16, 16, 16 * 1024);
+  else if (chunks <= 32) BSA_FUSED(32, 16, 16 * 2048);
+  else if (chunks <= 64) BSA_FUSED(64, 8, 8 * 4096);
+  else BSA_FUSED(0, 16, kSelectLds);
+#undef BSA_FUSED
+  return hipGetLastError();
 }
 
 }  // namespace bsa
