@@ -121,6 +121,13 @@ def lib():
             raise RuntimeError(
                 f"{_LIB_PATH} is missing: build it with `python -m video_dit_block_bsa_amd.build`"
             )
+        # torch brings its own HIP runtime and asks for it by its unversioned
+        # file name. Loaded first, libbsa.so would pull in the system copy
+        # (soname libamdhip64.so.7), torch would then load a second one, and
+        # kernels launched through the first would find no device. With torch
+        # imported first, libbsa.so binds to torch's copy by soname.
+        import torch  # noqa: F401
+
         L = ctypes.CDLL(_LIB_PATH)
         P, SP = ctypes.POINTER(Problem), ctypes.POINTER(SelectParams)
         vp, i32p = ctypes.c_void_p, ctypes.c_void_p
@@ -355,3 +362,4 @@ def bsa_attention_noisy(problem, q, k, v, idx, cnt, idx_stride, o, workspace, st
     _check(lib().bsa_attention_noisy(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                      _ptr(cnt), int(idx_stride), _ptr(o), ws_ptr,
                                      _nbytes(workspace), _stream(stream)))
+

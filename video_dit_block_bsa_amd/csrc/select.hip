@@ -5,7 +5,8 @@
 // section 3). The pages score blocks from pooled vectors "without computing
 // the full QK^T"; here the pooled score matrix does not leave the chip either.
 //
-// One workgroup owns a tile of query-block rows of one (batch, head):
+// One workgroup of 8 waves owns a tile of query-block rows of one (batch,
+// head):
 //   scores  S[r][j] = (Q_pool[r] . K_pool[j]) * scale for every key block j,
 //           with fp32 MFMA 16x16x4 (exact fp32 products, fp32 sums in a fixed
 //           order), written into LDS. Each wave streams its own 16-column
@@ -47,11 +48,14 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// Scores of rows i0 .. i0+15 against every key block into LDS rows of `lds`
-// floats (rows past the tile's `rows` are computed on row i0 and not kept).
-// Step s of a 16x16x4 MFMA contracts channels s, 32+s, 64+s and 96+s: lane
-// group kk = lane/16 supplies channel 32kk+s of its row (A) or column (B), so
-// each lane reads its 32 channels as 8 consecutive 16-byte loads.
+// Scores of rows i0 .. i0+rows-1 (rows <= 16) against every key block into
+// LDS rows of `lds` floats (MFMA rows past `rows` are computed on row i0 and
+// not kept).
+// Step s = 4i + j of a 16x16x4 MFMA contracts channels 16i + 4kk + j
+// (kk = 0..3): lane group kk = lane/16 supplies channel 16i + 4kk + j of its
+// row (A) or column (B). Load i then brings each lane the 16 bytes at offset
+// 64i + 16kk of its row, so the four lanes of a row read 64 contiguous bytes
+// and one load touches 16 cache lines, not 64.
 __device__ __forceinline__ void score_rows(const Geom& g, const float* __restrict__ qrow0,
                                            const float* __restrict__ kb, int rows, int lds,
                                            float* srows, int wave, int nwaves) {
@@ -60,10 +64,10 @@ __device__ __forceinline__ void score_rows(const Geom& g, const float* __restric
   const int kk = lane >> 4;
   float qa[32];
   {
-    const float* src = qrow0 + (size_t)(m < rows ? m : 0) * kHeadDim + 32 * kk;
+    const float* src = qrow0 + (size_t)(m < rows ? m : 0) * kHeadDim + 4 * kk;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const float4 x = *reinterpret_cast<const float4*>(src + 4 * s);
+      const float4 x = *reinterpret_cast<const float4*>(src + 16 * s);
       qa[4 * s] = x.x;
       qa[4 * s + 1] = x.y;
       qa[4 * s + 2] = x.z;
@@ -71,23 +75,30 @@ __device__ __forceinline__ void score_rows(const Geom& g, const float* __restric
     }
   }
   const int ntiles = (g.nbk + 15) >> 4;
-  for (int ct = wave; ct < ntiles; ct += nwaves) {
-    const int col = ct * 16 + m;
-    const float* src = kb + (size_t)(col < g.nbk ? col : 0) * kHeadDim + 32 * kk;
-    float kf[32];
+  // The next column tile's K_pool slices are loaded while the current one is
+  // contracted, so the loads' latency hides behind the MFMA chain.
+  auto load_cols = [&](int ct, float (&kf)[32]) {
+    const int col = min(ct * 16 + m, g.nbk - 1);
+    const float* src = kb + (size_t)col * kHeadDim + 4 * kk;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const float4 x = *reinterpret_cast<const float4*>(src + 4 * s);
+      const float4 x = *reinterpret_cast<const float4*>(src + 16 * s);
       kf[4 * s] = x.x;
       kf[4 * s + 1] = x.y;
       kf[4 * s + 2] = x.z;
       kf[4 * s + 3] = x.w;
     }
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
+  };
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  float kf[2][32];
+  if (wave < ntiles) load_cols(wave, kf[0]);
+  auto tile = [&](int ct, float (&cur)[32], float (&nxt)[32]) {
+    if (ct + nwaves < ntiles) load_cols(ct + nwaves, nxt);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s], kf[s], acc, 0, 0, 0);
+    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s], cur[s], acc, 0, 0, 0);
     // Accumulator value v is row 4*kk + v, column m of the tile.
+    const int col = ct * 16 + m;
     if (col < g.nbk) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -95,6 +106,10 @@ __device__ __forceinline__ void score_rows(const Geom& g, const float* __restric
         if (r < rows) srows[r * lds + col] = acc[v] * g.scale;
       }
     }
+  };
+  for (int ct = wave; ct < ntiles; ct += 2 * nwaves) {
+    tile(ct, kf[0], kf[1]);
+    if (ct + nwaves < ntiles) tile(ct + nwaves, kf[1], kf[0]);
   }
 }
 
@@ -287,12 +302,13 @@ hipError_t launch_select(const Geom& g, const float* qp, const float* kp, int mo
   a.stride = stride;
   a.lds = (g.nbk + 3) & ~3;
   const int chunks = (g.nbk + 63) / 64;
-  // Rows per tile: 16 while the rows' scores fit in registers with four
-  // waves per SIMD (<= 2048 key blocks), 8 up to 4096 key blocks (two waves
-  // per SIMD, 64 register chunks), then as many as 128 KB of LDS holds.
+  // Rows per tile: 8, one wave each (every workgroup reads all of K_pool, so
+  // more rows per tile means fewer reads). Up to 2048 key blocks their scores
+  // take at most 64 KB of LDS and two workgroups share a CU, one's scoring
+  // overlapping the other's searches; up to 4096, 128 KB; beyond, as many
+  // rows as 128 KB of LDS holds.
   int rows;
-  if (chunks <= 32) rows = 16;
-  else if (chunks <= 64) rows = 8;
+  if (chunks <= 64) rows = 8;
   else rows = a.lds <= kSelectLds / 4 ? 4 : a.lds <= kSelectLds / 2 ? 2 : 1;
   a.rows = rows;
   a.tiles = (g.nb - row0 + rows - 1) / rows;
@@ -300,14 +316,23 @@ hipError_t launch_select(const Geom& g, const float* qp, const float* kp, int mo
 #define BSA_FUSED(R, WAVES, LDS)                                                             \
   hipLaunchKernelGGL((fused_select_kernel<R, WAVES, LDS>), grid, dim3(64 * (WAVES)), 0, stream, a, \
                      qp, kp, idx, cnt)
-  if (chunks <= 1) BSA_FUSED(1, 16, 16 * 64);
-  else if (chunks <= 2) BSA_FUSED(2, 16, 16 * 128);
-  else if (chunks <= 4) BSA_FUSED(4, 16, 16 * 256);
-  else if (chunks <= 8) BSA_FUSED(8, 16, 16 * 512);
-  else if (chunks <= 16) BSA_FUSED(16, 16, 16 * 1024);
-  else if (chunks <= 32) BSA_FUSED(32, 16, 16 * 2048);
+  // Register chunks are rounded up to a multiple of 4 (8 past 32): every
+  // chunk is visited at each of the 32 search steps, so padding costs time.
+  if (chunks <= 1) BSA_FUSED(1, 8, 8 * 64);
+  else if (chunks <= 2) BSA_FUSED(2, 8, 8 * 128);
+  else if (chunks <= 4) BSA_FUSED(4, 8, 8 * 256);
+  else if (chunks <= 8) BSA_FUSED(8, 8, 8 * 512);
+  else if (chunks <= 12) BSA_FUSED(12, 8, 8 * 768);
+  else if (chunks <= 16) BSA_FUSED(16, 8, 8 * 1024);
+  else if (chunks <= 20) BSA_FUSED(20, 8, 8 * 1280);
+  else if (chunks <= 24) BSA_FUSED(24, 8, 8 * 1536);
+  else if (chunks <= 28) BSA_FUSED(28, 8, 8 * 1792);
+  else if (chunks <= 32) BSA_FUSED(32, 8, 8 * 2048);
+  else if (chunks <= 40) BSA_FUSED(40, 8, 8 * 2560);
+  else if (chunks <= 48) BSA_FUSED(48, 8, 8 * 3072);
+  else if (chunks <= 56) BSA_FUSED(56, 8, 8 * 3584);
   else if (chunks <= 64) BSA_FUSED(64, 8, 8 * 4096);
-  else BSA_FUSED(0, 16, kSelectLds);
+  else BSA_FUSED(0, 8, kSelectLds);
 #undef BSA_FUSED
   return hipGetLastError();
 }
