@@ -261,6 +261,26 @@ bsa_status bsa_attention_noisy(const bsa_problem* problem, const void* q, const 
                                int32_t idx_stride, void* o, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Allocation-free selection, for callers that cannot allocate device memory
+ * around the call: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. Same arguments, checks and results as
+ * bsa_select (idx and cnt are bit-identical), with the workspace taken from a
+ * static device array inside the library instead of the caller's buffer.
+ *   Limit. The array holds bsa_select_noalloc_max_workspace_bytes() bytes
+ *          (64 MiB); a problem whose bsa_select_workspace_bytes() exceeds it
+ *          is rejected with BSA_ERR_WORKSPACE before anything is launched.
+ *   Memory. Each GPU the library runs on holds its own copy of the array
+ *          until the process ends; its address is looked up once per device,
+ *          on that device's first call. The call allocates and frees nothing.
+ *   Concurrency. Every call on one GPU shares that GPU's array, which keeps
+ *          the last call's contents (no byte of it is read before the same
+ *          call writes it): calls that overlap on one GPU, on different
+ *          streams or threads, race and must not be issued. */
+size_t bsa_select_noalloc_max_workspace_bytes(void);
+bsa_status bsa_select_noalloc(const bsa_problem* problem, const bsa_select_params* params,
+                              const void* q, const void* k, int32_t* idx, int32_t* cnt,
+                              void* stream);
+
 /* Static description of a status code. */
 const char* bsa_status_string(int32_t status);
 

@@ -364,3 +364,21 @@ def test_binding_checks_tensors_before_the_library():
     with pytest.raises(B.BSAError, match="lse must be torch.float32"):
         B.bsa_attention_lse(p, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE,
                             torch.empty(2048, dtype=torch.float64), (0, 0), stream=0)
+
+
+def test_noalloc_select_checks_on_the_host():
+    """bsa_select_noalloc validates like bsa_select and rejects a problem
+    whose workspace exceeds its static scratch before touching a device."""
+    lib = B.lib()
+    sp = B.SelectParams.topk(105)
+    cap = B.select_noalloc_max_workspace_bytes()
+    assert cap == 64 << 20
+    big = _problem(batch=4)
+    assert B.select_workspace_bytes(big, sp) > cap
+    call = lambda p, s=sp: lib.bsa_select_noalloc(ctypes.byref(p), ctypes.byref(s), FAKE, FAKE,
+                                                  FAKE, FAKE, None)
+    assert call(big) == WORKSPACE
+    assert b"static scratch" in lib.bsa_last_error()
+    assert call(_problem(head_dim=64)) == UNSUPPORTED
+    assert call(_problem(), B.SelectParams.topk(0)) == INVALID
+    assert call(_problem(heads=0)) == OK

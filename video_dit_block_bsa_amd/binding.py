@@ -164,6 +164,10 @@ def lib():
         L.bsa_attention_noisy.argtypes = [P, vp, vp, vp, i32p, i32p, ctypes.c_int32, vp, vp,
                                           ctypes.c_size_t, vp]
         L.bsa_attention_noisy.restype = ctypes.c_int32
+        L.bsa_select_noalloc.argtypes = [P, SP, vp, vp, i32p, i32p, vp]
+        L.bsa_select_noalloc.restype = ctypes.c_int32
+        L.bsa_select_noalloc_max_workspace_bytes.argtypes = []
+        L.bsa_select_noalloc_max_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_status_string.argtypes = [ctypes.c_int32]
         L.bsa_status_string.restype = ctypes.c_char_p
         L.bsa_last_error.argtypes = []
@@ -363,3 +367,15 @@ def bsa_attention_noisy(problem, q, k, v, idx, cnt, idx_stride, o, workspace, st
                                      _ptr(cnt), int(idx_stride), _ptr(o), ws_ptr,
                                      _nbytes(workspace), _stream(stream)))
 
+
+def select_noalloc_max_workspace_bytes() -> int:
+    return lib().bsa_select_noalloc_max_workspace_bytes()
+
+
+def bsa_select_noalloc(problem, params, q, k, idx, cnt, stream=None):
+    """bsa_select_noalloc: bsa_select with the library's static device
+    scratch as workspace (no allocation) -> idx, cnt."""
+    _check_qkv(problem, q=q, k=k)
+    _check_lists(problem, idx, cnt, index_stride(problem, params))
+    _check(lib().bsa_select_noalloc(ctypes.byref(problem), ctypes.byref(params), _ptr(q), _ptr(k),
+                                    _ptr(idx), _ptr(cnt), _stream(stream)))

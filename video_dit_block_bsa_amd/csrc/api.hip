@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "bsa.h"
 #include "launch.h"
 
@@ -292,6 +294,41 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Static device scratch for bsa_select_noalloc: every GPU the library runs on
+// holds one copy until the process ends. In host code `scratch` names a
+// host-side stand-in, never the device array: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up on the
+// first call on that device (with that device current).
+bsa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BSA_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BSA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+  });
+  if (slot.err != hipSuccess || !slot.ptr)
+    return fail(BSA_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(slot.err));
+  *out = slot.ptr;
+  return BSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -330,6 +367,30 @@ bsa_status bsa_select(const bsa_problem* problem, const bsa_select_params* param
                       void* workspace, size_t workspace_bytes, void* stream) {
   return select_common(problem, params, q, k, nullptr, 0, idx, cnt, workspace, workspace_bytes,
                        stream, false);
+}
+
+size_t bsa_select_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+bsa_status bsa_select_noalloc(const bsa_problem* problem, const bsa_select_params* params,
+                              const void* q, const void* k, int32_t* idx, int32_t* cnt,
+                              void* stream) {
+  Checked c;
+  bsa_status st = check_problem(problem, &c);
+  if (st != BSA_OK) return st;
+  st = check_params(params);
+  if (st != BSA_OK) return st;
+  if (c.empty) return BSA_OK;
+  const size_t need = select_layout(c.g).total;
+  if (need > kScratchBytes)
+    return fail(BSA_ERR_WORKSPACE,
+                "select needs %zu workspace bytes; the static scratch of bsa_select_noalloc "
+                "holds %zu (use bsa_select with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != BSA_OK) return st;
+  return select_common(problem, params, q, k, nullptr, 0, idx, cnt, ws, kScratchBytes, stream,
+                       false);
 }
 
 size_t bsa_cond_cache_bytes(const bsa_problem* problem) {
