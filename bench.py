@@ -116,13 +116,23 @@ def traffic_for(workload_name: str):
     return w.get("hbm_bytes_per_launch")
 
 
-def roofline_record(flops: float, avg_ms: float, traffic) -> dict:
-    """Roofline of the attention kernel (the step's dominant kernel, one
-    launch per bsa_attention call) against both roofs: effective flops over
-    the bf16 MFMA peak, and HBM-side bytes counted by rocprofv3 (FETCH_SIZE
-    and WRITE_SIZE, or None without a current record) over the HBM peak. The
-    binding roof is the one the kernel comes closer to; `achieved`, `peak`,
-    `unit` and `frac` describe that roof."""
+def attention_launches(w) -> int:
+    """Kernel launches per bsa_attention call: the library sends a problem of
+    more than 32,768 query-block workgroups (batch*heads x query blocks) as
+    launches of 8 (batch, head) pairs each."""
+    bh = w.batch * w.heads
+    return -(-bh // 8) if bh * w.num_blocks > 32768 and bh > 8 else 1
+
+
+def roofline_record(flops: float, avg_ms: float, traffic, launches: int = 1) -> dict:
+    """Roofline of the attention kernel (the step's dominant kernel) against
+    both roofs, per launch: `flops` and `avg_ms` are one launch's effective
+    flops and average duration (a bsa_attention call of `launches` launches
+    of equal work). Effective flops go over the bf16 MFMA peak, HBM-side
+    bytes counted by rocprofv3 (FETCH_SIZE and WRITE_SIZE per launch, or None
+    without a current record) over the HBM peak. The binding roof is the one
+    the kernel comes closer to; `achieved`, `peak`, `unit` and `frac`
+    describe that roof."""
     sec = avg_ms * 1e-3
     tflops = flops / sec / 1e12
     frac_mfma = tflops / PEAK_BF16_TFLOPS
@@ -143,6 +153,7 @@ def roofline_record(flops: float, avg_ms: float, traffic) -> dict:
         "traffic": traffic,
         "flops_per_launch": flops,
         "avg_launch_ms": round(avg_ms, 4),
+        "launches_per_call": launches,
     }
 
 
@@ -421,7 +432,8 @@ def main():
         bwd = backward_bench(w, problem, qd, kd, vd, idx, cnt, stride, ws_att, stream, eff,
                              args.backward_steps)
 
-    roofline = roofline_record(eff, att_avg, traffic_for(w.name))
+    launches = attention_launches(w)
+    roofline = roofline_record(eff / launches, att_avg / launches, traffic_for(w.name), launches)
     cpu = None
     if args.cpu_blocks > 0:
         del qd, kd, vd

@@ -88,3 +88,20 @@ def test_roofline_names_the_closer_roof():
     assert r["bound"] == "mfma" and r["frac"] == r["frac_mfma"]
     r = bench.roofline_record(47.352e12, 46.37, None)
     assert r["bound"] == "mfma" and r["frac_hbm"] is None
+
+
+def test_attention_launch_count_mirrors_the_library():
+    """bench.py divides the step's attention time and flops by the launches
+    one bsa_attention call makes: the library splits problems of more than
+    32,768 query-block workgroups into launches of 8 heads."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from video_dit_block_bsa_amd import WORKLOADS
+
+    assert bench.attention_launches(WORKLOADS["long"]) == 4        # 32 x 1680 = 53,760
+    assert bench.attention_launches(WORKLOADS["long_q64"]) == 4
+    assert bench.attention_launches(WORKLOADS["720p"]) == 1        # 32 x 720 = 23,040
+    assert bench.attention_launches(WORKLOADS["vc"]) == 1
+    assert bench.attention_launches(WORKLOADS["tiny"]) == 1
+    src = open(os.path.join(ROOT, "video_dit_block_bsa_amd", "csrc", "attention.hip")).read()
+    assert "(size_t)g.bh * g.nb <= 32768" in src and "kGroupHeads = 8" in src

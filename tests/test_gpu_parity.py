@@ -524,3 +524,49 @@ def test_dense_720p_sampled():
                                      lambda p, i: range(g.num_blocks), SCALE, items)
     _log(f"dense 720p: max-abs {mx:.3e}, mean-abs {mean:.3e}")
     assert mx <= PT.MAX_ABS and mean <= PT.MEAN_ABS
+
+
+@pytest.mark.parametrize("with_lse", [False, True])
+def test_many_heads_launch_groups(with_lse):
+    """A problem of more than 32,768 query-block workgroups goes out in
+    launches of 8 heads: every head's output (and lse) is bit-identical to
+    the same head computed in a small single-launch problem. 1040 heads are
+    65 copies of 16 seeded heads, so head h must equal base head h % 16."""
+    import torch
+
+    from video_dit_block_bsa_amd import binding as B
+
+    T, H, W, base, copies = 8, 16, 32, 16, 65
+    q, k, v = make_qkv(T, H, W, base, kind="field", seed=21)
+    qb, kb, vb = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    small = Problem.make(T, H, W, base)
+    params = SelectParams.topk(5)
+    stride = B.index_stride(small, params)
+    idx_s, cnt_s = PT.run_select(small, params, qb, kb)
+    big = Problem.make(T, H, W, base * copies)
+    assert big.heads * big.num_blocks > 32768
+    qd, kd, vd = (t.repeat(1, copies, 1, 1).contiguous() for t in (qb, kb, vb))
+    idx_b, cnt_b = PT.run_select(big, params, qd, kd)
+    assert torch.equal(idx_b.view(copies, -1), idx_s.view(1, -1).expand(copies, -1))
+    assert torch.equal(cnt_b.view(copies, -1), cnt_s.view(1, -1).expand(copies, -1))
+
+    def attend(problem, qq, kk, vv, idx, cnt):
+        o = torch.full_like(qq, float("nan"))
+        ws = torch.empty(max(B.attention_workspace_bytes(problem), 1), dtype=torch.uint8,
+                         device="cuda")
+        if not with_lse:
+            B.bsa_attention(problem, qq, kk, vv, idx, cnt, stride, o, ws)
+            torch.cuda.synchronize()
+            return o, None
+        lse = torch.full(qq.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+        B.bsa_attention_lse(problem, qq, kk, vv, idx, cnt, stride, o, lse, ws)
+        torch.cuda.synchronize()
+        return o, lse
+
+    o_s, l_s = attend(small, qb, kb, vb, idx_s, cnt_s)
+    o_b, l_b = attend(big, qd, kd, vd, idx_b, cnt_b)
+    ob = o_b.view(torch.int16).view(1, copies, base, -1)
+    os_ = o_s.view(torch.int16).view(1, 1, base, -1)
+    assert torch.equal(ob, os_.expand_as(ob))
+    if with_lse:
+        assert torch.equal(l_b.view(copies, base, -1), l_s.view(1, base, -1).expand(copies, -1, -1))
