@@ -143,3 +143,49 @@ def test_vc_workload_full_size():
     n_cond = w.cond_frames * w.H * w.W
     assert torch.equal(o_c[:, :, n_cond:].view(torch.int16), o_f[:, :, n_cond:].view(torch.int16))
     assert bool(torch.isnan(o_c[:, :, :n_cond].float()).all())
+
+
+def test_noisy_path_many_heads_launch_groups():
+    """More than 32,768 query-block workgroups: both attention paths go out
+    in launches of 8 heads. 1040 heads are 65 copies of 16 seeded heads; the
+    cached path's noisy rows equal the full path's, and every head's output
+    equals its base head's in a 16-head problem (one launch), bit for bit."""
+    import torch
+
+    from video_dit_block_bsa_amd import binding as B
+
+    T, H, W, base, copies, cond = 8, 16, 32, 16, 65, 4
+    params = SelectParams.topk(4)
+    q, k, v = make_qkv(T, H, W, base, kind="field", seed=61)
+    qb, kb, vb = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    small = Problem.make(T, H, W, base, cond_frames=cond)
+    big = Problem.make(T, H, W, base * copies, cond_frames=cond)
+    g = PT.geometry(big)
+    nb, cq = g.num_blocks, g.cond_blocks
+    assert big.heads * nb > 32768
+    stride = B.index_stride(big, params)
+    idx_s, cnt_s = PT.run_select(small, params, qb, kb)
+    o_s = PT.run_attention(small, qb, kb, vb, idx_s, cnt_s, stride)
+    qd, kd, vd = (t.repeat(1, copies, 1, 1).contiguous() for t in (qb, kb, vb))
+    del qb, kb, vb
+    idx_f, cnt_f = PT.run_select(big, params, qd, kd)
+    o_f = PT.run_attention(big, qd, kd, vd, idx_f, cnt_f, stride)
+    cache = torch.empty((max(B.cond_cache_bytes(big), 16) // 4,), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.select_workspace_bytes(big, params), dtype=torch.uint8, device="cuda")
+    B.bsa_pool_cond_keys(big, kd, cache)
+    idx_c = torch.full_like(idx_f, -7)
+    cnt_c = torch.full_like(cnt_f, -7)
+    B.bsa_select_noisy(big, params, qd, kd, cache, idx_c, cnt_c, ws)
+    o_c = torch.full_like(qd, float("nan"))
+    B.bsa_attention_noisy(big, qd, kd, vd, idx_c, cnt_c, stride, o_c, torch.empty(16, dtype=torch.uint8,
+                                                                                     device="cuda"))
+    torch.cuda.synchronize()
+    n_cond = cond * H * W
+    of = o_f.view(torch.int16).view(copies, base, -1, 128)
+    oc = o_c.view(torch.int16).view(copies, base, -1, 128)
+    os_ = o_s.view(torch.int16).view(1, base, -1, 128)
+    assert torch.equal(of, os_.expand_as(of)), "grouped launches changed a head's output"
+    assert torch.equal(oc[:, :, n_cond:], of[:, :, n_cond:]), "noisy o rows differ"
+    rows_f = idx_f.view(-1, nb, stride)
+    rows_c = idx_c.view(-1, nb, stride)
+    assert torch.equal(rows_c[:, cq:], rows_f[:, cq:])
