@@ -690,10 +690,10 @@ hipError_t launch_attention_heads(const Geom& g, const bf16_bits* q, const bf16_
 
 // Launches of more than 32,768 workgroups go out as launches of 8 (batch,
 // head) pairs each. Measured at 215K tokens (53,760 workgroups as one
-// launch): 45.9-46.6 ms against 47.9-48.4 ms on three boxes; the chip holds a
-// higher clock through the shorter launches. Smaller grids (720p: 23,040
-// workgroups) gained nothing from it. Every head's work is the same either
-// way, so outputs do not change.
+// launch), each box against itself: 45.9-47.7 ms against 47.9-48.4 ms on
+// three boxes, with the clock climbing from 1.4 to 1.7 GHz over the launches
+// of a step. Smaller grids (720p: 23,040 workgroups) gained nothing from it.
+// Every head's work is the same either way, so outputs do not change.
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                             const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
                             int stride, bool dense, bf16_bits* o, float* lse, int q_begin,
