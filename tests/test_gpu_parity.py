@@ -526,29 +526,37 @@ def test_dense_720p_sampled():
     assert mx <= PT.MAX_ABS and mean <= PT.MEAN_ABS
 
 
+@pytest.mark.parametrize("batch,heads", [(1, 1040), (3, 347)])
 @pytest.mark.parametrize("with_lse", [False, True])
-def test_many_heads_launch_groups(with_lse):
+def test_many_heads_launch_groups(batch, heads, with_lse):
     """A problem of more than 32,768 query-block workgroups goes out in
-    launches of 8 heads: every head's output (and lse) is bit-identical to
-    the same head computed in a small single-launch problem. 1040 heads are
-    65 copies of 16 seeded heads, so head h must equal base head h % 16."""
+    launches of 8 (batch, head) pairs: every pair's output (and lse) is
+    bit-identical to the same head computed in a small single-launch problem.
+    The pairs are copies of 16 seeded heads, pair p a copy of base head
+    p % 16 (so a group offset off by 8 pairs would show); 3 x 347 = 1041
+    pairs leave a last launch of one pair."""
     import torch
 
     from video_dit_block_bsa_amd import binding as B
 
-    T, H, W, base, copies = 8, 16, 32, 16, 65
+    T, H, W, base = 8, 16, 32, 16
+    bh = batch * heads
+    copies = -(-bh // base)
     q, k, v = make_qkv(T, H, W, base, kind="field", seed=21)
     qb, kb, vb = PT.to_device(q), PT.to_device(k), PT.to_device(v)
     small = Problem.make(T, H, W, base)
     params = SelectParams.topk(5)
     stride = B.index_stride(small, params)
     idx_s, cnt_s = PT.run_select(small, params, qb, kb)
-    big = Problem.make(T, H, W, base * copies)
-    assert big.heads * big.num_blocks > 32768
-    qd, kd, vd = (t.repeat(1, copies, 1, 1).contiguous() for t in (qb, kb, vb))
+    big = Problem.make(T, H, W, heads, batch=batch)
+    assert bh * big.num_blocks > 32768 and bh % 8 in (0, 1)
+    qd, kd, vd = (t.repeat(1, copies, 1, 1)[:, :bh].reshape(batch, heads, -1, 128).contiguous()
+                  for t in (qb, kb, vb))
     idx_b, cnt_b = PT.run_select(big, params, qd, kd)
-    assert torch.equal(idx_b.view(copies, -1), idx_s.view(1, -1).expand(copies, -1))
-    assert torch.equal(cnt_b.view(copies, -1), cnt_s.view(1, -1).expand(copies, -1))
+    per = big.num_blocks * stride
+    assert torch.equal(idx_b.view(-1)[: bh * per].view(bh, per),
+                       idx_s.view(base, per).repeat(copies, 1)[:bh])
+    assert torch.equal(cnt_b.view(bh, -1), cnt_s.view(base, -1).repeat(copies, 1)[:bh])
 
     def attend(problem, qq, kk, vv, idx, cnt):
         o = torch.full_like(qq, float("nan"))
@@ -565,8 +573,7 @@ def test_many_heads_launch_groups(with_lse):
 
     o_s, l_s = attend(small, qb, kb, vb, idx_s, cnt_s)
     o_b, l_b = attend(big, qd, kd, vd, idx_b, cnt_b)
-    ob = o_b.view(torch.int16).view(1, copies, base, -1)
-    os_ = o_s.view(torch.int16).view(1, 1, base, -1)
-    assert torch.equal(ob, os_.expand_as(ob))
+    want = o_s.view(torch.int16).view(base, -1).repeat(copies, 1)[:bh]
+    assert torch.equal(o_b.view(torch.int16).view(bh, -1), want)
     if with_lse:
-        assert torch.equal(l_b.view(copies, base, -1), l_s.view(1, base, -1).expand(copies, -1, -1))
+        assert torch.equal(l_b.view(bh, -1), l_s.view(base, -1).repeat(copies, 1)[:bh])
