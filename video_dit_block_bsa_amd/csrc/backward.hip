@@ -777,6 +777,90 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     }
   };
 
+  // The same sub-tiles with the MFMA operands read from LDS ahead of their
+  // use (grids the chunks divide; the general kernels, which need the
+  // registers, keep `compute`): right after a sub-tile's chain is issued, the
+  // wave reads all eight operands of that sub-tile's accumulation and the
+  // first four of the next sub-tile's chain, so the reads complete under the
+  // chain's MFMAs (dS role) or the exponentials (P role) and the barrier's
+  // wait for the hand-off finds them done. Measured at 215K tokens: backward
+  // 163.7 against 168.1 ms on one box (all eight chain operands ahead, or only
+  // four accumulation operands, gained less; all of both spilled); the
+  // outputs are bit-identical, since every product and sum is the same.
+  auto compute_pf = [&](auto rolec, auto qhc, const char* qt, const char* dt, const float* sts,
+                        bool keep_hi) __attribute__((always_inline)) {
+    constexpr bool dsr = decltype(rolec)::value != 0;
+    constexpr int NT = kHalfKeys ? 2 : 4;
+    constexpr int TT0 = kHalfKeys ? 2 * decltype(qhc)::value : 0;
+    char* xbase = xch + xs_id * 4096;
+    const char* rt = dsr ? dt : qt;  // row operands of the chain (dO for dP, Q for S)
+    const char* xt = dsr ? qt : dt;  // transposed operands of the accumulation
+    constexpr int kRop = 4;  // chain operands read ahead
+    constexpr int kTop = 8;  // accumulation operands read ahead
+    bf16x8 rop[kRop];
+#pragma unroll
+    for (int s = 0; s < kRop; ++s) rop[s] = row_operand(rt, TT0, s, tl);
+#pragma unroll
+    for (int tl2 = 0; tl2 < NT; ++tl2) {
+      const int tt = TT0 + tl2;
+      char* xs = xbase + (tl2 & 1) * 2048;
+      f32x16 cacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) cacc = mfma(s < kRop ? rop[s] : row_operand(rt, tt, s, tl), xf[s], cacc);
+      bf16x8 top[kTop];
+#pragma unroll
+      for (int i = 0; i < kTop; ++i) top[i] = tr_operand(xt, 2 * tt + (i >> 2), i & 3, tl);
+      if (tl2 + 1 < NT) {
+#pragma unroll
+        for (int s = 0; s < kRop; ++s) rop[s] = row_operand(rt, tt + 1, s, tl);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 bop[2];
+      if constexpr (!dsr) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int q0 = 32 * tt + 16 * hh + 8 * gs;
+          u32x4 packed;
+#pragma unroll
+          for (int j2 = 0; j2 < 4; ++j2) {
+            const int i0 = 8 * hh + 2 * j2;
+            const f32x2 l2 = *reinterpret_cast<const f32x2*>(sts + q0 + 2 * j2);
+            const uint32_t pw =
+                pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(cacc[i0], a.c_log2, -l2[0])),
+                          __builtin_amdgcn_exp2f(__builtin_fmaf(cacc[i0 + 1], a.c_log2, -l2[1])));
+            packed[j2] = (kSplit && tt >= 2 && !keep_hi) ? 0u : pw;
+          }
+          bop[hh] = __builtin_bit_cast(bf16x8, packed);
+          *reinterpret_cast<u32x4*>(xs + hh * 1024 + lane * 16) = packed;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the hand-off is written
+        workgroup_barrier();
+      } else {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): done with the slot's previous use
+        workgroup_barrier();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int q0 = 32 * tt + 16 * hh + 8 * gs;
+          const u32x4 pb = *reinterpret_cast<const u32x4*>(xs + hh * 1024 + lane * 16);
+          u32x4 packed;
+#pragma unroll
+          for (int j2 = 0; j2 < 4; ++j2) {
+            const int i0 = 8 * hh + 2 * j2;
+            const f32x2 d2 = *reinterpret_cast<const f32x2*>(sts + kBlockTokens + q0 + 2 * j2);
+            packed[j2] = pack_bf16(bf16_to_f32(pb[j2] & 0xffffu) * (cacc[i0] - d2[0]),
+                                   bf16_to_f32(pb[j2] >> 16) * (cacc[i0 + 1] - d2[1]));
+          }
+          bop[hh] = __builtin_bit_cast(bf16x8, packed);
+        }
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[u] = mfma(4 * k2 + u < kTop ? top[4 * k2 + u] : tr_operand(xt, 2 * tt + k2, u, tl), bop[k2], acc[u]);
+    }
+  };
+
   auto run = [&](auto rolec, auto qhc) __attribute__((always_inline)) {
     Rows cur = first_rows();
     if (cur.qa >= g.nb) return;
@@ -787,9 +871,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       workgroup_barrier();
       if (nxt.qa < g.nb) load_rows(nxt, b == 0 ? q1s : q0s, b == 0 ? d1s : d0s, b == 0 ? st1s : st0s);
-      compute(rolec, qhc, reinterpret_cast<const char*>(b == 0 ? q0s : q1s),
-              reinterpret_cast<const char*>(b == 0 ? d0s : d1s), b == 0 ? st0s : st1s,
-              !kSplit || cur.qb2 < g.nb);
+      if constexpr (!kPartial)
+        compute_pf(rolec, qhc, reinterpret_cast<const char*>(b == 0 ? q0s : q1s),
+                   reinterpret_cast<const char*>(b == 0 ? d0s : d1s), b == 0 ? st0s : st1s,
+                   !kSplit || cur.qb2 < g.nb);
+      else
+        compute(rolec, qhc, reinterpret_cast<const char*>(b == 0 ? q0s : q1s),
+                reinterpret_cast<const char*>(b == 0 ? d0s : d1s), b == 0 ? st0s : st1s,
+                !kSplit || cur.qb2 < g.nb);
       if (nxt.qa >= g.nb) return false;
       cur = nxt;
       nxt = next_rows(cur);
