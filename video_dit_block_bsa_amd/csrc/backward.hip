@@ -49,8 +49,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 
 // ---------------------------------------------------------------- prep ---
-// One workgroup per (block, batch*head). Thread t handles half (t % 2) of the
-// channels of slot t / 2; the two halves meet with one lane exchange. stats
+// One workgroup per (block, batch*head). Thread t reads 16-byte chunk t % 16
+// (channels 8(t%16) .. +7) of slots 16i + t/16, i = 0..7, from O and dO, so
+// each load of a wave covers four whole 256-byte rows; the 16 lanes of a
+// slot then add their partial dot products with four lane exchanges. stats
 // holds, per (batch*head, block), 128 values lse*log2(e) followed by 128
 // values D, in slot order (64-token blocks fill the first 64 of each). A
 // query with lse = -inf (no key block) gets +inf, so that its recomputed
@@ -64,36 +66,42 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(Geom g, int nbw,
   const int blk = blockIdx.x;
   const int bh = blockIdx.y;
   const int t = threadIdx.x;
-  const int j = t >> 1;
-  const int half = t & 1;
+  const int chunk = t & 15;
+  const int r = t >> 4;
   // A slot of a partial block outside the grid has no token: D = 0 and
   // lse*log2(e) = +inf, so every probability recomputed for it is 0.
-  const bool inside = j < g.nq && (!g.partial || block_slot_valid(g, blk, j));
-  const int tok = inside ? block_token(g, blk, j) : 0;
-  const size_t off = ((size_t)bh * g.S + tok) * kHeadDim + 64 * half;
+  auto slot_tok = [&](int j, bool& inside) __attribute__((always_inline)) {
+    inside = j < g.nq && (!g.partial || block_slot_valid(g, blk, j));
+    return inside ? block_token(g, blk, j) : 0;
+  };
   u32x4 ov[8], dv[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    ov[c] = inside ? *reinterpret_cast<const u32x4*>(o + off + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-    dv[c] = inside ? *reinterpret_cast<const u32x4*>(dout + off + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < 8; ++i) {
+    bool inside;
+    const int tok = slot_tok(16 * i + r, inside);
+    const size_t off = ((size_t)bh * g.S + tok) * kHeadDim + 8 * chunk;
+    ov[i] = inside ? *reinterpret_cast<const u32x4*>(o + off) : u32x4{0u, 0u, 0u, 0u};
+    dv[i] = inside ? *reinterpret_cast<const u32x4*>(dout + off) : u32x4{0u, 0u, 0u, 0u};
   }
-  float acc = 0.f;
+  float* st = stats + ((size_t)bh * g.nb + blk) * (2 * kBlockTokens);
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+  for (int i = 0; i < 8; ++i) {
+    float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc = __builtin_fmaf(bf16_to_f32(ov[c][e] & 0xffffu), bf16_to_f32(dv[c][e] & 0xffffu), acc);
-      acc = __builtin_fmaf(bf16_to_f32(ov[c][e] >> 16), bf16_to_f32(dv[c][e] >> 16), acc);
+      acc = __builtin_fmaf(bf16_to_f32(ov[i][e] & 0xffffu), bf16_to_f32(dv[i][e] & 0xffffu), acc);
+      acc = __builtin_fmaf(bf16_to_f32(ov[i][e] >> 16), bf16_to_f32(dv[i][e] >> 16), acc);
     }
-  acc += __shfl_xor(acc, 1);
-  float* st = stats + ((size_t)bh * g.nb + blk) * (2 * kBlockTokens);
-  if (j >= g.nq) {
-    // 64-token blocks use the first 64 entries of each half.
-  } else if (half == 1) {
-    st[kBlockTokens + j] = acc;
-  } else {
+#pragma unroll
+    for (int x = 1; x < 16; x <<= 1) acc += __shfl_xor(acc, x);
+    const int j = 16 * i + r;
+    if (chunk == 0 && j < g.nq) st[kBlockTokens + j] = acc;
+  }
+  if (t < g.nq) {
+    bool inside;
+    const int tok = slot_tok(t, inside);
     const float l = inside ? lse[(size_t)bh * g.S + tok] : -INFINITY;
-    st[j] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    st[t] = (l == -INFINITY) ? INFINITY : l * kLog2e;
   }
   // Mask rows are per key block (nbk of them); query block blk clears rows
   // blk, blk + nb, ...
