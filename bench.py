@@ -116,12 +116,27 @@ def traffic_for(workload_name: str):
     return w.get("hbm_bytes_per_launch")
 
 
+LAUNCH_WORKGROUPS = 15 * 512  # workgroups per sparse attention launch (library constant)
+
+
 def attention_launches(w) -> int:
-    """Kernel launches per bsa_attention call: the library sends a problem of
-    more than 32,768 query-block workgroups (batch*heads x query blocks) as
-    launches of 8 (batch, head) pairs each."""
+    """Kernel launches per bsa_attention call, as the library makes them:
+    launches of LAUNCH_WORKGROUPS workgroups, counted over batch*heads x the
+    query-block workgroups of a head rounded up to a multiple of 8. A
+    workgroup takes one query block, or with 64-token query blocks and
+    128-token key blocks on grids the chunks divide (more than one block
+    along w) a t-adjacent pair of them."""
     bh = w.batch * w.heads
-    return -(-bh // 8) if bh * w.num_blocks > 32768 and bh > 8 else 1
+    (ct, ch, cw), (kt, kh, kw) = w.chunk, w.kchunk
+    divides = all(n % c == 0 for n, c in zip((w.T, w.H, w.W), w.chunk)) and \
+        all(n % c == 0 for n, c in zip((w.T, w.H, w.W), w.kchunk))
+    one_wide = w.W // cw == 1 or (w.H // ch) * (w.W // cw) == 1 or w.W // kw == 1 or \
+        (w.H // kh) * (w.W // kw) == 1
+    per_head = w.num_blocks
+    if w.block_tokens != 128 and w.key_block_tokens == 128 and divides and not one_wide:
+        nhw = (w.H // ch) * (w.W // cw)
+        per_head = (w.num_blocks // nhw + 1) // 2 * nhw
+    return -(-(bh * (-(-per_head // 8) * 8)) // LAUNCH_WORKGROUPS)
 
 
 def roofline_record(flops: float, avg_ms: float, traffic, launches: int = 1) -> dict:

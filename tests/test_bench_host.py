@@ -92,16 +92,22 @@ def test_roofline_names_the_closer_roof():
 
 def test_attention_launch_count_mirrors_the_library():
     """bench.py divides the step's attention time and flops by the launches
-    one bsa_attention call makes: the library splits problems of more than
-    32,768 query-block workgroups into launches of 8 heads."""
+    one bsa_attention call makes: the library sends sparse calls as launches
+    of 7,680 workgroups (one per query block, or per t-adjacent pair of
+    64-token query blocks)."""
     sys.path.insert(0, ROOT)
     import bench
     from video_dit_block_bsa_amd import WORKLOADS
 
-    assert bench.attention_launches(WORKLOADS["long"]) == 4        # 32 x 1680 = 53,760
-    assert bench.attention_launches(WORKLOADS["long_q64"]) == 4
-    assert bench.attention_launches(WORKLOADS["720p"]) == 1        # 32 x 720 = 23,040
-    assert bench.attention_launches(WORKLOADS["vc"]) == 1
+    assert bench.LAUNCH_WORKGROUPS == 7680
+    assert bench.attention_launches(WORKLOADS["long"]) == 7        # 32 x 1680 = 53,760
+    assert bench.attention_launches(WORKLOADS["long_k64"]) == 7
+    assert bench.attention_launches(WORKLOADS["long_k256"]) == 7
+    assert bench.attention_launches(WORKLOADS["long_q64"]) == 7    # 32 x 1680 pairs
+    assert bench.attention_launches(WORKLOADS["720p"]) == 3        # 32 x 720 = 23,040
+    assert bench.attention_launches(WORKLOADS["vc"]) == 2          # 32 x 480 = 15,360
+    assert bench.attention_launches(WORKLOADS["480p"]) == 1        # 32 x 168 = 5,376
     assert bench.attention_launches(WORKLOADS["tiny"]) == 1
     src = open(os.path.join(ROOT, "video_dit_block_bsa_amd", "csrc", "attention.hip")).read()
+    assert "kLaunchWorkgroups = 15 * 512;" in src
     assert "(size_t)g.bh * g.nb <= 32768" in src and "kGroupHeads = 8" in src

@@ -526,20 +526,22 @@ def test_dense_720p_sampled():
     assert mx <= PT.MAX_ABS and mean <= PT.MEAN_ABS
 
 
-@pytest.mark.parametrize("batch,heads", [(1, 1040), (3, 347)])
+@pytest.mark.parametrize("batch,heads,H", [(1, 1040, 16), (3, 347, 16), (1, 160, 28), (3, 53, 28)])
 @pytest.mark.parametrize("with_lse", [False, True])
-def test_many_heads_launch_groups(batch, heads, with_lse):
-    """A problem of more than 32,768 query-block workgroups goes out in
-    launches of 8 (batch, head) pairs: every pair's output (and lse) is
-    bit-identical to the same head computed in a small single-launch problem.
-    The pairs are copies of 16 seeded heads, pair p a copy of base head
-    p % 16 (so a group offset off by 8 pairs would show); 3 x 347 = 1041
-    pairs leave a last launch of one pair."""
+def test_many_heads_launch_groups(batch, heads, H, with_lse):
+    """A sparse call of more than 7,680 query-block workgroups goes out as
+    launches of 7,680 workgroups, numbered across the launches: every (batch,
+    head) pair's output (and lse) is bit-identical to the same head computed
+    in a small single-launch problem. The pairs are copies of 16 seeded
+    heads, pair p a copy of base head p % 16, so a range offset that lands on
+    the wrong head shows. With 32 query blocks per head the ranges start at
+    head boundaries (33,280 and 33,312 workgroups: five launches); with 56
+    they start inside a head (7,680 = 137 x 56 + 8)."""
     import torch
 
     from video_dit_block_bsa_amd import binding as B
 
-    T, H, W, base = 8, 16, 32, 16
+    T, W, base = 8, 32, 16
     bh = batch * heads
     copies = -(-bh // base)
     q, k, v = make_qkv(T, H, W, base, kind="field", seed=21)
@@ -549,7 +551,9 @@ def test_many_heads_launch_groups(batch, heads, with_lse):
     stride = B.index_stride(small, params)
     idx_s, cnt_s = PT.run_select(small, params, qb, kb)
     big = Problem.make(T, H, W, heads, batch=batch)
-    assert bh * big.num_blocks > 32768 and bh % 8 in (0, 1)
+    nq8 = -(-big.num_blocks // 8) * 8
+    assert base * nq8 <= 7680 < bh * nq8
+    assert H == 16 or 7680 % nq8 != 0
     qd, kd, vd = (t.repeat(1, copies, 1, 1)[:, :bh].reshape(batch, heads, -1, 128).contiguous()
                   for t in (qb, kb, vb))
     idx_b, cnt_b = PT.run_select(big, params, qd, kd)
@@ -577,3 +581,40 @@ def test_many_heads_launch_groups(batch, heads, with_lse):
     assert torch.equal(o_b.view(torch.int16).view(bh, -1), want)
     if with_lse:
         assert torch.equal(l_b.view(bh, -1), l_s.view(base, -1).repeat(copies, 1)[:bh])
+
+
+@pytest.mark.parametrize("kind", ["dense", "paired_q64"])
+def test_many_heads_dense_and_paired_blocks(kind):
+    """1,041 (batch, head) pairs (3 x 347, copies of 16 seeded heads) give
+    every pair's output bit-identical to its base head's in a 16-head
+    single-launch problem, for the two other launch splits: dense calls of
+    more than 32,768 workgroups go out as 130 launches of 8 pairs and a last
+    one of one pair; paired 64-token query blocks (one workgroup per
+    t-adjacent pair, 33,312 workgroups) as five launches of up to 7,680."""
+    import torch
+
+    from video_dit_block_bsa_amd import binding as B
+
+    T, H, W, base, batch, heads = 8, 16, 32, 16, 3, 347
+    chunk = (4, 4, 8) if kind == "dense" else (2, 4, 8)
+    bh = batch * heads
+    copies = -(-bh // base)
+    q, k, v = make_qkv(T, H, W, base, kind="field", seed=23)
+    qb, kb, vb = PT.to_device(q), PT.to_device(k), PT.to_device(v)
+    small = Problem.make(T, H, W, base, chunk=chunk, key_chunk=(4, 4, 8))
+    big = Problem.make(T, H, W, heads, batch=batch, chunk=chunk, key_chunk=(4, 4, 8))
+    assert bh * big.num_blocks > 32768 and bh % 8 == 1
+    qd, kd, vd = (t.repeat(1, copies, 1, 1)[:, :bh].reshape(batch, heads, -1, 128).contiguous()
+                  for t in (qb, kb, vb))
+    if kind == "dense":
+        o_s = PT.run_dense(small, qb, kb, vb)
+        o_b = PT.run_dense(big, qd, kd, vd)
+    else:
+        params = SelectParams.topk(5)
+        stride = B.index_stride(small, params)
+        idx_s, cnt_s = PT.run_select(small, params, qb, kb)
+        idx_b, cnt_b = PT.run_select(big, params, qd, kd)
+        o_s = PT.run_attention(small, qb, kb, vb, idx_s, cnt_s, stride)
+        o_b = PT.run_attention(big, qd, kd, vd, idx_b, cnt_b, stride)
+    want = o_s.view(torch.int16).view(base, -1).repeat(copies, 1)[:bh]
+    assert torch.equal(o_b.view(torch.int16).view(bh, -1), want)

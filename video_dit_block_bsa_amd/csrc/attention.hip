@@ -147,8 +147,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
   const Geom& g = a.g;
 
   // XCD-aware remap: hardware id x runs on XCD x % 8; give XCD c the query
-  // blocks [c*chunk, (c+1)*chunk) of the current head.
-  const int x = blockIdx.x;
+  // blocks [c*chunk, (c+1)*chunk) of the current head. A call split into
+  // workgroup ranges numbers its workgroups across the launches (x0 is a
+  // multiple of 8, so x % 8 is still the XCD).
+  const int x = blockIdx.x + a.x0;
   const int pair = x / a.nq8;
   const int r = x - pair * a.nq8;
   const int chunk = a.nq8 >> 3;
@@ -596,6 +598,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
 
 namespace {
 
+// 64-token query blocks with 128-token key blocks go in t-adjacent pairs
+// (kUnion), counted from the launch's first t-row, on grids the chunks divide.
+bool pairs_query_blocks(const Geom& g, int q_begin) {
+  return g.nq != kBlockTokens && g.nk == kBlockTokens && !needs_general(g) &&
+         q_begin % (g.nH * g.nW) == 0;
+}
+
+// A sparse call goes out as launches of at most this many workgroups: 15
+// full rounds of the chip (256 compute units holding two workgroups each),
+// so every launch but the last ends without a partly filled round, and the
+// clock, which climbs over the launches of a step under this load, gets
+// several launch boundaries. Measured against launches of 8 heads at 215K
+// tokens (53,760 workgroups), each box against itself: 0.5-2 % less time per
+// step on three boxes; at 720p (23,040 workgroups, one launch before) 0.8 %.
+// Ranges of 21 rounds measured the same, ranges of 5-10 rounds and of 35
+// rounds slower.
+constexpr unsigned kLaunchWorkgroups = 15 * 512;
+
 hipError_t launch_attention_heads(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                                   const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
                                   int stride, bool dense, bf16_bits* o, float* lse, int q_begin,
@@ -648,58 +668,69 @@ hipError_t launch_attention_heads(const Geom& g, const bf16_bits* q, const bf16_
   }
   AttnArgs a = make_attn_args(g, stride, q_begin);
   const int mode = g.nk == 64 ? 2 : g.nk > kBlockTokens ? 1 : 0;
-  // 64-token query blocks with 128-token key blocks go in t-adjacent pairs
-  // (kUnion), counted from the launch's first t-row.
   const int nhw = g.nH * g.nW;
-  if (split && mode == 0 && !part && q_begin % nhw == 0) {
+  if (pairs_query_blocks(g, q_begin)) {
     const int pairs = ((g.nb - q_begin) / nhw + 1) / 2 * nhw;
     a.nq8 = (pairs + 7) / 8 * 8;
-    const dim3 grid_u((unsigned)((size_t)g.bh * a.nq8));
-    if (lse)
-      hipLaunchKernelGGL((attn_kernel<false, true, 0, false, false, true>), grid_u, dim3(kThreads), 0,
-                         stream, a, q, k, v, idx, cnt, o, lse);
-    else
-      hipLaunchKernelGGL((attn_kernel<false, false, 0, false, false, true>), grid_u, dim3(kThreads), 0,
-                         stream, a, q, k, v, idx, cnt, o, lse);
-    return hipGetLastError();
+    const unsigned total = (unsigned)((size_t)g.bh * a.nq8);
+    for (unsigned x0 = 0; x0 < total; x0 += kLaunchWorkgroups) {
+      a.x0 = (int)x0;
+      const dim3 range(total - x0 < kLaunchWorkgroups ? total - x0 : kLaunchWorkgroups);
+      if (lse)
+        hipLaunchKernelGGL((attn_kernel<false, true, 0, false, false, true>), range, dim3(kThreads), 0,
+                           stream, a, q, k, v, idx, cnt, o, lse);
+      else
+        hipLaunchKernelGGL((attn_kernel<false, false, 0, false, false, true>), range, dim3(kThreads),
+                           0, stream, a, q, k, v, idx, cnt, o, lse);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
 #define BSA_LAUNCH_ATTN(LSE, MODE, SPLIT)                                                      \
   if (part)                                                                                     \
-    hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT, true>), grid, dim3(kThreads), 0,   \
+    hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT, true>), range, dim3(kThreads), 0,  \
                        stream, a, q, k, v, idx, cnt, o, lse);                                   \
   else                                                                                          \
-    hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT, false>), grid, dim3(kThreads), 0,  \
+    hipLaunchKernelGGL((attn_kernel<false, LSE, MODE, SPLIT, false>), range, dim3(kThreads), 0, \
                        stream, a, q, k, v, idx, cnt, o, lse)
 #define BSA_LAUNCH_ATTN_MODES(LSE, SPLIT)                \
   if (mode == 0) { BSA_LAUNCH_ATTN(LSE, 0, SPLIT); }     \
   else if (mode == 1) { BSA_LAUNCH_ATTN(LSE, 1, SPLIT); } \
   else { BSA_LAUNCH_ATTN(LSE, 2, SPLIT); }
-  if (lse) {
-    if (split) { BSA_LAUNCH_ATTN_MODES(true, true); }
-    else { BSA_LAUNCH_ATTN_MODES(true, false); }
-  } else {
-    if (split) { BSA_LAUNCH_ATTN_MODES(false, true); }
-    else { BSA_LAUNCH_ATTN_MODES(false, false); }
+  for (unsigned x0 = 0; x0 < grid.x; x0 += kLaunchWorkgroups) {
+    a.x0 = (int)x0;
+    const dim3 range(grid.x - x0 < kLaunchWorkgroups ? grid.x - x0 : kLaunchWorkgroups);
+    if (lse) {
+      if (split) { BSA_LAUNCH_ATTN_MODES(true, true); }
+      else { BSA_LAUNCH_ATTN_MODES(true, false); }
+    } else {
+      if (split) { BSA_LAUNCH_ATTN_MODES(false, true); }
+      else { BSA_LAUNCH_ATTN_MODES(false, false); }
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
 #undef BSA_LAUNCH_ATTN_MODES
 #undef BSA_LAUNCH_ATTN
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace
 
-// Launches of more than 32,768 workgroups go out as launches of 8 (batch,
-// head) pairs each. Measured at 215K tokens (53,760 workgroups as one
-// launch), each box against itself: 45.9-47.7 ms against 47.9-48.4 ms on
-// three boxes, with the clock climbing from 1.4 to 1.7 GHz over the launches
-// of a step. Smaller grids (720p: 23,040 workgroups) gained nothing from it.
-// Every head's work is the same either way, so outputs do not change.
+// Sparse calls split themselves into workgroup ranges (above). Dense calls
+// of more than 32,768 workgroups go out as launches of 8 (batch, head) pairs
+// each: measured at 215K tokens (53,760 workgroups as one launch), each box
+// against itself, the sparse kernel in 8-head launches took 45.9-47.7 ms
+// against 47.9-48.4 ms on three boxes, with the clock climbing from 1.4 to
+// 1.7 GHz over the launches of a step. Every workgroup's work is the same in
+// any split, so outputs do not change.
 hipError_t launch_attention(const Geom& g, const bf16_bits* q, const bf16_bits* k,
                             const bf16_bits* v, const int32_t* idx, const int32_t* cnt,
                             int stride, bool dense, bf16_bits* o, float* lse, int q_begin,
                             hipStream_t stream) {
   constexpr int kGroupHeads = 8;
-  if ((size_t)g.bh * g.nb <= 32768 || g.bh <= kGroupHeads)
+  if (!dense || (size_t)g.bh * g.nb <= 32768 || g.bh <= kGroupHeads)
     return launch_attention_heads(g, q, k, v, idx, cnt, stride, dense, o, lse, q_begin, stream);
   for (int h0 = 0; h0 < g.bh; h0 += kGroupHeads) {
     Geom gh = g;

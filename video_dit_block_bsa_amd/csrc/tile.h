@@ -28,6 +28,7 @@ struct AttnArgs {
   int lcwk, lchk;     // log2 of the key chunk's w and h extents
   int lcw, lch;       // the same for the query chunk
   float c_log2;       // scale * log2(e)
+  int x0;             // id of the launch's first workgroup among all of the call's (a multiple of 8)
 };
 
 // x / d with m = magic(d): the high half of x * m, exact for the ranges the
@@ -141,6 +142,7 @@ inline AttnArgs make_attn_args(const Geom& g, int stride, int q_begin = 0) {
   a.stride = stride;
   a.q_begin = q_begin;
   a.nq8 = (g.nb - q_begin + 7) / 8 * 8;
+  a.x0 = 0;
   a.mag_nw = magic(g.nW);
   a.mag_nhw = magic(g.nH * g.nW);
   a.mag_nwk = magic(g.nWk);
